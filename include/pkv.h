@@ -1,0 +1,196 @@
+/*
+ * pkv -- chunk attention over a paged KV cache, forward and backward, for AMD MI355X (gfx950).
+ *
+ * C ABI. Every pointer argument named *_dev is a device pointer (or a device-mapped pinned host
+ * pointer where stated); every other pointer is host memory. Sizes are element counts unless the
+ * name ends in _bytes. No call allocates memory except paged_kv_alloc. Compute calls enqueue work
+ * on the caller's HIP stream (passed as void*; NULL is the default stream) and return without
+ * synchronising; device faults surface at the caller's next synchronisation.
+ *
+ * Citations name the web summaries of "Out of the Memory Barrier: A Highly Memory Efficient
+ * Training System for LLMs with Million-Token Contexts" (gist.science, editions pt / es / it)
+ * and a section on them.
+ *
+ * Conventions shared by all calls:
+ *  - bf16 values travel as uint16_t bit patterns.
+ *  - A pool stores, per physical page p and KV head g, one contiguous block
+ *      kv[p][g][0][t][d] = key, kv[p][g][1][t][d] = value   (bf16, t < page_size, d < head_dim)
+ *    and, if created with PKV_GRADS, a gradient block of the same shape in fp32
+ *      grad[p][g][0][t][d] = dK, grad[p][g][1][t][d] = dV,
+ *    plus one fp32 representative key (mean key) per page and head, rep[p][g][d].
+ *  - A block table bt_dev (int32, device) maps logical page i (token positions
+ *    [i*page_size, (i+1)*page_size)) to a physical page bt_dev[i]. It is owned by the caller and
+ *    may be any permutation. n_bt is its length.
+ *  - Queries and query gradients of one chunk are [C][H_q][head_dim] bf16, row-major. Query head
+ *    h reads KV head h / G with G = H_q / H_kv. The chunk starts at token q0 = n_prior*page_size.
+ *  - lse is [H_q][C] fp32 natural-log log-sum-exp of the scaled scores.
+ *  - Validation happens before anything is enqueued; a call that fails enqueues nothing.
+ *    Block-table and selection entries live on the device and are checked there: an entry out of
+ *    range is skipped (treated as an empty page) and recorded in the pool's error word, read by
+ *    paged_kv_check.
+ *  - Errors: the return value is a status code below; pkv_last_error() gives a message
+ *    (thread-local, valid until the next call on the same thread).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_E_INVALID (-1)     /* null pointer, bad shape, C % page_size != 0, H_q % H_kv != 0 */
+#define PKV_E_UNSUPPORTED (-2) /* head_dim not in {64,128} or page_size not in {64,128} */
+#define PKV_E_NOMEM (-3)       /* allocation failed or workspace too small */
+#define PKV_E_RANGE (-4)       /* token positions or pages beyond the pool or block table */
+#define PKV_E_HIP (-5)         /* a HIP runtime call failed; see pkv_last_error */
+#define PKV_E_STATE (-6)       /* operation not valid for this pool (e.g. attention on a host-tier pool) */
+#define PKV_E_DEVICE (-7)      /* paged_kv_check: a kernel met an out-of-range table entry */
+
+#define PKV_GRADS 1u      /* allocate fp32 gradient pages (zero-initialised) on the device */
+#define PKV_HOST_TIER 2u  /* keep the bf16 KV pages in pinned, device-mapped host memory */
+
+/* paged_kv_export / paged_kv_import selectors */
+#define PKV_K 0
+#define PKV_V 1
+#define PKV_DK 2
+#define PKV_DV 3
+#define PKV_REP 4
+
+typedef struct pkv_pool pkv_pool;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int pkv_version(void);
+
+/* Message for the last failed call on this thread ("" if none). Never NULL. */
+const char* pkv_last_error(void);
+
+/*
+ * Create a pool of n_pages physical pages on the current HIP device.
+ * Paged KV cache with gradients kept in pages too: pt 2.B, es 2.B ("paged memory manager"), it 2.B.
+ * flags: PKV_GRADS adds fp32 gradient pages (zeroed); PKV_HOST_TIER places the KV pages in pinned
+ * host memory that kernels read over the host link (pt 2.D, es 2.B "asynchronous CPU offloading",
+ * it 2.C); gradients and representatives of such a pool stay on the device.
+ * The pool owns all its memory; paged_kv_free releases it.
+ */
+int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n_kv_heads,
+                   int32_t head_dim, uint32_t flags);
+
+/* Synchronise the device and release the pool. NULL is a no-op returning PKV_OK. */
+int paged_kv_free(pkv_pool* pool);
+
+/* Shape of a pool (any output pointer may be NULL). */
+int paged_kv_info(const pkv_pool* pool, int32_t* n_pages, int32_t* page_size, int32_t* n_kv_heads,
+                  int32_t* head_dim, uint32_t* flags);
+
+/*
+ * Device address of a pool array: what = PKV_K/PKV_V give the bf16 KV base (both return the same
+ * base, the [K|V] index is part of the layout above), PKV_DK/PKV_DV the fp32 gradient base,
+ * PKV_REP the fp32 representative base. For PKV_HOST_TIER pools the KV base is the device-mapped
+ * pointer of the pinned host array. Returns NULL on error.
+ */
+void* paged_kv_data(const pkv_pool* pool, int32_t what);
+
+/*
+ * Append n_tokens tokens at positions [pos0, pos0 + n_tokens) without moving any existing page
+ * (pt 2.B: no reallocation or copy on append). k_dev, v_dev: [n_tokens][H_kv][head_dim] bf16.
+ * For every page whose first token is written by this call, its gradient block is zeroed
+ * (PKV_GRADS pools). For every page whose last token is written by this call, its representative
+ * key is computed as the float32 sequential sum over the page's tokens times 1/page_size
+ * (es 2.B: a mean representative vector per key page).
+ */
+int paged_kv_append(pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t pos0, int32_t n_tokens,
+                    const uint16_t* k_dev, const uint16_t* v_dev, void* stream);
+
+/* Zero the gradient blocks of logical pages [0, n_pages) through bt_dev, or of the whole pool when
+ * bt_dev is NULL. Uses a fill kernel (no memset node), so it may be captured in a graph. */
+int paged_kv_zero_grad(pkv_pool* pool, const int32_t* bt_dev, int32_t n_pages, void* stream);
+
+/*
+ * Copy logical pages [first_page, first_page + n_pages) of one array into dst_dev in logical
+ * order: PKV_K/PKV_V -> [n_pages*page_size][H_kv][head_dim] bf16; PKV_DK/PKV_DV -> same shape fp32;
+ * PKV_REP -> [n_pages][H_kv][head_dim] fp32. For tests and checkpoint-style read-back.
+ */
+int paged_kv_export(const pkv_pool* pool, int32_t what, const int32_t* bt_dev, int32_t n_bt,
+                    int32_t first_page, int32_t n_pages, void* dst_dev, void* stream);
+
+/* Synchronise the device, return PKV_E_DEVICE if a kernel recorded an out-of-range table entry
+ * since the last check (and clear the record), else PKV_OK. */
+int paged_kv_check(pkv_pool* pool);
+
+/*
+ * Page-level top-K selection for one query chunk (pt 2.C, es 2.B "page-level sparse attention",
+ * it 2.D). For each KV head g:
+ *   qsum_g = float32 sum of the chunk's queries over tokens and the group's G heads, in the
+ *            order: 64-token blocks summed sequentially, blocks summed sequentially, heads summed
+ *            sequentially;
+ *   score(p) = sequential float32 dot(qsum_g, rep[bt[p]][g]) with no fused multiply-add, for
+ *            candidate logical pages p in [0, n_cand), n_cand = max(n_prior - n_local, 0);
+ *   the min(top_k, n_cand) best candidates by (score descending, page id ascending; NaN lowest),
+ *   sorted ascending, followed by the n_local most recent prior pages [n_cand, n_prior).
+ * Output sel_dev: [H_kv][n_sel] int32 logical page ids, n_sel = min(top_k, n_cand) + (n_prior -
+ * n_cand), also stored to *n_sel_out (host; known without synchronising).
+ * q_dev: [C][H_q][head_dim] bf16, C % 64 == 0. ws_dev: at least page_topk_ws_bytes(...) bytes.
+ */
+size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int32_t H_q);
+int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
+                     const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
+                     int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes, void* stream);
+
+/*
+ * Forward attention of one query chunk over the paged cache (pt 2.A, 2.B; es 2.B custom kernels).
+ * Query head h (KV head g = h / G) at chunk row t (position q0 + t) attends to
+ *   dense (sel_dev == NULL): every key at position <= q0 + t, i.e. logical pages [0, n_prior)
+ *                            plus the chunk's own block;
+ *   sparse: the pages sel_dev[g*n_sel + i], i < n_sel (ascending logical ids < n_prior), plus
+ *           the own block, causally.
+ * with softmax(scale * q.k). The own block (logical pages [n_prior, n_prior + C/page_size)) must
+ * already be appended. Only KV heads [kvh0, kvh0 + n_kvh) and their query heads are computed.
+ * Outputs: o_dev [C][H_q][head_dim] bf16 and lse_dev [H_q][C] fp32 for those heads.
+ * ws_dev: at least chunk_attn_fwd_ws_bytes(...) bytes of device scratch (may be NULL if 0). The
+ * *_ws_bytes queries take n_sel < 0 for dense calls.
+ */
+size_t chunk_attn_fwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh,
+                               int32_t C, int32_t H_q);
+int chunk_attn_fwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
+                   const int32_t* sel_dev, int32_t n_sel, int32_t kvh0, int32_t n_kvh,
+                   const uint16_t* q_dev, int32_t C, int32_t H_q, float scale,
+                   uint16_t* o_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+/*
+ * Backward attention of one query chunk (pt 2.A recomputation; pt 2.B, it 2.B in-place gradient
+ * accumulation into gradient pages). Probabilities are recomputed from q, the pages and lse.
+ * dq_dev [C][H_q][head_dim] bf16 is written. dK and dV of every attended key are ADDED (fp32) into
+ * the gradient pages of gpool through gbt_dev (gpool may equal pool and gbt_dev may equal bt_dev;
+ * gpool must have PKV_GRADS). sel_dev/n_sel must equal the forward's. o_dev, dout_dev:
+ * [C][H_q][head_dim] bf16; lse_dev as written by chunk_attn_fwd.
+ * Calls that add into the same gradient pages commute (fp32 atomic adds).
+ */
+size_t chunk_attn_bwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh,
+                               int32_t C, int32_t H_q);
+int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt,
+                   pkv_pool* gpool, const int32_t* gbt_dev, int32_t n_gbt, int32_t n_prior,
+                   const int32_t* sel_dev, int32_t n_sel, int32_t kvh0, int32_t n_kvh,
+                   const uint16_t* q_dev, const uint16_t* o_dev, const uint16_t* dout_dev,
+                   const float* lse_dev, int32_t C, int32_t H_q, float scale, uint16_t* dq_dev,
+                   void* ws_dev, size_t ws_bytes, void* stream);
+
+/*
+ * Host-tier gather (pt 2.D, es 2.B, it 2.C: KV moves between host and GPU memory on dedicated
+ * streams from pinned memory). For KV head kvh and i < n_sel, copies the (page, kvh) block of
+ * logical page sel_dev[i] (host pool, physical page host_bt_dev[sel_dev[i]]) into the same head's
+ * block of device pool page dst_pages_dev[i]. Indices stay on the device; nothing synchronises.
+ * host must be a PKV_HOST_TIER pool and dev a device pool of the same page size, heads and dim.
+ */
+int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_dev, int32_t n_host_bt,
+                    const int32_t* sel_dev, int32_t n_sel, int32_t kvh, const int32_t* dst_pages_dev,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

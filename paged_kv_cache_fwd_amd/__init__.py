@@ -1,0 +1,251 @@
+"""Python binding of libpkv (paged chunk attention for MI355X): argument marshalling only.
+
+Every computation runs in the HIP kernels behind the C ABI declared in include/pkv.h. PyTorch is
+used for device memory and the current stream. The binding raises if the compiled library is
+missing; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK, PKV_E_INVALID, PKV_E_UNSUPPORTED, PKV_E_NOMEM, PKV_E_RANGE, PKV_E_HIP, PKV_E_STATE, PKV_E_DEVICE = \
+    0, -1, -2, -3, -4, -5, -6, -7
+PKV_GRADS, PKV_HOST_TIER = 1, 2
+PKV_K, PKV_V, PKV_DK, PKV_DV, PKV_REP = 0, 1, 2, 3, 4
+
+EXPORTED = (
+    "pkv_version", "pkv_last_error", "paged_kv_alloc", "paged_kv_free", "paged_kv_info", "paged_kv_data",
+    "paged_kv_append", "paged_kv_zero_grad", "paged_kv_export", "paged_kv_check", "page_topk_ws_bytes",
+    "page_topk_select", "chunk_attn_fwd_ws_bytes", "chunk_attn_fwd", "chunk_attn_bwd_ws_bytes",
+    "chunk_attn_bwd", "paged_kv_gather",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pkv error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_U = ctypes.c_uint32
+_S = ctypes.c_size_t
+_F = ctypes.c_float
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the compiled library (once). Raises if it was not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m paged_kv_cache_fwd_amd.build` "
+                           "or __graft_entry__.build(); there is no fallback implementation")
+    lib = ctypes.CDLL(p)
+    sig = {
+        "pkv_version": (_I, []),
+        "pkv_last_error": (ctypes.c_char_p, []),
+        "paged_kv_alloc": (_I, [ctypes.POINTER(_P), _I, _I, _I, _I, _U]),
+        "paged_kv_free": (_I, [_P]),
+        "paged_kv_info": (_I, [_P, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_I),
+                               ctypes.POINTER(_U)]),
+        "paged_kv_data": (_P, [_P, _I]),
+        "paged_kv_append": (_I, [_P, _P, _I, _I, _I, _P, _P, _P]),
+        "paged_kv_zero_grad": (_I, [_P, _P, _I, _P]),
+        "paged_kv_export": (_I, [_P, _I, _P, _I, _I, _I, _P, _P]),
+        "paged_kv_check": (_I, [_P]),
+        "page_topk_ws_bytes": (_S, [_P, _I, _I, _I]),
+        "page_topk_select": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, ctypes.POINTER(_I), _P, _S, _P]),
+        "chunk_attn_fwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I]),
+        "chunk_attn_fwd": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
+        "chunk_attn_bwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I]),
+        "chunk_attn_bwd": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _S,
+                                _P]),
+        "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != PKV_OK:
+        raise PkvError(rc, load().pkv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor, got {t.dtype} on {t.device}")
+
+
+class Pool:
+    """A paged KV pool (pages of K|V in bf16, optional fp32 gradient pages, fp32 page reps)."""
+
+    def __init__(self, n_pages: int, page_size: int, n_kv_heads: int, head_dim: int, grads: bool = True,
+                 host_tier: bool = False):
+        lib = load()
+        h = ctypes.c_void_p()
+        flags = (PKV_GRADS if grads else 0) | (PKV_HOST_TIER if host_tier else 0)
+        _check(lib.paged_kv_alloc(ctypes.byref(h), n_pages, page_size, n_kv_heads, head_dim, flags))
+        self.handle = h
+        self.n_pages, self.page, self.h_kv, self.d = n_pages, page_size, n_kv_heads, head_dim
+        self.grads, self.host_tier = grads, host_tier
+
+    def free(self):
+        if self.handle:
+            _check(load().paged_kv_free(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def append(self, bt: torch.Tensor, pos0: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+        _need(bt, torch.int32, "bt")
+        _need(k, torch.bfloat16, "k")
+        _need(v, torch.bfloat16, "v")
+        n = k.shape[0]
+        _check(load().paged_kv_append(self.handle, _ptr(bt), bt.numel(), pos0, n, _ptr(k), _ptr(v), _stream(stream)))
+
+    def zero_grad(self, bt: Optional[torch.Tensor] = None, n_pages: int = 0, stream=None):
+        _check(load().paged_kv_zero_grad(self.handle, _ptr(bt), n_pages, _stream(stream)))
+
+    def export(self, what: int, bt: torch.Tensor, first_page: int, n_pages: int, stream=None) -> torch.Tensor:
+        _need(bt, torch.int32, "bt")
+        if what in (PKV_K, PKV_V):
+            out = torch.empty((n_pages * self.page, self.h_kv, self.d), dtype=torch.bfloat16, device=bt.device)
+        elif what in (PKV_DK, PKV_DV):
+            out = torch.empty((n_pages * self.page, self.h_kv, self.d), dtype=torch.float32, device=bt.device)
+        else:
+            out = torch.empty((n_pages, self.h_kv, self.d), dtype=torch.float32, device=bt.device)
+        _check(load().paged_kv_export(self.handle, what, _ptr(bt), bt.numel(), first_page, n_pages, _ptr(out),
+                                      _stream(stream)))
+        return out
+
+    def check(self):
+        _check(load().paged_kv_check(self.handle))
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def page_topk_select(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, top_k: int, n_local: int,
+                     sel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Returns sel [H_kv][n_sel] int32 (logical page ids, ascending per head)."""
+    lib = load()
+    _need(bt, torch.int32, "bt")
+    _need(q, torch.bfloat16, "q")
+    C, H_q, _ = q.shape
+    n_cand = max(n_prior - n_local, 0)
+    n_sel = min(top_k, n_cand) + (n_prior - n_cand)
+    if sel is None:
+        sel = torch.empty((pool.h_kv, max(n_sel, 0)), dtype=torch.int32, device=q.device)
+    nb = lib.page_topk_ws_bytes(pool.handle, n_prior, C, H_q)
+    ws = _ws(nb, q.device, ws)
+    out_n = _I(0)
+    _check(lib.page_topk_select(pool.handle, _ptr(bt), bt.numel(), n_prior, _ptr(q), C, H_q, top_k, n_local,
+                                _ptr(sel), ctypes.byref(out_n), _ptr(ws), nb, _stream(stream)))
+    assert out_n.value == n_sel
+    return sel[:, :n_sel] if sel.shape[1] != n_sel else sel
+
+
+def chunk_attn_fwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int) -> int:
+    return load().chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+
+
+def chunk_attn_bwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int) -> int:
+    return load().chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+
+
+def chunk_attn_fwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, scale: float,
+                   sel: Optional[torch.Tensor] = None, kvh0: int = 0, n_kvh: Optional[int] = None,
+                   o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None):
+    """Forward of one chunk; returns (o [C][H_q][d] bf16, lse [H_q][C] fp32)."""
+    lib = load()
+    _need(bt, torch.int32, "bt")
+    _need(q, torch.bfloat16, "q")
+    C, H_q, d = q.shape
+    n_kvh = pool.h_kv - kvh0 if n_kvh is None else n_kvh
+    n_sel = -1 if sel is None else sel.shape[1]
+    if sel is not None:
+        _need(sel, torch.int32, "sel")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H_q, C), dtype=torch.float32, device=q.device)
+    nb = lib.chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+    ws = _ws(nb, q.device, ws)
+    _check(lib.chunk_attn_fwd(pool.handle, _ptr(bt), bt.numel(), n_prior, _ptr(sel), max(n_sel, 0), kvh0, n_kvh,
+                              _ptr(q), C, H_q, float(scale), _ptr(o), _ptr(lse), _ptr(ws), nb, _stream(stream)))
+    return o, lse
+
+
+def chunk_attn_bwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, o: torch.Tensor,
+                   dout: torch.Tensor, lse: torch.Tensor, scale: float, sel: Optional[torch.Tensor] = None,
+                   kvh0: int = 0, n_kvh: Optional[int] = None, gpool: Optional[Pool] = None,
+                   gbt: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+                   ws: Optional[torch.Tensor] = None, stream=None):
+    """Backward of one chunk; returns dq. dK/dV are added into the gradient pages of gpool."""
+    lib = load()
+    _need(bt, torch.int32, "bt")
+    for t, nm in ((q, "q"), (o, "o"), (dout, "dout")):
+        _need(t, torch.bfloat16, nm)
+    _need(lse, torch.float32, "lse")
+    C, H_q, d = q.shape
+    n_kvh = pool.h_kv - kvh0 if n_kvh is None else n_kvh
+    n_sel = -1 if sel is None else sel.shape[1]
+    if sel is not None:
+        _need(sel, torch.int32, "sel")
+    gpool = pool if gpool is None else gpool
+    gbt = bt if gbt is None else gbt
+    if dq is None:
+        dq = torch.empty_like(q)
+    nb = lib.chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+    ws = _ws(nb, q.device, ws)
+    _check(lib.chunk_attn_bwd(pool.handle, _ptr(bt), bt.numel(), gpool.handle, _ptr(gbt), gbt.numel(), n_prior,
+                              _ptr(sel), max(n_sel, 0), kvh0, n_kvh, _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), C,
+                              H_q, float(scale), _ptr(dq), _ptr(ws), nb, _stream(stream)))
+    return dq
+
+
+def paged_kv_gather(host: Pool, dev: Pool, host_bt: torch.Tensor, sel_row: torch.Tensor, kvh: int,
+                    dst_pages: torch.Tensor, stream=None):
+    """Copy the (page, kvh) blocks of the logical pages sel_row from a host-tier pool into the device
+    pool pages dst_pages (both int32 device vectors of equal length)."""
+    _need(host_bt, torch.int32, "host_bt")
+    _need(sel_row, torch.int32, "sel_row")
+    _need(dst_pages, torch.int32, "dst_pages")
+    _check(load().paged_kv_gather(host.handle, dev.handle, _ptr(host_bt), host_bt.numel(), _ptr(sel_row),
+                                  sel_row.numel(), kvh, _ptr(dst_pages), _stream(stream)))

@@ -1,0 +1,66 @@
+"""Build libpkv.so in-tree with hipcc for gfx950 (kernels) and g++ (host ABI)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libpkv.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+
+KERNELS = {
+    "k_paging.hip": ["-ffp-contract=off"],
+    "k_select.hip": ["-ffp-contract=off"],
+    "k_attn_fwd.hip": [],
+    "k_attn_bwd.hip": [],
+}
+HOST = ["pkv_abi.cpp"]
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
+    # Packed fp32 arithmetic stays off: the compiler emits plain fp32 ops only.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-gpu-rdc", "-munsafe-fp-atomics",
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
+    return r.stderr
+
+
+def build(verbose: bool = False, extra_hip_flags=None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = []
+    objs = []
+    for src, flags in KERNELS.items():
+        obj = os.path.join(BUILD, src + ".o")
+        objs.append(obj)
+        jobs.append([HIPCC, *HIP_FLAGS, *flags, *(extra_hip_flags or []), "-c", os.path.join(CSRC, src), "-o", obj])
+    for src in HOST:
+        obj = os.path.join(BUILD, src + ".o")
+        objs.append(obj)
+        jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
+                     "-I" + os.path.join(ROCM, "include"), "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        logs = list(ex.map(_run, jobs))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    if verbose:
+        for lg in logs:
+            if lg.strip():
+                sys.stderr.write(lg)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

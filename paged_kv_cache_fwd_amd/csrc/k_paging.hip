@@ -1,0 +1,216 @@
+// Paged KV pool kernels: append (scatter through the block table), representative keys, gradient
+// zeroing, logical-order export and the host-tier gather.
+//
+// Paged KV cache and gradient pages: "Out of the Memory Barrier" summaries, pt 2.B / es 2.B / it 2.B
+// (pages are never moved when tokens are appended). Mean representative key per page: es 2.B.
+// Host tier gathered over the host link from pinned memory: pt 2.D / es 2.B / it 2.C.
+#include "pkv_device.h"
+
+#pragma clang fp contract(off)
+
+namespace pkv {
+
+// One thread per 16-byte chunk (8 bf16) of K or V.
+__global__ __launch_bounds__(256) void k_append(uint16_t* __restrict__ kv, int32_t n_pool, int32_t P, int32_t H,
+                                                int32_t D, const int32_t* __restrict__ bt, int32_t n_bt,
+                                                int32_t pos0, int32_t n, const uint16_t* __restrict__ k,
+                                                const uint16_t* __restrict__ v, int32_t* err) {
+  const int64_t per = (int64_t)n * H * (D / 8);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= 2 * per) return;
+  const int which = idx >= per;
+  const int64_t c = which ? idx - per : idx;
+  const int32_t dc = (int32_t)(c % (D / 8));
+  const int64_t tg = c / (D / 8);
+  const int32_t g = (int32_t)(tg % H);
+  const int32_t t = (int32_t)(tg / H);
+  const int32_t pos = pos0 + t;
+  const int32_t phys = phys_page(bt, n_bt, n_pool, pos / P, err);
+  if (phys < 0) return;
+  const uint16_t* src = (which ? v : k) + (tg * D + dc * 8);
+  uint16_t* dst = kv + ((((int64_t)phys * H + g) * 2 + which) * P + (pos % P)) * D + dc * 8;
+  *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+}
+
+// Representative key of each page completed by an append: float32 sequential sum over the page's
+// tokens in token order starting from +0.0, times 1/P (exact: P is a power of two).
+__global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ kv, float* __restrict__ rep,
+                                                   int32_t n_pool, int32_t P, int32_t H, int32_t D,
+                                                   const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
+                                                   int32_t n_lp, int32_t* err) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n_lp * H * D) return;
+  const int32_t j = (int32_t)(idx % D);
+  const int32_t g = (int32_t)((idx / D) % H);
+  const int32_t lp = lp0 + (int32_t)(idx / ((int64_t)D * H));
+  const int32_t phys = phys_page(bt, n_bt, n_pool, lp, err);
+  if (phys < 0) return;
+  const uint16_t* kp = kv + (((int64_t)phys * H + g) * 2) * P * D + j;
+  float acc = 0.0f;
+  for (int32_t t = 0; t < P; ++t) acc = __fadd_rn(acc, bf16_to_f32(kp[(int64_t)t * D]));
+  rep[((int64_t)phys * H + g) * D + j] = __fmul_rn(acc, 1.0f / (float)P);
+}
+
+// Zero the gradient blocks of logical pages [lp0, lp0 + n_lp) (bt == NULL: physical = logical).
+__global__ __launch_bounds__(256) void k_zero_grad(float* __restrict__ grad, int32_t n_pool, int32_t P, int32_t H,
+                                                   int32_t D, const int32_t* __restrict__ bt, int32_t n_bt,
+                                                   int32_t lp0, int32_t n_lp, int32_t* err) {
+  const int64_t per_page = (int64_t)H * 2 * P * D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= per_page * n_lp) return;
+  const int32_t lp = lp0 + (int32_t)(idx / per_page);
+  const int32_t phys = bt ? phys_page(bt, n_bt, n_pool, lp, err) : lp;
+  if (phys < 0 || phys >= n_pool) return;
+  reinterpret_cast<f32x4*>(grad)[(int64_t)phys * per_page + idx % per_page] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+// Export K/V (bf16) in logical order: dst[(lp*P + t)*H + g][d].
+__global__ __launch_bounds__(256) void k_export_kv(const uint16_t* __restrict__ kv, int32_t n_pool, int32_t P,
+                                                   int32_t H, int32_t D, int32_t which,
+                                                   const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
+                                                   int32_t n_lp, uint16_t* __restrict__ dst, int32_t* err) {
+  const int64_t total = (int64_t)n_lp * P * H * (D / 8);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int32_t dc = (int32_t)(idx % (D / 8));
+  const int64_t row = idx / (D / 8);  // (lp_rel*P + t)*H + g
+  const int32_t g = (int32_t)(row % H);
+  const int32_t t = (int32_t)((row / H) % P);
+  const int32_t lr = (int32_t)(row / ((int64_t)H * P));
+  const int32_t phys = phys_page(bt, n_bt, n_pool, lp0 + lr, err);
+  u32x4 val = (u32x4){0u, 0u, 0u, 0u};
+  if (phys >= 0)
+    val = *reinterpret_cast<const u32x4*>(kv + ((((int64_t)phys * H + g) * 2 + which) * P + t) * D + dc * 8);
+  *reinterpret_cast<u32x4*>(dst + row * D + dc * 8) = val;
+}
+
+// Export dK/dV (fp32) in logical order.
+__global__ __launch_bounds__(256) void k_export_grad(const float* __restrict__ grad, int32_t n_pool, int32_t P,
+                                                     int32_t H, int32_t D, int32_t which,
+                                                     const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
+                                                     int32_t n_lp, float* __restrict__ dst, int32_t* err) {
+  const int64_t total = (int64_t)n_lp * P * H * (D / 4);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int32_t dc = (int32_t)(idx % (D / 4));
+  const int64_t row = idx / (D / 4);
+  const int32_t g = (int32_t)(row % H);
+  const int32_t t = (int32_t)((row / H) % P);
+  const int32_t lr = (int32_t)(row / ((int64_t)H * P));
+  const int32_t phys = phys_page(bt, n_bt, n_pool, lp0 + lr, err);
+  f32x4 val = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (phys >= 0)
+    val = *reinterpret_cast<const f32x4*>(grad + ((((int64_t)phys * H + g) * 2 + which) * P + t) * D + dc * 4);
+  *reinterpret_cast<f32x4*>(dst + row * D + dc * 4) = val;
+}
+
+// Export representatives [lp][g][d].
+__global__ __launch_bounds__(256) void k_export_rep(const float* __restrict__ rep, int32_t n_pool, int32_t H, int32_t D,
+                                                    const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
+                                                    int32_t n_lp, float* __restrict__ dst, int32_t* err) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n_lp * H * D) return;
+  const int32_t lr = (int32_t)(idx / ((int64_t)H * D));
+  const int32_t phys = phys_page(bt, n_bt, n_pool, lp0 + lr, err);
+  dst[idx] = phys >= 0 ? rep[(int64_t)phys * H * D + idx % ((int64_t)H * D)] : 0.0f;
+}
+
+// Host tier -> device: one workgroup per selected page copies the (page, kvh) K|V block.
+__global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ host_kv, int32_t n_host_pool,
+                                                uint16_t* __restrict__ dev_kv, int32_t n_dev_pool, int32_t P,
+                                                int32_t H, int32_t D, const int32_t* __restrict__ host_bt,
+                                                int32_t n_host_bt, const int32_t* __restrict__ sel,
+                                                const int32_t* __restrict__ dst_pages, int32_t kvh, int32_t* err) {
+  const int32_t i = blockIdx.x;
+  const int32_t hp = phys_page(host_bt, n_host_bt, n_host_pool, sel[i], err);
+  const int32_t dp = dst_pages[i];
+  if (hp < 0) return;
+  if (dp < 0 || dp >= n_dev_pool) {
+    flag_error(err, 4);
+    return;
+  }
+  const int64_t n16 = (int64_t)2 * P * D / 8;  // 16-byte chunks in one (page, head) block
+  const u32x4* src = reinterpret_cast<const u32x4*>(host_kv + ((int64_t)hp * H + kvh) * 2 * P * D);
+  u32x4* dst = reinterpret_cast<u32x4*>(dev_kv + ((int64_t)dp * H + kvh) * 2 * P * D);
+  constexpr int kUnroll = 8;
+  for (int64_t c0 = threadIdx.x; c0 < n16; c0 += 256 * kUnroll) {
+    u32x4 buf[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * 256;
+      if (c < n16) buf[u] = __builtin_nontemporal_load(src + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * 256;
+      if (c < n16) dst[c] = buf[u];
+    }
+  }
+}
+
+static inline unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t pos0, int32_t n,
+                         const uint16_t* k, const uint16_t* v, hipStream_t s) {
+  const int32_t P = pool.page, H = pool.h_kv, D = pool.d;
+  // Pages whose first token is written here get zeroed gradients.
+  const int32_t first_new = (pos0 + P - 1) / P;           // first page starting at or after pos0
+  const int32_t end_new = (pos0 + n + P - 1) / P;         // pages starting before pos0 + n
+  if (pool.grad && end_new > first_new) {
+    const int64_t work = (int64_t)(end_new - first_new) * H * 2 * P * D / 4;
+    hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D, bt,
+                       n_bt, first_new, end_new - first_new, pool.err);
+  }
+  const int64_t chunks = (int64_t)2 * n * H * (D / 8);
+  hipLaunchKernelGGL(k_append, dim3(grid_for(chunks)), dim3(256), 0, s, pool.kv, pool.n_pages, P, H, D, bt, n_bt,
+                     pos0, n, k, v, pool.err);
+  // Pages whose last token is written here get their representative key.
+  const int32_t first_full = pos0 / P;                    // candidate: page containing pos0
+  const int32_t lp_a = ((first_full + 1) * P - 1 >= pos0) ? first_full : first_full + 1;
+  const int32_t lp_b = (pos0 + n) / P;                    // pages fully ending before pos0 + n
+  if (lp_b > lp_a) {
+    const int64_t work = (int64_t)(lp_b - lp_a) * H * D;
+    hipLaunchKernelGGL(k_page_reps, dim3(grid_for(work)), dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, P, H, D,
+                       bt, n_bt, lp_a, lp_b - lp_a, pool.err);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_grad(const pkv_pool& pool, const int32_t* bt, int32_t first_page, int32_t n_pages,
+                            hipStream_t s) {
+  const int64_t work = (int64_t)n_pages * pool.h_kv * 2 * pool.page * pool.d / 4;
+  if (work == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, pool.page,
+                     pool.h_kv, pool.d, bt, first_page + n_pages, first_page, n_pages, pool.err);
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, int32_t first_page,
+                         int32_t n_pages, void* dst, hipStream_t s) {
+  const int32_t P = pool.page, H = pool.h_kv, D = pool.d;
+  const int32_t n_bt = first_page + n_pages;
+  if (what == 0 || what == 1) {
+    const int64_t work = (int64_t)n_pages * P * H * (D / 8);
+    hipLaunchKernelGGL(k_export_kv, dim3(grid_for(work)), dim3(256), 0, s, pool.kv, pool.n_pages, P, H, D, what, bt,
+                       n_bt, first_page, n_pages, (uint16_t*)dst, pool.err);
+  } else if (what == 2 || what == 3) {
+    const int64_t work = (int64_t)n_pages * P * H * (D / 4);
+    hipLaunchKernelGGL(k_export_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D,
+                       what - 2, bt, n_bt, first_page, n_pages, (float*)dst, pool.err);
+  } else {
+    const int64_t work = (int64_t)n_pages * H * D;
+    hipLaunchKernelGGL(k_export_rep, dim3(grid_for(work)), dim3(256), 0, s, pool.rep, pool.n_pages, H, D, bt, n_bt,
+                       first_page, n_pages, (float*)dst, pool.err);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
+                         const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages, hipStream_t s) {
+  if (n_sel == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather, dim3(n_sel), dim3(256), 0, s, host.kv, host.n_pages, dev.kv, dev.n_pages, host.page,
+                     host.h_kv, host.d, host_bt, n_host_bt, sel, dst_pages, kvh, dev.err);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

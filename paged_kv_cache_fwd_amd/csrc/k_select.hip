@@ -1,0 +1,199 @@
+// Page-level top-K selection: query-chunk summary, dot-product page scores against the mean-key
+// representatives, and an exact top-K by (score descending, logical page id ascending).
+//
+// "Out of the Memory Barrier" summaries: es 2.B (a mean representative vector per key page, the
+// most relevant pages for the current queries), pt 2.C (top-K page retrieval approximating dense
+// attention), it 2.D (recent pages kept for natively sparse models).
+//
+// Every float operation here is a single IEEE-rounded add or multiply in a fixed order (this file
+// is compiled with contraction off as well), so the selected ids are reproducible bit for bit:
+//   part[h][b][j] = sum_{t<64} Q[64b+t][h][j];  hsum[h][j] = sum_b part[h][b][j];
+//   qsum[g][j] = sum_{hh<G} hsum[gG+hh][j];      score[g][p] = sum_j qsum[g][j] * rep[p][g][j].
+#include "pkv_device.h"
+
+#pragma clang fp contract(off)
+
+namespace pkv {
+
+// part[h][b][j]: one thread per (h, b, j), 64 sequential adds; lanes run along j (coalesced).
+__global__ __launch_bounds__(256) void k_qsum_part(const uint16_t* __restrict__ q, int32_t H_q, int32_t D,
+                                                   int32_t nb, float* __restrict__ part) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)H_q * nb * D) return;
+  const int32_t j = (int32_t)(idx % D);
+  const int32_t b = (int32_t)((idx / D) % nb);
+  const int32_t h = (int32_t)(idx / ((int64_t)D * nb));
+  const uint16_t* src = q + ((int64_t)(64 * b) * H_q + h) * D + j;
+  float acc = 0.0f;
+#pragma unroll 16
+  for (int32_t t = 0; t < 64; ++t) acc = __fadd_rn(acc, bf16_to_f32(src[(int64_t)t * H_q * D]));
+  part[idx] = acc;
+}
+
+// qsum[g][j]: one thread per (g, j).
+__global__ __launch_bounds__(256) void k_qsum(const float* __restrict__ part, int32_t H_kv, int32_t G, int32_t D,
+                                              int32_t nb, float* __restrict__ qsum) {
+  const int32_t idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= H_kv * D) return;
+  const int32_t j = idx % D, g = idx / D;
+  float qs = 0.0f;
+  for (int32_t hh = 0; hh < G; ++hh) {
+    const float* ph = part + ((int64_t)(g * G + hh) * nb) * D + j;
+    float hs = 0.0f;
+    for (int32_t b = 0; b < nb; ++b) hs = __fadd_rn(hs, ph[(int64_t)b * D]);
+    qs = __fadd_rn(qs, hs);
+  }
+  qsum[idx] = qs;
+}
+
+// score[g][p] for candidate logical pages p < n_cand; an unreadable page scores NaN (ranks last).
+__global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qsum, const float* __restrict__ rep,
+                                                int32_t n_pool, int32_t H_kv, int32_t D,
+                                                const int32_t* __restrict__ bt, int32_t n_bt, int32_t n_cand,
+                                                float* __restrict__ scores, int32_t* err) {
+  const int32_t g = blockIdx.y;
+  const int32_t p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= n_cand) return;
+  const int32_t phys = phys_page(bt, n_bt, n_pool, p, err);
+  float acc = __uint_as_float(0x7fc00000u);
+  if (phys >= 0) {
+    const f32x4* r = reinterpret_cast<const f32x4*>(rep + ((int64_t)phys * H_kv + g) * D);
+    const float* qs = qsum + (int64_t)g * D;
+    acc = 0.0f;
+    for (int32_t j4 = 0; j4 < D / 4; ++j4) {
+      const f32x4 rv = r[j4];
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 0], rv[0]));
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 1], rv[1]));
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 2], rv[2]));
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 3], rv[3]));
+    }
+  }
+  scores[(int64_t)g * n_cand + p] = acc;
+}
+
+// Order key: larger is better. High word: score mapped to an order-preserving unsigned integer
+// (+0 and -0 equal, NaN below everything); low word: ~page id, so equal scores prefer lower ids.
+__device__ __forceinline__ uint64_t order_key(float s, int32_t id) {
+  uint32_t hi;
+  if (s != s) {
+    hi = 0u;
+  } else {
+    uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);
+    hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)hi << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+constexpr int kSelThreads = 1024;
+
+// One workgroup per KV head: radix select (8 passes of 8 bits, most significant first) finds the
+// K-th largest order key exactly; the winners are then compacted in ascending id order with a
+// block-wide ballot scan, and the local pages are appended.
+__global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ scores, int32_t n_cand,
+                                                      int32_t K, int32_t n_prior, int32_t n_sel,
+                                                      int32_t* __restrict__ sel) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t s_prefix, s_mask;
+  __shared__ uint32_t s_remaining;
+  __shared__ uint32_t wave_tot[kSelThreads / 64];
+  const int32_t g = blockIdx.x;
+  const int32_t tid = threadIdx.x;
+  const float* sc = scores + (int64_t)g * n_cand;
+  int32_t* out = sel + (int64_t)g * n_sel;
+
+  uint64_t threshold = 0;  // select keys >= threshold
+  const bool take_all = (K >= n_cand);
+  if (!take_all && K > 0) {
+    if (tid == 0) {
+      s_prefix = 0;
+      s_mask = 0;
+      s_remaining = (uint32_t)K;
+    }
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0u;
+      __syncthreads();
+      const uint64_t prefix = s_prefix, mask = s_mask;
+      for (int32_t i = tid; i < n_cand; i += kSelThreads) {
+        const uint64_t key = order_key(sc[i], i);
+        if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t cum = 0, rem = s_remaining;
+        for (int dg = 255; dg >= 0; --dg) {
+          const uint32_t c = hist[dg];
+          if (cum + c >= rem) {
+            s_prefix = prefix | ((uint64_t)dg << shift);
+            s_remaining = rem - cum;
+            break;
+          }
+          cum += c;
+        }
+        s_mask = mask | ((uint64_t)255 << shift);
+      }
+      __syncthreads();
+    }
+    threshold = s_prefix;
+  }
+  const int32_t kk = take_all ? n_cand : K;
+  // Compaction in id order.
+  const int lane = tid & 63, wave = tid >> 6;
+  int32_t base = 0;
+  if (kk > 0) {
+    for (int32_t c0 = 0; c0 < n_cand; c0 += kSelThreads) {
+      const int32_t i = c0 + tid;
+      const bool f = (i < n_cand) && (take_all || order_key(sc[i], i) >= threshold);
+      const uint64_t ball = __ballot(f);
+      const uint32_t before = __popcll(ball & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_tot[wave] = __popcll(ball);
+      __syncthreads();
+      uint32_t wbase = 0, total = 0;
+      for (int w = 0; w < kSelThreads / 64; ++w) {
+        const uint32_t t = wave_tot[w];
+        wbase += (w < wave) ? t : 0u;
+        total += t;
+      }
+      if (f) {
+        const int32_t pos = base + (int32_t)(wbase + before);
+        if (pos < kk) out[pos] = i;
+      }
+      base += (int32_t)total;
+      __syncthreads();
+    }
+  }
+  for (int32_t u = tid; u < n_prior - n_cand; u += kSelThreads) out[kk + u] = n_cand + u;
+}
+
+size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d) {
+  const size_t nb = (size_t)C / 64;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return al((size_t)h_q * nb * d * 4) + al((size_t)h_kv * d * 4) + al((size_t)h_kv * (size_t)(n_cand > 0 ? n_cand : 1) * 4);
+}
+
+hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const uint16_t* q,
+                       int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t* sel, void* ws,
+                       hipStream_t s) {
+  const int32_t H = pool.h_kv, D = pool.d, G = h_q / H;
+  const int32_t nb = C / 64;
+  const int32_t n_cand = n_prior > n_local ? n_prior - n_local : 0;
+  const int32_t K = top_k < n_cand ? top_k : n_cand;
+  const int32_t n_sel = K + (n_prior - n_cand);
+  if (n_sel == 0) return hipSuccess;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* w = (char*)ws;
+  float* part = (float*)w;
+  float* qsum = (float*)(w + al((size_t)h_q * nb * D * 4));
+  float* scores = (float*)(w + al((size_t)h_q * nb * D * 4) + al((size_t)H * D * 4));
+  if (n_cand > 0 && K > 0 && K < n_cand) {
+    const int64_t n1 = (int64_t)h_q * nb * D;
+    hipLaunchKernelGGL(k_qsum_part, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, q, h_q, D, nb, part);
+    hipLaunchKernelGGL(k_qsum, dim3((unsigned)((H * D + 255) / 256)), dim3(256), 0, s, part, H, G, D, nb, qsum);
+    hipLaunchKernelGGL(k_scores, dim3((unsigned)((n_cand + 255) / 256), H), dim3(256), 0, s, qsum, pool.rep,
+                       pool.n_pages, H, D, bt, n_bt, n_cand, scores, pool.err);
+  }
+  hipLaunchKernelGGL(k_topk, dim3(H), dim3(kSelThreads), 0, s, scores, n_cand, K, n_prior, n_sel, sel);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

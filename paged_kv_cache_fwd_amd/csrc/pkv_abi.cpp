@@ -1,0 +1,512 @@
+// C ABI of the paged chunk-attention library: argument validation, pool management and launch
+// planning. Every check happens before anything is enqueued; kernels live in the *.hip files.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void ok() { g_err.clear(); }
+
+bool supported(int32_t page, int32_t d) { return (page == 64 || page == 128) && (d == 64 || d == 128); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t kv_bytes(const pkv_pool& p) { return (size_t)p.n_pages * p.h_kv * 2 * p.page * p.d * sizeof(uint16_t); }
+size_t grad_bytes(const pkv_pool& p) { return (size_t)p.n_pages * p.h_kv * 2 * p.page * p.d * sizeof(float); }
+size_t rep_bytes(const pkv_pool& p) { return (size_t)p.n_pages * p.h_kv * p.d * sizeof(float); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shared checks of chunk_attn_fwd / chunk_attn_bwd.
+int check_attn(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const int32_t* sel,
+               int32_t n_sel, int32_t kvh0, int32_t n_kvh, const uint16_t* q, int32_t C, int32_t H_q,
+               float scale) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (pool->flags & PKV_HOST_TIER)
+    return fail(PKV_E_STATE, "attention reads device pages; gather host-tier pages into a device pool first");
+  if (!bt) return fail(PKV_E_INVALID, "block table is NULL");
+  if (!q) return fail(PKV_E_INVALID, "q is NULL");
+  if (!aligned16(q)) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
+  if (C <= 0 || C % pool->page != 0) return fail(PKV_E_INVALID, "C=%d must be a positive multiple of the page size %d", C, pool->page);
+  if (H_q <= 0 || H_q % pool->h_kv != 0) return fail(PKV_E_INVALID, "H_q=%d must be a positive multiple of H_kv=%d", H_q, pool->h_kv);
+  if ((int64_t)C * (H_q / pool->h_kv) > (int64_t)1 << 30) return fail(PKV_E_INVALID, "chunk too large");
+  if (n_prior < 0) return fail(PKV_E_INVALID, "n_prior < 0");
+  if (n_bt < 0 || (int64_t)n_prior + C / pool->page > n_bt)
+    return fail(PKV_E_RANGE, "pages [0, %d) exceed the block table (%d entries)", n_prior + C / pool->page, n_bt);
+  if ((int64_t)(n_prior + C / pool->page) * pool->page > (int64_t)1 << 30) return fail(PKV_E_RANGE, "context too long");
+  if (kvh0 < 0 || n_kvh <= 0 || kvh0 + n_kvh > pool->h_kv)
+    return fail(PKV_E_INVALID, "KV head range [%d, %d) outside [0, %d)", kvh0, kvh0 + n_kvh, pool->h_kv);
+  if (sel) {
+    if (n_sel < 0 || n_sel > n_prior) return fail(PKV_E_INVALID, "n_sel=%d must be in [0, n_prior=%d]", n_sel, n_prior);
+  }
+  if (!std::isfinite(scale)) return fail(PKV_E_INVALID, "scale is not finite");
+  return PKV_OK;
+}
+
+pkv::AttnArgs make_args(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const int32_t* sel,
+                        int32_t n_sel, int32_t kvh0, int32_t n_kvh, const uint16_t* q, int32_t C, int32_t H_q,
+                        float scale) {
+  pkv::AttnArgs a;
+  a.kv = pool->kv;
+  a.n_pool_pages = pool->n_pages;
+  a.page = pool->page;
+  a.h_kv = pool->h_kv;
+  a.d = pool->d;
+  a.bt = bt;
+  a.n_bt = n_bt;
+  a.n_prior = n_prior;
+  a.sel = sel;
+  a.n_sel = sel ? n_sel : 0;
+  a.kvh0 = kvh0;
+  a.n_kvh = n_kvh;
+  a.q = q;
+  a.C = C;
+  a.h_q = H_q;
+  a.G = H_q / pool->h_kv;
+  a.scale = scale;
+  a.err = pool->err;
+  return a;
+}
+
+}  // namespace
+
+namespace pkv {
+
+int num_cus() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cached = n;
+    else
+      cached = 256;
+  }
+  return cached;
+}
+
+// Pick the key-range split count: a workgroup costs (its tiles + fixed overhead), and workgroups
+// run one per CU in waves, so minimise waves * per-workgroup cost.
+static int32_t best_split(int64_t base_units, double tiles, double overhead, int32_t max_split) {
+  const int64_t slots = num_cus();
+  int32_t best = 1;
+  double best_cost = 1e300;
+  for (int32_t s = 1; s <= max_split; ++s) {
+    const double waves = std::ceil((double)(base_units * s) / (double)slots);
+    const double cost = waves * (std::ceil(tiles / s) + overhead) + (s > 1 ? 1.0 : 0.0);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
+FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d) {
+  FwdPlan p;
+  const int64_t rows = (int64_t)C * G;
+  p.n_rb = (int32_t)((rows + 255) / 256);
+  const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
+  const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
+  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split);
+  p.ws_bytes = p.splits > 1 ? align256((size_t)p.splits * n_kvh * rows * d * 4) + align256((size_t)p.splits * n_kvh * rows * 4) : 0;
+  return p;
+}
+
+BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d) {
+  BwdPlan p;
+  const int64_t rows = (int64_t)C * G;
+  p.n_rb = (int32_t)((rows + 255) / 256);
+  const double tiles = (double)n_list_pages * (page / 32) + (C / 32 + 1) / 2.0;
+  const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
+  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 4.0, max_split);
+  const int64_t n_kt = (int64_t)(n_list_pages + C / page) * (page / 32);
+  p.n_ku = (int32_t)((n_kt + 3) / 4);
+  const int64_t n_blk = (rows + 63) / 64;
+  const int32_t max_rs = (int32_t)std::min<int64_t>(64, n_blk);
+  p.row_splits = best_split((int64_t)n_kvh * p.n_ku, (double)n_blk, 2.0, max_rs);
+  // [H_q][C] row dots (H_q = n_kvh*G is enough for the heads computed, but the buffer is indexed by
+  // absolute head, so size it for every head the pool can address), then dQ partials.
+  p.ws_bytes = 0;  // filled by the caller, which knows H_q
+  (void)d;
+  return p;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n_kv_heads, int32_t head_dim,
+                   uint32_t flags) {
+  if (!out) return fail(PKV_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (n_pages <= 0 || n_kv_heads <= 0) return fail(PKV_E_INVALID, "n_pages and n_kv_heads must be positive");
+  if (!supported(page_size, head_dim))
+    return fail(PKV_E_UNSUPPORTED, "page_size %d / head_dim %d not supported (both must be 64 or 128)", page_size,
+                head_dim);
+  if (flags & ~(PKV_GRADS | PKV_HOST_TIER)) return fail(PKV_E_INVALID, "unknown flags 0x%x", flags);
+  pkv_pool* p = new (std::nothrow) pkv_pool();
+  if (!p) return fail(PKV_E_NOMEM, "out of host memory");
+  p->n_pages = n_pages;
+  p->page = page_size;
+  p->h_kv = n_kv_heads;
+  p->d = head_dim;
+  p->flags = flags;
+  p->kv = nullptr;
+  p->kv_host = nullptr;
+  p->grad = nullptr;
+  p->rep = nullptr;
+  p->err = nullptr;
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  auto cleanup = [&]() {
+    if (p->kv_host) (void)hipHostFree(p->kv_host);
+    else if (p->kv) (void)hipFree(p->kv);
+    if (p->grad) (void)hipFree(p->grad);
+    if (p->rep) (void)hipFree(p->rep);
+    if (p->err) (void)hipFree(p->err);
+    delete p;
+  };
+  if (getenv("PKV_FAIL_HOST_ALLOC") && (flags & PKV_HOST_TIER)) {
+    cleanup();
+    return fail(PKV_E_NOMEM, "pinned host allocation failed (injected by PKV_FAIL_HOST_ALLOC)");
+  }
+  if (flags & PKV_HOST_TIER) {
+    e = hipHostMalloc(&p->kv_host, kv_bytes(*p), hipHostMallocMapped | hipHostMallocPortable);
+    if (e != hipSuccess) {
+      p->kv_host = nullptr;
+      (void)hipGetLastError();
+      cleanup();
+      return fail(PKV_E_NOMEM, "hipHostMalloc(%zu bytes): %s", kv_bytes(*p), hipGetErrorString(e));
+    }
+    void* dptr = nullptr;
+    e = hipHostGetDevicePointer(&dptr, p->kv_host, 0);
+    if (e != hipSuccess) {
+      cleanup();
+      return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    p->kv = (uint16_t*)dptr;
+    memset(p->kv_host, 0, kv_bytes(*p));
+  } else {
+    e = hipMalloc((void**)&p->kv, kv_bytes(*p));
+    if (e != hipSuccess) {
+      p->kv = nullptr;
+      (void)hipGetLastError();
+      cleanup();
+      return fail(PKV_E_NOMEM, "hipMalloc(%zu bytes) for KV pages: %s", kv_bytes(*p), hipGetErrorString(e));
+    }
+    e = hipMemset(p->kv, 0, kv_bytes(*p));
+    if (e != hipSuccess) {
+      cleanup();
+      return hip_fail(e, "hipMemset(kv)");
+    }
+  }
+  if (flags & PKV_GRADS) {
+    e = hipMalloc((void**)&p->grad, grad_bytes(*p));
+    if (e != hipSuccess) {
+      p->grad = nullptr;
+      (void)hipGetLastError();
+      cleanup();
+      return fail(PKV_E_NOMEM, "hipMalloc(%zu bytes) for gradient pages: %s", grad_bytes(*p), hipGetErrorString(e));
+    }
+    e = hipMemset(p->grad, 0, grad_bytes(*p));
+    if (e != hipSuccess) {
+      cleanup();
+      return hip_fail(e, "hipMemset(grad)");
+    }
+  }
+  e = hipMalloc((void**)&p->rep, rep_bytes(*p));
+  if (e == hipSuccess) e = hipMemset(p->rep, 0, rep_bytes(*p));
+  if (e == hipSuccess) e = hipMalloc((void**)&p->err, 256);
+  if (e == hipSuccess) e = hipMemset(p->err, 0, 256);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    cleanup();
+    return fail(PKV_E_NOMEM, "device allocation failed: %s", hipGetErrorString(e));
+  }
+  *out = p;
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_free(pkv_pool* pool) {
+  if (!pool) {
+    ok();
+    return PKV_OK;
+  }
+  hipError_t e = hipDeviceSynchronize();
+  if (pool->kv_host) (void)hipHostFree(pool->kv_host);
+  else if (pool->kv) (void)hipFree(pool->kv);
+  if (pool->grad) (void)hipFree(pool->grad);
+  if (pool->rep) (void)hipFree(pool->rep);
+  if (pool->err) (void)hipFree(pool->err);
+  delete pool;
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize in paged_kv_free");
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_info(const pkv_pool* pool, int32_t* n_pages, int32_t* page_size, int32_t* n_kv_heads,
+                  int32_t* head_dim, uint32_t* flags) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (n_pages) *n_pages = pool->n_pages;
+  if (page_size) *page_size = pool->page;
+  if (n_kv_heads) *n_kv_heads = pool->h_kv;
+  if (head_dim) *head_dim = pool->d;
+  if (flags) *flags = pool->flags;
+  ok();
+  return PKV_OK;
+}
+
+void* paged_kv_data(const pkv_pool* pool, int32_t what) {
+  if (!pool) {
+    fail(PKV_E_INVALID, "pool is NULL");
+    return nullptr;
+  }
+  ok();
+  switch (what) {
+    case PKV_K:
+    case PKV_V:
+      return pool->kv;
+    case PKV_DK:
+    case PKV_DV:
+      if (!pool->grad) fail(PKV_E_STATE, "pool has no gradient pages");
+      return pool->grad;
+    case PKV_REP:
+      return pool->rep;
+    default:
+      fail(PKV_E_INVALID, "unknown array selector %d", what);
+      return nullptr;
+  }
+}
+
+int paged_kv_append(pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t pos0, int32_t n_tokens,
+                    const uint16_t* k_dev, const uint16_t* v_dev, void* stream) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (!bt_dev || !k_dev || !v_dev) return fail(PKV_E_INVALID, "NULL block table, k or v");
+  if (!aligned16(k_dev) || !aligned16(v_dev)) return fail(PKV_E_INVALID, "k and v must be 16-byte aligned");
+  if (pos0 < 0 || n_tokens < 0) return fail(PKV_E_INVALID, "pos0 and n_tokens must be >= 0");
+  if (n_bt < 0 || (int64_t)pos0 + n_tokens > (int64_t)n_bt * pool->page)
+    return fail(PKV_E_RANGE, "positions [%d, %lld) exceed the block table (%d pages of %d)", pos0,
+                (long long)pos0 + n_tokens, n_bt, pool->page);
+  if (n_tokens == 0) {
+    ok();
+    return PKV_OK;
+  }
+  hipError_t e = pkv::launch_append(*pool, bt_dev, n_bt, pos0, n_tokens, k_dev, v_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_zero_grad(pkv_pool* pool, const int32_t* bt_dev, int32_t n_pages, void* stream) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (!pool->grad) return fail(PKV_E_STATE, "pool has no gradient pages");
+  int32_t n = n_pages;
+  if (!bt_dev) n = pool->n_pages;
+  if (n < 0) return fail(PKV_E_INVALID, "n_pages < 0");
+  hipError_t e = pkv::launch_zero_grad(*pool, bt_dev, 0, n, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "zero_grad launch");
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_export(const pkv_pool* pool, int32_t what, const int32_t* bt_dev, int32_t n_bt, int32_t first_page,
+                    int32_t n_pages, void* dst_dev, void* stream) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (!bt_dev || !dst_dev) return fail(PKV_E_INVALID, "NULL block table or destination");
+  if (what < PKV_K || what > PKV_REP) return fail(PKV_E_INVALID, "unknown array selector %d", what);
+  if ((what == PKV_DK || what == PKV_DV) && !pool->grad) return fail(PKV_E_STATE, "pool has no gradient pages");
+  if (first_page < 0 || n_pages < 0 || (int64_t)first_page + n_pages > n_bt)
+    return fail(PKV_E_RANGE, "pages [%d, %lld) exceed the block table (%d)", first_page,
+                (long long)first_page + n_pages, n_bt);
+  if (!aligned16(dst_dev)) return fail(PKV_E_INVALID, "destination must be 16-byte aligned");
+  if (n_pages == 0) {
+    ok();
+    return PKV_OK;
+  }
+  hipError_t e = pkv::launch_export(*pool, what, bt_dev, first_page, n_pages, dst_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "export launch");
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_check(pkv_pool* pool) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  int32_t word = 0;
+  e = hipMemcpy(&word, pool->err, sizeof(word), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "reading the error word");
+  if (word != 0) {
+    const int32_t zero = 0;
+    e = hipMemcpy(pool->err, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "clearing the error word");
+    const char* what = word == 1   ? "block-table entry outside the pool"
+                       : word == 2 ? "selected page outside [0, n_prior)"
+                       : word == 3 ? "logical page beyond the block table"
+                                   : "gather destination outside the device pool";
+    return fail(PKV_E_DEVICE, "a kernel skipped a page: %s", what);
+  }
+  ok();
+  return PKV_OK;
+}
+
+size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int32_t H_q) {
+  if (!pool || C <= 0 || H_q <= 0 || n_prior < 0) return 0;
+  return pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d);
+}
+
+int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
+                     const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
+                     int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (!bt_dev || !q_dev || !n_sel_out) return fail(PKV_E_INVALID, "NULL block table, q or n_sel_out");
+  if (C <= 0 || C % 64 != 0) return fail(PKV_E_INVALID, "C=%d must be a positive multiple of 64", C);
+  if (H_q <= 0 || H_q % pool->h_kv != 0) return fail(PKV_E_INVALID, "H_q=%d must be a multiple of H_kv=%d", H_q, pool->h_kv);
+  if (top_k < 0 || n_local < 0 || n_prior < 0) return fail(PKV_E_INVALID, "top_k, n_local, n_prior must be >= 0");
+  if (n_prior > n_bt) return fail(PKV_E_RANGE, "n_prior=%d exceeds the block table (%d)", n_prior, n_bt);
+  const int32_t n_cand = n_prior > n_local ? n_prior - n_local : 0;
+  const int32_t kk = std::min(top_k, n_cand);
+  const int32_t n_sel = kk + (n_prior - n_cand);
+  if (n_sel > 0 && !sel_dev) return fail(PKV_E_INVALID, "sel is NULL");
+  if (ws_bytes < pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d) || (!ws_dev && kk > 0 && kk < n_cand))
+    return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes,
+                pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d));
+  *n_sel_out = n_sel;
+  hipError_t e = pkv::launch_topk(*pool, bt_dev, n_bt, n_prior, q_dev, C, H_q, top_k, n_local, sel_dev, ws_dev,
+                                  (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  ok();
+  return PKV_OK;
+}
+
+size_t chunk_attn_fwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh, int32_t C,
+                               int32_t H_q) {
+  if (!pool || C <= 0 || H_q <= 0 || n_kvh <= 0 || H_q % pool->h_kv != 0) return 0;
+  const int32_t n_list = n_sel >= 0 ? n_sel : n_prior;
+  return pkv::plan_fwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d).ws_bytes;
+}
+
+int chunk_attn_fwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior, const int32_t* sel_dev,
+                   int32_t n_sel, int32_t kvh0, int32_t n_kvh, const uint16_t* q_dev, int32_t C, int32_t H_q,
+                   float scale, uint16_t* o_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  int rc = check_attn(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+  if (rc != PKV_OK) return rc;
+  if (!o_dev || !lse_dev) return fail(PKV_E_INVALID, "NULL o or lse");
+  if (!aligned16(o_dev)) return fail(PKV_E_INVALID, "o must be 16-byte aligned");
+  const int32_t n_list = sel_dev ? n_sel : n_prior;
+  const pkv::FwdPlan plan = pkv::plan_fwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d);
+  if (plan.ws_bytes > 0 && (!ws_dev || ws_bytes < plan.ws_bytes))
+    return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+  const pkv::AttnArgs a = make_args(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+  hipError_t e = pkv::launch_fwd(a, plan, o_dev, lse_dev, ws_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  ok();
+  return PKV_OK;
+}
+
+static size_t bwd_ws(const pkv_pool* pool, const pkv::BwdPlan& plan, int32_t n_kvh, int32_t C, int32_t H_q) {
+  const size_t dbytes = (((size_t)H_q * C + 63) & ~(size_t)63) * 4;
+  const size_t dq = plan.splits > 1 ? (size_t)plan.splits * n_kvh * C * (H_q / pool->h_kv) * pool->d * 4 : 0;
+  return align256(dbytes + dq);
+}
+
+size_t chunk_attn_bwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh, int32_t C,
+                               int32_t H_q) {
+  if (!pool || C <= 0 || H_q <= 0 || n_kvh <= 0 || H_q % pool->h_kv != 0) return 0;
+  const int32_t n_list = n_sel >= 0 ? n_sel : n_prior;
+  const pkv::BwdPlan plan = pkv::plan_bwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d);
+  return bwd_ws(pool, plan, n_kvh, C, H_q);
+}
+
+int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, pkv_pool* gpool, const int32_t* gbt_dev,
+                   int32_t n_gbt, int32_t n_prior, const int32_t* sel_dev, int32_t n_sel, int32_t kvh0, int32_t n_kvh,
+                   const uint16_t* q_dev, const uint16_t* o_dev, const uint16_t* dout_dev, const float* lse_dev,
+                   int32_t C, int32_t H_q, float scale, uint16_t* dq_dev, void* ws_dev, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_attn(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+  if (rc != PKV_OK) return rc;
+  if (!gpool) return fail(PKV_E_INVALID, "gradient pool is NULL");
+  if (!gpool->grad) return fail(PKV_E_STATE, "gradient pool has no gradient pages");
+  if (gpool->page != pool->page || gpool->h_kv != pool->h_kv || gpool->d != pool->d)
+    return fail(PKV_E_INVALID, "gradient pool shape differs from the KV pool");
+  if (!gbt_dev) return fail(PKV_E_INVALID, "gradient block table is NULL");
+  if ((int64_t)n_prior + C / pool->page > n_gbt)
+    return fail(PKV_E_RANGE, "pages [0, %d) exceed the gradient block table (%d)", n_prior + C / pool->page, n_gbt);
+  if (!o_dev || !dout_dev || !lse_dev || !dq_dev) return fail(PKV_E_INVALID, "NULL o, dout, lse or dq");
+  if (!aligned16(o_dev) || !aligned16(dout_dev) || !aligned16(dq_dev))
+    return fail(PKV_E_INVALID, "o, dout and dq must be 16-byte aligned");
+  const int32_t n_list = sel_dev ? n_sel : n_prior;
+  const pkv::BwdPlan plan = pkv::plan_bwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d);
+  const size_t need = bwd_ws(pool, plan, n_kvh, C, H_q);
+  if (!ws_dev || ws_bytes < need) return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  const pkv::AttnArgs a = make_args(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+  pkv::BwdExtra x;
+  x.o = o_dev;
+  x.dout = dout_dev;
+  x.lse = lse_dev;
+  x.dq = dq_dev;
+  x.grad = gpool->grad;
+  x.gbt = gbt_dev;
+  x.n_gbt = n_gbt;
+  x.n_gpool_pages = gpool->n_pages;
+  hipError_t e = pkv::launch_bwd(a, x, plan, ws_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_dev, int32_t n_host_bt,
+                    const int32_t* sel_dev, int32_t n_sel, int32_t kvh, const int32_t* dst_pages_dev, void* stream) {
+  if (!host || !dev) return fail(PKV_E_INVALID, "NULL pool");
+  if (!(host->flags & PKV_HOST_TIER)) return fail(PKV_E_STATE, "source pool is not a host-tier pool");
+  if (dev->flags & PKV_HOST_TIER) return fail(PKV_E_STATE, "destination pool must be a device pool");
+  if (host->page != dev->page || host->h_kv != dev->h_kv || host->d != dev->d)
+    return fail(PKV_E_INVALID, "pool shapes differ");
+  if (kvh < 0 || kvh >= host->h_kv) return fail(PKV_E_INVALID, "kvh=%d outside [0, %d)", kvh, host->h_kv);
+  if (n_sel < 0) return fail(PKV_E_INVALID, "n_sel < 0");
+  if (n_sel > 0 && (!host_bt_dev || !sel_dev || !dst_pages_dev)) return fail(PKV_E_INVALID, "NULL table");
+  hipError_t e = pkv::launch_gather(*host, *dev, host_bt_dev, n_host_bt, sel_dev, n_sel, kvh, dst_pages_dev,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  ok();
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Device helpers for the gfx950 kernels: vector types, bf16 packing, MFMA wrappers, page lookup.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round-to-nearest-even float -> bf16 (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// D(32x32, fp32) += A(32x16) * B(16x32), bf16 inputs. Lane l supplies A row l%32 and B column l%32,
+// eight consecutive contraction indices from 8*(l/32). Accumulator element i of lane l holds row
+// 8*(i/4) + 4*(l/32) + (i%4), column l%32.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// Record an out-of-range table entry (first writer wins; the value is informational).
+__device__ __forceinline__ void flag_error(int32_t* err, int32_t code) {
+  if (err) atomicCAS(err, 0, code);
+}
+
+// Logical page of entry pi of a chunk's key-page list for KV head g: the prior part (all of
+// [0, n_prior) when dense, else the selected pages) followed by the chunk's own pages.
+// Returns -1 (and flags) for an out-of-range selection entry.
+__device__ __forceinline__ int32_t list_page(const AttnArgs& a, int32_t g, int32_t pi) {
+  if (a.sel == nullptr) return pi;
+  if (pi < a.n_sel) {
+    int32_t lp = a.sel[(size_t)g * a.n_sel + pi];
+    if (lp < 0 || lp >= a.n_prior) {
+      flag_error(a.err, 2);
+      return -1;
+    }
+    return lp;
+  }
+  return a.n_prior + (pi - a.n_sel);
+}
+
+// Physical page of a logical page through the block table, -1 (flagged) if out of range.
+__device__ __forceinline__ int32_t phys_page(const int32_t* bt, int32_t n_bt, int32_t n_pool, int32_t lp,
+                                             int32_t* err) {
+  if (lp < 0) return -1;
+  if (lp >= n_bt) {
+    flag_error(err, 3);
+    return -1;
+  }
+  int32_t p = bt[lp];
+  if (p < 0 || p >= n_pool) {
+    flag_error(err, 1);
+    return -1;
+  }
+  return p;
+}
+
+// Number of prior pages in the key list (selected count when sparse).
+__device__ __forceinline__ int32_t list_prior(const AttnArgs& a) { return a.sel ? a.n_sel : a.n_prior; }
+
+// XCD-aware block ordering: workgroups are dispatched round-robin over 8 XCDs, so consecutive
+// logical units are gathered onto one XCD (sharing its L2). Bijective on [0, n).
+__device__ __forceinline__ int32_t xcd_remap(int32_t bid, int32_t n) {
+  const int32_t x = bid & 7, k = bid >> 3;
+  const int32_t q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
+}  // namespace pkv

@@ -1,0 +1,91 @@
+// Internal declarations shared by the host ABI (pkv_abi.cpp) and the kernel files (*.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+struct pkv_pool {
+  int32_t n_pages;
+  int32_t page;
+  int32_t h_kv;
+  int32_t d;
+  uint32_t flags;
+  int device;
+  uint16_t* kv;       // device address of the bf16 KV pages (device-mapped pinned host for host tier)
+  void* kv_host;      // host allocation of a host-tier pool (NULL otherwise)
+  float* grad;        // fp32 gradient pages (NULL without PKV_GRADS)
+  float* rep;         // fp32 representative key per (page, head)
+  int32_t* err;       // device word: nonzero once a kernel met an out-of-range table entry
+};
+
+namespace pkv {
+
+// Everything a chunk-attention kernel needs to walk one chunk's key list.
+struct AttnArgs {
+  const uint16_t* kv;
+  int32_t n_pool_pages;
+  int32_t page;
+  int32_t h_kv;
+  int32_t d;
+  const int32_t* bt;
+  int32_t n_bt;
+  int32_t n_prior;
+  const int32_t* sel;  // NULL = dense
+  int32_t n_sel;
+  int32_t kvh0;
+  int32_t n_kvh;
+  const uint16_t* q;
+  int32_t C;
+  int32_t h_q;
+  int32_t G;
+  float scale;
+  int32_t* err;
+};
+
+struct BwdExtra {
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  float* grad;          // gradient pool base
+  const int32_t* gbt;   // gradient block table
+  int32_t n_gbt;
+  int32_t n_gpool_pages;
+};
+
+// Launch-shape decisions, computed on the host from the shapes alone.
+struct FwdPlan {
+  int32_t n_rb;       // row blocks of 256 rows per KV head
+  int32_t splits;     // key-range splits (>1 needs the combine kernel and workspace)
+  size_t ws_bytes;
+};
+struct BwdPlan {
+  int32_t n_rb;        // dQ pass: row blocks of 256 rows per KV head
+  int32_t splits;      // dQ pass: key-range splits
+  int32_t n_ku;        // dK/dV pass: key units of 128 keys per KV head
+  int32_t row_splits;  // dK/dV pass: row-range splits
+  size_t ws_bytes;
+};
+
+int num_cus();
+FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
+BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
+
+hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t pos0, int32_t n,
+                         const uint16_t* k, const uint16_t* v, hipStream_t s);
+hipError_t launch_zero_grad(const pkv_pool& pool, const int32_t* bt, int32_t first_page, int32_t n_pages,
+                            hipStream_t s);
+hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, int32_t first_page,
+                         int32_t n_pages, void* dst, hipStream_t s);
+hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
+                         const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages,
+                         hipStream_t s);
+size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d);
+hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const uint16_t* q,
+                       int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t* sel, void* ws,
+                       hipStream_t s);
+hipError_t launch_fwd(const AttnArgs& a, const FwdPlan& plan, uint16_t* o, float* lse, void* ws, hipStream_t s);
+hipError_t launch_bwd(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, void* ws, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,240 @@
+"""GPU parity: HIP path (through the C ABI) against the CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (ATOL_GRAD, ATOL_LSE, ATOL_O, compare, fill_pool, host, i32, say, scatter_grads, t16)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_fwd_amd as m
+    m.load()
+    return m
+
+
+def _run_chunks(pkv, wl, bt_np, sel_fn=None, chunks=None):
+    """Append everything, run fwd+bwd for the chunks in order; return per-chunk outputs and grads."""
+    L = wl.context
+    pool, bt = fill_pool(pkv, wl, wl.n_pages, bt_np)
+    outs = []
+    for c in (chunks or wl.chunks):
+        n_prior = wl.n_prior(c)
+        q, do = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+        sel = sel_fn(c, n_prior) if sel_fn else None
+        sel_t = i32(sel) if sel is not None else None
+        o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, t16(q), wl.scale, sel=sel_t)
+        dq = pkv.chunk_attn_bwd(pool, bt, n_prior, t16(q), o, t16(do), lse, wl.scale, sel=sel_t)
+        outs.append((c, sel, host(o), lse.cpu().numpy(), host(dq)))
+    dk = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy()
+    dv = pool.export(pkv.PKV_DV, bt, 0, wl.n_pages).cpu().numpy()
+    torch.cuda.synchronize()
+    pool.check()
+    pool.free()
+    return outs, dk, dv
+
+
+def _check_against_oracle(wl, outs, dk, dv, page):
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    dk_ref = np.zeros((wl.context, wl.h_kv, wl.d))
+    dv_ref = np.zeros_like(dk_ref)
+    for c, sel, o, lse, dq in outs:
+        q, do = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+        say(f"chunk {c}:")
+        ref = oracle.chunk_backward(q, k, v, do, wl.q0(c), wl.scale, sel=sel, page=page)
+        compare("O", o, ref["o"], ATOL_O)
+        compare("LSE", lse, ref["lse"], ATOL_LSE, rel=1e-5)
+        compare("dQ", dq, ref["dq"], ATOL_GRAD)
+        a, b = scatter_grads(ref, wl.context, wl.h_kv, wl.d)
+        dk_ref += a
+        dv_ref += b
+    say("accumulated over chunks:")
+    compare("dK", dk, dk_ref, ATOL_GRAD)
+    compare("dV", dv, dv_ref, ATOL_GRAD)
+
+
+def test_tiny_all_chunks_dense(pkv):
+    """4/1 heads, d=64, 2048 tokens as 4x512, page 64, seeded page permutation, dense."""
+    wl = synth.WORKLOADS["tiny"]
+    say("case tiny dense seed 0")
+    outs, dk, dv = _run_chunks(pkv, wl, synth.page_permutation(wl))
+    _check_against_oracle(wl, outs, dk, dv, wl.page)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_tiny_other_seeds(pkv, seed):
+    wl = synth.WORKLOADS["tiny"].with_seed(seed)
+    say(f"case tiny dense seed {seed}")
+    outs, dk, dv = _run_chunks(pkv, wl, synth.page_permutation(wl))
+    _check_against_oracle(wl, outs, dk, dv, wl.page)
+
+
+def _mid(seed=0, G=7, h_kv=2, C=384, chunks=(0, 1, 2), d=128, page=128, offset=0.5):
+    # 2688 rows per KV head (10.5 blocks of 256): spans several tiles and a ragged tail.
+    return synth.Workload("mid", G * h_kv, h_kv, d, page, C * len(chunks), C, tuple(chunks), offset_std=offset,
+                          seed=seed)
+
+
+def test_mid_gqa7_ragged_dense(pkv):
+    wl = _mid()
+    say("case mid 14/2 heads d=128 page 128 C=384 dense")
+    outs, dk, dv = _run_chunks(pkv, wl, synth.page_permutation(wl))
+    _check_against_oracle(wl, outs, dk, dv, wl.page)
+
+
+def test_mid_sparse_selection(pkv):
+    wl = _mid(seed=3, chunks=(0, 1, 2, 3))
+    say("case mid sparse (fixed selections)")
+
+    def sel_fn(c, n_prior):
+        if n_prior == 0:
+            return np.zeros((wl.h_kv, 0), np.int32)
+        rng = np.random.default_rng(100 + c)
+        k = max(1, n_prior // 2)
+        return np.stack([np.sort(rng.choice(n_prior, k, replace=False)) for _ in range(wl.h_kv)]).astype(np.int32)
+
+    outs, dk, dv = _run_chunks(pkv, wl, synth.page_permutation(wl), sel_fn=sel_fn)
+    _check_against_oracle(wl, outs, dk, dv, wl.page)
+
+
+def test_mid_page64_d64(pkv):
+    wl = _mid(seed=4, G=3, h_kv=2, C=256, chunks=(0, 1, 2), d=64, page=64, offset=0.0)
+    say("case mid 6/2 heads d=64 page 64 C=256")
+    outs, dk, dv = _run_chunks(pkv, wl, synth.page_permutation(wl))
+    _check_against_oracle(wl, outs, dk, dv, wl.page)
+
+
+def test_head_subsets_match_full_call(pkv):
+    """Running KV heads one at a time (kvh0/n_kvh) gives the same bits as one call over all heads."""
+    wl = _mid(seed=5, chunks=(0, 1))
+    c = 1
+    bt_np = synth.page_permutation(wl)
+    pool, bt = fill_pool(pkv, wl, wl.n_pages, bt_np)
+    q = t16(synth.q_chunk(wl, c))
+    n_prior = wl.n_prior(c)
+    o_all, lse_all = pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale)
+    o_h = torch.zeros_like(o_all)
+    lse_h = torch.zeros_like(lse_all)
+    for g in range(wl.h_kv):
+        pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, kvh0=g, n_kvh=1, o=o_h, lse=lse_h)
+    torch.cuda.synchronize()
+    # Split counts may differ between the calls, so compare to tolerance, not bits.
+    compare("O heads", host(o_h), host(o_all), 1e-2)
+    compare("LSE heads", lse_h.cpu().numpy(), lse_all.cpu().numpy(), 1e-4, rel=1e-5)
+    pool.free()
+
+
+def test_permutation_invariance_bitwise(pkv):
+    """Two page permutations of the same data: identical O/LSE/dQ bits (the kernels walk logical
+    pages in the same order); dK/dV equal up to the order of the atomic adds of row splits."""
+    wl = _mid(seed=6, chunks=(0, 1, 2))
+    res = []
+    for perm_seed in (11, 12):
+        bt_np = np.random.default_rng(perm_seed).permutation(wl.n_pages).astype(np.int32)
+        outs, dk, dv = _run_chunks(pkv, wl, bt_np)
+        res.append((outs, dk, dv))
+    for (c, _, o1, l1, q1), (_, _, o2, l2, q2) in zip(res[0][0], res[1][0]):
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(q1, q2), c
+    for a, b in ((res[0][1], res[1][1]), (res[0][2], res[1][2])):
+        assert np.max(np.abs(a - b)) <= 1e-5 * max(1.0, float(np.max(np.abs(a))))
+
+
+def test_sparse_all_pages_equals_dense_bitwise(pkv):
+    wl = _mid(seed=7, chunks=(0, 1, 2))
+    c = 2
+    bt_np = synth.page_permutation(wl)
+    pool, bt = fill_pool(pkv, wl, wl.n_pages, bt_np)
+    n_prior = wl.n_prior(c)
+    q = t16(synth.q_chunk(wl, c))
+    sel = i32(np.tile(np.arange(n_prior, dtype=np.int32), (wl.h_kv, 1)))
+    o1, l1 = pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale)
+    o2, l2 = pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, sel=sel)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    pool.free()
+
+
+def test_sparse_backward_leaves_unselected_pages(pkv):
+    wl = _mid(seed=8, chunks=(0, 1, 2, 3))
+    c = 3
+    bt_np = synth.page_permutation(wl)
+    pool, bt = fill_pool(pkv, wl, wl.n_pages, bt_np)
+    n_prior = wl.n_prior(c)
+    sel_np = np.array([[0, 3, 5], [1, 2, 6]], dtype=np.int32)
+    sel = i32(sel_np)
+    q, do = t16(synth.q_chunk(wl, c)), t16(synth.do_chunk(wl, c))
+    # Put known non-zero values in every gradient page first: run a dense backward of chunk 1.
+    q1, do1 = t16(synth.q_chunk(wl, 1)), t16(synth.do_chunk(wl, 1))
+    o1, l1 = pkv.chunk_attn_fwd(pool, bt, wl.n_prior(1), q1, wl.scale)
+    pkv.chunk_attn_bwd(pool, bt, wl.n_prior(1), q1, o1, do1, l1, wl.scale)
+    before = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy()
+    o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, sel=sel)
+    pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, sel=sel)
+    after = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy()
+    torch.cuda.synchronize()
+    P = wl.page
+    for g in range(wl.h_kv):
+        for lp in range(n_prior):
+            same = np.array_equal(before[lp * P:(lp + 1) * P, g], after[lp * P:(lp + 1) * P, g])
+            assert same == (lp not in sel_np[g]), (g, lp)
+    pool.free()
+
+
+def test_topk_selection_bit_exact(pkv):
+    wl = synth.Workload("sel", 28, 4, 128, 128, 128 * 200, 4096, (0,), offset_std=0.5, seed=9)
+    n_prior = 168
+    bt_np = synth.page_permutation(wl)
+    pool, bt = fill_pool(pkv, wl, n_prior, bt_np)
+    q_np = synth.q_chunk(wl, 5)
+    kk, _ = synth.kv_tokens(wl, 0, n_prior)
+    for top_k, n_local in ((16, 4), (64, 4), (0, 3), (200, 4), (5, 0)):
+        sel = pkv.page_topk_select(pool, bt, n_prior, t16(q_np), top_k, n_local)
+        want, sc, reps = oracle.topk_pages(q_np, kk, wl.page, wl.h_kv, n_prior, top_k, n_local)
+        got = sel.cpu().numpy()
+        say(f"  top_k={top_k} n_local={n_local}: n_sel={got.shape[1]}")
+        assert np.array_equal(got, want), (top_k, n_local)
+    rep_g = pool.export(pkv.PKV_REP, bt, 0, n_prior).cpu().numpy()
+    assert np.array_equal(rep_g, oracle.page_reps(oracle.page_key_sums(kk, wl.page), wl.page))
+    torch.cuda.synchronize()
+    pool.free()
+
+
+def test_topk_no_fma_and_ties(pkv):
+    """Constructed keys: the score of page 1 is exactly 0 only without FMA; duplicated pages tie and
+    the lower id wins."""
+    wl = synth.Workload("fma", 1, 1, 64, 64, 64 * 6, 64, (0,), seed=0)
+    P, d = 64, 64
+    K = np.zeros((6 * P, 1, d), np.float32)
+    # page 1: dims 0,1 mean to 1 + 2^-11 and 1 + 2^-12 (one token each a bit above 1).
+    K[P:2 * P, 0, 0] = 1.0
+    K[P:2 * P, 0, 1] = 1.0
+    K[P, 0, 0] = 1.0 + 2.0 ** -5     # sum = 64 + 2^-5 -> mean 1 + 2^-11
+    K[P, 0, 1] = 1.0 + 2.0 ** -6     # mean 1 + 2^-12
+    K[2 * P:3 * P, 0, 2] = 0.5       # page 2 score = 0.5 * qsum[2]
+    K[3 * P:4 * P] = K[2 * P:3 * P]  # page 3 duplicates page 2
+    Kb = synth.bf16_round(K)
+    Vb = synth.bf16_round(np.zeros_like(K))
+    # Queries: qsum = (-1, 1 + 2^-12, 1, 0, ...): token 0 carries (-1, 1, 1), token 1 carries 2^-12 on dim 1.
+    Q = np.zeros((64, 1, d), np.float32)
+    Q[0, 0, 0], Q[0, 0, 1], Q[0, 0, 2] = -1.0, 1.0, 1.0
+    Q[1, 0, 1] = 2.0 ** -12
+    Qb = synth.bf16_round(Q)
+    pool = pkv.Pool(6, P, 1, d)
+    bt = i32(np.arange(6))
+    pool.append(bt, 0, t16(Kb), t16(Vb))
+    # Scores: pages 0, 1, 4, 5 -> exactly 0 (page 1 only without FMA), pages 2, 3 -> 0.5.
+    for top_k, expect in ((1, [2]), (3, [0, 2, 3]), (4, [0, 1, 2, 3])):
+        want, sc, _ = oracle.topk_pages(Qb, Kb, P, 1, 6, top_k, 0)
+        assert sc[0, 1] == 0.0 and sc[0, 2] == sc[0, 3] == 0.5
+        assert want.tolist() == [expect]
+        got = pkv.page_topk_select(pool, bt, 6, t16(Qb), top_k, 0).cpu().numpy()
+        assert got.tolist() == [expect], (top_k, got)
+    torch.cuda.synchronize()
+    pool.free()

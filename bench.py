@@ -1,0 +1,239 @@
+#!/usr/bin/env python
+"""Benchmark: paged chunk attention forward + backward at a 256K context on one MI355X.
+
+Workload (one step = the whole hot path over one synthetic batch, inputs resident in HBM):
+  dense256k  append the final 4096-token chunk's K/V into its pages, forward, backward
+             (28 query / 4 KV heads, d=128, page 128, 2016 prior pages + the causal own block);
+  topk256k   the same plus page selection (top-64 by mean-key score + 4 most recent pages), with
+             forward and backward over the selected pages only.
+The headline value is the dense step's algorithmic TFLOP/s (forward 4*d*H_q*pairs, backward
+10*d*H_q*pairs); the top-K step is reported beside it.
+
+Prints one JSON line on stdout. Progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "chunk attn fwd+bwd TFLOP/s (and % bf16 peak) at 256K ctx, dense and top-K paged"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pairs_dense(C, q0):
+    return C * q0 + C * (C + 1) // 2
+
+
+def pairs_sparse(C, n_sel, P):
+    return C * n_sel * P + C * (C + 1) // 2
+
+
+def cpu_baseline(wl, k_np, v_np, q_np, do_np, c, tokens):
+    """The oracle, untuned, in float32 on the host cores: KV head 0 and its query heads, the last
+    `tokens` chunk tokens against every visible key (forward + backward)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    G = wl.group
+    q0 = wl.q0(c)
+    L = q0 + wl.chunk
+    q = oracle.widen_bf16(q_np[:, :G, :])
+    do = oracle.widen_bf16(do_np[:, :G, :])
+    k = oracle.widen_bf16(k_np[:L, :1, :])
+    v = oracle.widen_bf16(v_np[:L, :1, :])
+    rows = np.arange(wl.chunk - tokens, wl.chunk)
+    t0 = time.perf_counter()
+    oracle.chunk_forward(q, k, v, q0, wl.scale, page=wl.page, rows=rows, dtype=np.float32)
+    oracle.chunk_backward(q, k, v, do, q0, wl.scale, page=wl.page, rows=rows, dtype=np.float32)
+    dt = time.perf_counter() - t0
+    pairs = int(sum(q0 + t + 1 for t in rows)) * G
+    flop = 14.0 * wl.d * pairs
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"KV head 0 with its {G} query heads, last {tokens} of {wl.chunk} chunk tokens against all "
+                      f"{L} visible keys, forward+backward, float32; {flop:.3e} FLOP in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=256, help="chunk tokens in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-topk", action="store_true")
+    ap.add_argument("--topk-only", action="store_true",
+                    help="time only the top-K step (for per-workload profiles; prints no headline value)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_fwd_amd as pkv
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    pkv.load()
+    wl = synth.WORKLOADS["dense256k"]
+    wlk = synth.WORKLOADS["topk256k"]
+    c = wl.chunks[0]
+    C, P, H_q, H_kv, d = wl.chunk, wl.page, wl.h_q, wl.h_kv, wl.d
+    q0, n_prior, n_pages = wl.q0(c), wl.n_prior(c), wl.n_pages
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    log(f"[bench] generating {n_pages} pages of K/V ({wl.note})")
+    t0 = time.time()
+    k_np, v_np = synth.kv_tokens(wl, 0, n_pages)
+    q_np, do_np = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+    bt_np = synth.page_permutation(wl)
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s; appending prior pages")
+    pool = pkv.Pool(n_pages, P, H_kv, d, grads=True)
+    bt = torch.from_numpy(bt_np).to(dev)
+    per = 256
+    for p0 in range(0, n_prior, per):
+        n = min(per, n_prior - p0)
+        pool.append(bt, p0 * P, t16(k_np[p0 * P:(p0 + n) * P]), t16(v_np[p0 * P:(p0 + n) * P]))
+    k_own, v_own = t16(k_np[q0:q0 + C]), t16(v_np[q0:q0 + C])
+    q, do = t16(q_np), t16(do_np)
+    o = torch.empty_like(q)
+    dq = torch.empty_like(q)
+    lse = torch.empty((H_q, C), dtype=torch.float32, device=dev)
+    top_k, n_local = wlk.top_k, wlk.n_local
+    n_sel = min(top_k, n_prior - n_local) + n_local
+    sel = torch.empty((H_kv, n_sel), dtype=torch.int32, device=dev)
+    ws_f = torch.empty(max(pkv.chunk_attn_fwd_ws_bytes(pool, n_prior, -1, H_kv, C, H_q),
+                           pkv.chunk_attn_fwd_ws_bytes(pool, n_prior, n_sel, H_kv, C, H_q), 1),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(pkv.chunk_attn_bwd_ws_bytes(pool, n_prior, -1, H_kv, C, H_q),
+                           pkv.chunk_attn_bwd_ws_bytes(pool, n_prior, n_sel, H_kv, C, H_q), 1),
+                       dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(max(pkv.load().page_topk_ws_bytes(pool.handle, n_prior, C, H_q), 1), dtype=torch.uint8,
+                       device=dev)
+    torch.cuda.synchronize()
+
+    def step_dense():
+        pool.append(bt, q0, k_own, v_own)
+        pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, o=o, lse=lse, ws=ws_f)
+        pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, dq=dq, ws=ws_b)
+
+    def step_topk():
+        pool.append(bt, q0, k_own, v_own)
+        s = pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
+        pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, sel=s, o=o, lse=lse, ws=ws_f)
+        pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, sel=s, dq=dq, ws=ws_b)
+
+    def run(step, name):
+        log(f"[bench] {name}: {args.warmup} warmup steps")
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        pool.zero_grad()
+        torch.cuda.synchronize()
+        pkv.timing_enable(True)
+        log(f"[bench] {name}: {args.steps} timed steps")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        pkv.timing_enable(False)
+        kt = pkv.timing_collect()
+        pool.check()
+        return dt / args.steps * 1e3, kt
+
+    pd = pairs_dense(C, q0)
+    flop_dense = 14.0 * d * H_q * pd
+    if args.topk_only:
+        ps = pairs_sparse(C, n_sel, P)
+        ms_topk, kt_topk = run(step_topk, "topk256k")
+        print(json.dumps({"workload": "topk256k", "ms_per_step": round(ms_topk, 4),
+                          "TFLOP/s": round(14.0 * d * H_q * ps / (ms_topk * 1e-3) / 1e12, 2),
+                          "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}), flush=True)
+        pool.free()
+        return
+    ms_dense, kt_dense = run(step_dense, "dense256k")
+    tflops_dense = flop_dense / (ms_dense * 1e-3) / 1e12
+    log(f"[bench] dense256k: {ms_dense:.3f} ms/step, {tflops_dense:.1f} TFLOP/s")
+    for kname, (n, ms) in sorted(kt_dense.items(), key=lambda x: -x[1][1]):
+        log(f"[bench]   {kname:18s} launches {n:4d}  avg {ms / n:.3f} ms")
+
+    # Roofline of the dominant kernel: its own algorithmic MFMA work per launch / its average duration.
+    kernel_flop = {"k_attn_fwd": 4.0 * d * H_q * pd, "k_bwd_dq": 6.0 * d * H_q * pd,
+                   "k_bwd_dkdv": 8.0 * d * H_q * pd}
+    dom = max(kt_dense.items(), key=lambda x: x[1][1])[0]
+    n_l, tot_ms = kt_dense[dom]
+    avg_ms = tot_ms / n_l
+    if dom in kernel_flop:
+        ach = kernel_flop[dom] / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(avg_ms, 4),
+                    "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_dense.items()}}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": None, "traffic": None, "avg_launch_ms": round(avg_ms, 4)}
+
+    topk = None
+    if not args.no_topk:
+        ps = pairs_sparse(C, n_sel, P)
+        flop_topk = 14.0 * d * H_q * ps
+        ms_topk, kt_topk = run(step_topk, "topk256k")
+        log(f"[bench] topk256k: {ms_topk:.3f} ms/step, {flop_topk / (ms_topk * 1e-3) / 1e12:.1f} TFLOP/s")
+        for kname, (n, ms) in sorted(kt_topk.items(), key=lambda x: -x[1][1]):
+            log(f"[bench]   {kname:18s} launches {n:4d}  avg {ms / n:.3f} ms")
+        sel_ms = sum(v[1] / v[0] for k, v in kt_topk.items() if k in ("k_qsum_part", "k_qsum", "k_scores", "k_topk"))
+        sel_bytes = C * H_q * d * 2 + (n_prior - n_local) * H_kv * d * 4  # Q chunk + candidate reps
+        topk = {"workload": "topk256k: top-64 + 4 local pages of 2016 by mean-key score, + own block",
+                "value": round(flop_topk / (ms_topk * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(ms_topk, 4), "flop_per_step": flop_topk,
+                "step_speedup_vs_dense": round(ms_dense / ms_topk, 2),
+                "select_ms": round(sel_ms, 4),
+                "select_GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1) if sel_ms > 0 else None,
+                "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle sample ({args.cpu_tokens} tokens)")
+        cpu = cpu_baseline(wl, k_np, v_np, q_np, do_np, c, args.cpu_tokens)
+        log(f"[bench] CPU oracle: {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+    pool.free()
+
+    out = {
+        "metric": METRIC, "value": round(tflops_dense, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_dense, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dense256k: final 4096-token chunk at position 258048 over 2016 prior 128-token pages "
+                               "+ causal own block, 28/4 heads, d=128, K = N(0,1) + per-page N(0,0.5) offset",
+                   "context": wl.context, "chunk": C, "page": P, "h_q": H_q, "h_kv": H_kv, "head_dim": d,
+                   "flop_per_step": flop_dense, "pct_bf16_peak": round(100.0 * tflops_dense / PEAK_BF16_TFLOPS, 2),
+                   "step": "append own block + forward + backward (dK/dV accumulated into gradient pages)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "topk256k": topk,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -189,6 +189,19 @@ int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_
                     const int32_t* sel_dev, int32_t n_sel, int32_t kvh, const int32_t* dst_pages_dev,
                     void* stream);
 
+/*
+ * Per-kernel timing (tracing aid, off by default). While enabled, every kernel launch of the
+ * library is bracketed by two HIP events recorded on the launch's own stream.
+ * pkv_timing_enable(1) clears earlier records and starts recording; pkv_timing_enable(0) stops.
+ * pkv_timing_collect() waits for the recorded events and aggregates them per kernel name; it
+ * returns the number of names (or a negative status). pkv_timing_get(i, ...) returns name i,
+ * its launch count and the summed duration in milliseconds. Records are process-wide and not
+ * thread-safe against concurrent launches from several host threads.
+ */
+int pkv_timing_enable(int on);
+int pkv_timing_collect(void);
+int pkv_timing_get(int i, const char** name, int32_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

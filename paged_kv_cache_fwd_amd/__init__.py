@@ -24,7 +24,7 @@ EXPORTED = (
     "pkv_version", "pkv_last_error", "paged_kv_alloc", "paged_kv_free", "paged_kv_info", "paged_kv_data",
     "paged_kv_append", "paged_kv_zero_grad", "paged_kv_export", "paged_kv_check", "page_topk_ws_bytes",
     "page_topk_select", "chunk_attn_fwd_ws_bytes", "chunk_attn_fwd", "chunk_attn_bwd_ws_bytes",
-    "chunk_attn_bwd", "paged_kv_gather",
+    "chunk_attn_bwd", "paged_kv_gather", "pkv_timing_enable", "pkv_timing_collect", "pkv_timing_get",
 )
 
 
@@ -72,6 +72,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "chunk_attn_bwd": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _S,
                                 _P]),
         "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P]),
+        "pkv_timing_enable": (_I, [ctypes.c_int]),
+        "pkv_timing_collect": (ctypes.c_int, []),
+        "pkv_timing_get": (_I, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I),
+                                ctypes.POINTER(ctypes.c_double)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -249,3 +253,24 @@ def paged_kv_gather(host: Pool, dev: Pool, host_bt: torch.Tensor, sel_row: torch
     _need(dst_pages, torch.int32, "dst_pages")
     _check(load().paged_kv_gather(host.handle, dev.handle, _ptr(host_bt), host_bt.numel(), _ptr(sel_row),
                                   sel_row.numel(), kvh, _ptr(dst_pages), _stream(stream)))
+
+
+def timing_enable(on: bool = True):
+    """Start (clearing earlier records) or stop per-kernel HIP-event timing inside the library."""
+    _check(load().pkv_timing_enable(1 if on else 0))
+
+
+def timing_collect() -> dict:
+    """Wait for the recorded launches; return {kernel name: (launches, total ms)}."""
+    lib = load()
+    n = lib.pkv_timing_collect()
+    if n < 0:
+        _check(n)
+    out = {}
+    for i in range(n):
+        name = ctypes.c_char_p()
+        cnt = _I(0)
+        ms = ctypes.c_double(0.0)
+        _check(lib.pkv_timing_get(i, ctypes.byref(name), ctypes.byref(cnt), ctypes.byref(ms)))
+        out[name.value.decode()] = (cnt.value, ms.value)
+    return out

@@ -589,21 +589,33 @@ static hipError_t launch_bwd_d(const AttnArgs& a, const BwdExtra& e, const BwdPl
   float* ws_dq = dbuf + (((size_t)a.h_q * a.C + 63) & ~(size_t)63);
   {
     const int64_t work = (int64_t)a.C * a.n_kvh * a.G;
-    hipLaunchKernelGGL(k_bwd_rowdot<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, e.o, e.dout,
-                       dbuf);
+    {
+      TimerScope ts_("k_bwd_rowdot", s);
+      hipLaunchKernelGGL(k_bwd_rowdot<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, e.o, e.dout,
+                         dbuf);
+    }
   }
   {
     const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
-    hipLaunchKernelGGL(k_bwd_dq<D>, dim3(n_units), dim3(256), 0, s, a, e, plan.n_rb, plan.splits, dbuf, ws_dq);
+    {
+      TimerScope ts_("k_bwd_dq", s);
+      hipLaunchKernelGGL(k_bwd_dq<D>, dim3(n_units), dim3(256), 0, s, a, e, plan.n_rb, plan.splits, dbuf, ws_dq);
+    }
     if (plan.splits > 1) {
       const int64_t work = rows_total * (D / 8);
-      hipLaunchKernelGGL(k_bwd_dq_reduce<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, plan.splits,
-                         ws_dq, e.dq);
+      {
+        TimerScope ts_("k_bwd_dq_reduce", s);
+        hipLaunchKernelGGL(k_bwd_dq_reduce<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, plan.splits,
+                           ws_dq, e.dq);
+      }
     }
   }
   {
     const int32_t n_units = a.n_kvh * plan.n_ku * plan.row_splits;
-    hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(n_units), dim3(256), 0, s, a, e, plan.n_ku, plan.row_splits, dbuf);
+    {
+      TimerScope ts_("k_bwd_dkdv", s);
+      hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(n_units), dim3(256), 0, s, a, e, plan.n_ku, plan.row_splits, dbuf);
+    }
   }
   return hipGetLastError();
 }

@@ -334,11 +334,17 @@ static hipError_t launch_fwd_d(const AttnArgs& a, const FwdPlan& plan, uint16_t*
   float* ws_o = (float*)ws;
   float* ws_lse = ws_o ? ws_o + (size_t)plan.splits * rows_total * D : nullptr;
   const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
-  hipLaunchKernelGGL(k_attn_fwd<D>, dim3(n_units), dim3(256), 0, s, a, plan.n_rb, plan.splits, o, lse, ws_o, ws_lse);
+  {
+    TimerScope ts_("k_attn_fwd", s);
+    hipLaunchKernelGGL(k_attn_fwd<D>, dim3(n_units), dim3(256), 0, s, a, plan.n_rb, plan.splits, o, lse, ws_o, ws_lse);
+  }
   if (plan.splits > 1) {
     const int64_t work = rows_total * (D / 8);
-    hipLaunchKernelGGL(k_fwd_combine<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, plan.splits,
-                       ws_o, ws_lse, o, lse);
+    {
+      TimerScope ts_("k_fwd_combine", s);
+      hipLaunchKernelGGL(k_fwd_combine<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, plan.splits,
+                         ws_o, ws_lse, o, lse);
+    }
   }
   return hipGetLastError();
 }

@@ -158,20 +158,29 @@ hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, 
   const int32_t end_new = (pos0 + n + P - 1) / P;         // pages starting before pos0 + n
   if (pool.grad && end_new > first_new) {
     const int64_t work = (int64_t)(end_new - first_new) * H * 2 * P * D / 4;
-    hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D, bt,
-                       n_bt, first_new, end_new - first_new, pool.err);
+    {
+      TimerScope ts_("k_zero_grad", s);
+      hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D, bt,
+                         n_bt, first_new, end_new - first_new, pool.err);
+    }
   }
   const int64_t chunks = (int64_t)2 * n * H * (D / 8);
-  hipLaunchKernelGGL(k_append, dim3(grid_for(chunks)), dim3(256), 0, s, pool.kv, pool.n_pages, P, H, D, bt, n_bt,
-                     pos0, n, k, v, pool.err);
+  {
+    TimerScope ts_("k_append", s);
+    hipLaunchKernelGGL(k_append, dim3(grid_for(chunks)), dim3(256), 0, s, pool.kv, pool.n_pages, P, H, D, bt, n_bt,
+                       pos0, n, k, v, pool.err);
+  }
   // Pages whose last token is written here get their representative key.
   const int32_t first_full = pos0 / P;                    // candidate: page containing pos0
   const int32_t lp_a = ((first_full + 1) * P - 1 >= pos0) ? first_full : first_full + 1;
   const int32_t lp_b = (pos0 + n) / P;                    // pages fully ending before pos0 + n
   if (lp_b > lp_a) {
     const int64_t work = (int64_t)(lp_b - lp_a) * H * D;
-    hipLaunchKernelGGL(k_page_reps, dim3(grid_for(work)), dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, P, H, D,
-                       bt, n_bt, lp_a, lp_b - lp_a, pool.err);
+    {
+      TimerScope ts_("k_page_reps", s);
+      hipLaunchKernelGGL(k_page_reps, dim3(grid_for(work)), dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, P, H, D,
+                         bt, n_bt, lp_a, lp_b - lp_a, pool.err);
+    }
   }
   return hipGetLastError();
 }
@@ -180,8 +189,11 @@ hipError_t launch_zero_grad(const pkv_pool& pool, const int32_t* bt, int32_t fir
                             hipStream_t s) {
   const int64_t work = (int64_t)n_pages * pool.h_kv * 2 * pool.page * pool.d / 4;
   if (work == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, pool.page,
-                     pool.h_kv, pool.d, bt, first_page + n_pages, first_page, n_pages, pool.err);
+  {
+    TimerScope ts_("k_zero_grad", s);
+    hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, pool.page,
+                       pool.h_kv, pool.d, bt, first_page + n_pages, first_page, n_pages, pool.err);
+  }
   return hipGetLastError();
 }
 
@@ -191,16 +203,25 @@ hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, 
   const int32_t n_bt = first_page + n_pages;
   if (what == 0 || what == 1) {
     const int64_t work = (int64_t)n_pages * P * H * (D / 8);
-    hipLaunchKernelGGL(k_export_kv, dim3(grid_for(work)), dim3(256), 0, s, pool.kv, pool.n_pages, P, H, D, what, bt,
-                       n_bt, first_page, n_pages, (uint16_t*)dst, pool.err);
+    {
+      TimerScope ts_("k_export_kv", s);
+      hipLaunchKernelGGL(k_export_kv, dim3(grid_for(work)), dim3(256), 0, s, pool.kv, pool.n_pages, P, H, D, what, bt,
+                         n_bt, first_page, n_pages, (uint16_t*)dst, pool.err);
+    }
   } else if (what == 2 || what == 3) {
     const int64_t work = (int64_t)n_pages * P * H * (D / 4);
-    hipLaunchKernelGGL(k_export_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D,
-                       what - 2, bt, n_bt, first_page, n_pages, (float*)dst, pool.err);
+    {
+      TimerScope ts_("k_export_grad", s);
+      hipLaunchKernelGGL(k_export_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D,
+                         what - 2, bt, n_bt, first_page, n_pages, (float*)dst, pool.err);
+    }
   } else {
     const int64_t work = (int64_t)n_pages * H * D;
-    hipLaunchKernelGGL(k_export_rep, dim3(grid_for(work)), dim3(256), 0, s, pool.rep, pool.n_pages, H, D, bt, n_bt,
-                       first_page, n_pages, (float*)dst, pool.err);
+    {
+      TimerScope ts_("k_export_rep", s);
+      hipLaunchKernelGGL(k_export_rep, dim3(grid_for(work)), dim3(256), 0, s, pool.rep, pool.n_pages, H, D, bt, n_bt,
+                         first_page, n_pages, (float*)dst, pool.err);
+    }
   }
   return hipGetLastError();
 }
@@ -208,8 +229,11 @@ hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, 
 hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
                          const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages, hipStream_t s) {
   if (n_sel == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather, dim3(n_sel), dim3(256), 0, s, host.kv, host.n_pages, dev.kv, dev.n_pages, host.page,
-                     host.h_kv, host.d, host_bt, n_host_bt, sel, dst_pages, kvh, dev.err);
+  {
+    TimerScope ts_("k_gather", s);
+    hipLaunchKernelGGL(k_gather, dim3(n_sel), dim3(256), 0, s, host.kv, host.n_pages, dev.kv, dev.n_pages, host.page,
+                       host.h_kv, host.d, host_bt, n_host_bt, sel, dst_pages, kvh, dev.err);
+  }
   return hipGetLastError();
 }
 

@@ -187,12 +187,24 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
   float* scores = (float*)(w + al((size_t)h_q * nb * D * 4) + al((size_t)H * D * 4));
   if (n_cand > 0 && K > 0 && K < n_cand) {
     const int64_t n1 = (int64_t)h_q * nb * D;
-    hipLaunchKernelGGL(k_qsum_part, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, q, h_q, D, nb, part);
-    hipLaunchKernelGGL(k_qsum, dim3((unsigned)((H * D + 255) / 256)), dim3(256), 0, s, part, H, G, D, nb, qsum);
-    hipLaunchKernelGGL(k_scores, dim3((unsigned)((n_cand + 255) / 256), H), dim3(256), 0, s, qsum, pool.rep,
-                       pool.n_pages, H, D, bt, n_bt, n_cand, scores, pool.err);
+    {
+      TimerScope ts_("k_qsum_part", s);
+      hipLaunchKernelGGL(k_qsum_part, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, q, h_q, D, nb, part);
+    }
+    {
+      TimerScope ts_("k_qsum", s);
+      hipLaunchKernelGGL(k_qsum, dim3((unsigned)((H * D + 255) / 256)), dim3(256), 0, s, part, H, G, D, nb, qsum);
+    }
+    {
+      TimerScope ts_("k_scores", s);
+      hipLaunchKernelGGL(k_scores, dim3((unsigned)((n_cand + 255) / 256), H), dim3(256), 0, s, qsum, pool.rep,
+                         pool.n_pages, H, D, bt, n_bt, n_cand, scores, pool.err);
+    }
   }
-  hipLaunchKernelGGL(k_topk, dim3(H), dim3(kSelThreads), 0, s, scores, n_cand, K, n_prior, n_sel, sel);
+  {
+    TimerScope ts_("k_topk", s);
+    hipLaunchKernelGGL(k_topk, dim3(H), dim3(kSelThreads), 0, s, scores, n_cand, K, n_prior, n_sel, sel);
+  }
   return hipGetLastError();
 }
 

@@ -9,7 +9,10 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/pkv.h"
 #include "pkv_internal.h"
@@ -99,6 +102,37 @@ pkv::AttnArgs make_args(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, i
 
 namespace pkv {
 
+namespace {
+struct TimingRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<TimingRec> g_recs;     // recorded launches (events reused across enable cycles)
+size_t g_nrec = 0;
+std::vector<std::pair<std::string, std::pair<int32_t, double>>> g_summary;
+std::mutex g_tmu;
+}  // namespace
+
+TimerScope::TimerScope(const char* name, hipStream_t s) : slot_(-1), s_(s) {
+  if (!g_timing) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  if (g_nrec == g_recs.size()) {
+    TimingRec r{name, nullptr, nullptr};
+    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+    g_recs.push_back(r);
+  }
+  g_recs[g_nrec].name = name;
+  if (hipEventRecord(g_recs[g_nrec].a, s) != hipSuccess) return;
+  slot_ = (int)g_nrec++;
+}
+
+TimerScope::~TimerScope() {
+  if (slot_ < 0) return;
+  std::lock_guard<std::mutex> lk(g_tmu);
+  (void)hipEventRecord(g_recs[slot_].b, s_);
+}
+
 int num_cus() {
   static int cached = 0;
   if (cached == 0) {
@@ -164,6 +198,45 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, i
 extern "C" {
 
 int pkv_version(void) { return 100; }
+
+int pkv_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(pkv::g_tmu);
+  pkv::g_timing = on != 0;
+  if (on) {
+    pkv::g_nrec = 0;
+    pkv::g_summary.clear();
+  }
+  ok();
+  return PKV_OK;
+}
+
+int pkv_timing_collect(void) {
+  std::lock_guard<std::mutex> lk(pkv::g_tmu);
+  std::map<std::string, std::pair<int32_t, double>> agg;
+  for (size_t i = 0; i < pkv::g_nrec; ++i) {
+    hipError_t e = hipEventSynchronize(pkv::g_recs[i].b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (timing)");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pkv::g_recs[i].a, pkv::g_recs[i].b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime (timing)");
+    auto& slot = agg[pkv::g_recs[i].name];
+    slot.first += 1;
+    slot.second += ms;
+  }
+  pkv::g_summary.assign(agg.begin(), agg.end());
+  ok();
+  return (int)pkv::g_summary.size();
+}
+
+int pkv_timing_get(int i, const char** name, int32_t* launches, double* total_ms) {
+  std::lock_guard<std::mutex> lk(pkv::g_tmu);
+  if (i < 0 || (size_t)i >= pkv::g_summary.size()) return fail(PKV_E_INVALID, "timing index %d out of range", i);
+  if (name) *name = pkv::g_summary[i].first.c_str();
+  if (launches) *launches = pkv::g_summary[i].second.first;
+  if (total_ms) *total_ms = pkv::g_summary[i].second.second;
+  ok();
+  return PKV_OK;
+}
 
 const char* pkv_last_error(void) { return g_err.c_str(); }
 

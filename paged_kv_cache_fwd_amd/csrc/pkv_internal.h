@@ -54,6 +54,17 @@ struct BwdExtra {
   int32_t n_gpool_pages;
 };
 
+// Brackets one kernel launch with HIP events on its stream while timing is enabled.
+class TimerScope {
+ public:
+  TimerScope(const char* name, hipStream_t s);
+  ~TimerScope();
+
+ private:
+  int slot_;
+  hipStream_t s_;
+};
+
 // Launch-shape decisions, computed on the host from the shapes alone.
 struct FwdPlan {
   int32_t n_rb;       // row blocks of 256 rows per KV head

@@ -1,0 +1,107 @@
+"""GPU parity at full size (256K context, 28/4 heads, d=128, page 128), in the launch configuration
+the benchmark times: sampled rows against the oracle computed row by row in float32, the complete
+sparse step against the oracle, gradient-sum invariants that hold at any size, and bit-exact page
+selection."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import ATOL_GRAD, ATOL_LSE, ATOL_O, compare, fill_pool, host, i32, say, t16
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_fwd_amd as m
+    m.load()
+    return m
+
+
+@pytest.fixture(scope="module")
+def big(pkv):
+    wl = synth.WORKLOADS["dense256k"]
+    c = wl.chunks[0]
+    say("setup dense256k pool (2048 pages)")
+    bt_np = synth.page_permutation(wl)
+    pool, bt = fill_pool(pkv, wl, wl.n_pages, bt_np)
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    q, do = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+    yield wl, c, pool, bt, k, v, q, do
+    pool.free()
+
+
+def _sample_rows(C):
+    rng = np.random.default_rng(1234)
+    return np.unique(np.concatenate([[0, 1, 127, 128, C - 1], rng.choice(C, 19, replace=False)]))
+
+
+def test_dense256k_sampled_rows_and_invariants(pkv, big):
+    wl, c, pool, bt, k, v, q, do = big
+    n_prior = wl.n_prior(c)
+    pool.zero_grad()
+    qt, dot = t16(q), t16(do)
+    o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, qt, wl.scale)
+    dq = pkv.chunk_attn_bwd(pool, bt, n_prior, qt, o, dot, lse, wl.scale)
+    dk = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    dv = pool.export(pkv.PKV_DV, bt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    pool.check()
+    rows = _sample_rows(wl.chunk)
+    say(f"dense256k: oracle on {len(rows)} sampled tokens x {wl.h_q} heads (float32)")
+    ref = oracle.chunk_backward(q, k, v, do, wl.q0(c), wl.scale, page=wl.page, rows=rows, dtype=np.float32)
+    compare("O rows", host(o)[rows], ref["o"], ATOL_O)
+    compare("LSE rows", lse.cpu().numpy()[:, rows], ref["lse"], ATOL_LSE, rel=1e-5)
+    compare("dQ rows", host(dq)[rows], ref["dq"], ATOL_GRAD)
+    # Invariants per KV head: sum_j dV_j = sum of dO over the group's rows; sum_j dK_j = 0.
+    dof = synth.bf16_widen(do).astype(np.float64)
+    G = wl.group
+    for g in range(wl.h_kv):
+        want = dof[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+        got = dv[:, g].sum(axis=0)
+        err = np.linalg.norm(got - want) / np.linalg.norm(want)
+        skew = np.linalg.norm(dk[:, g].sum(axis=0)) / np.abs(dk[:, g]).sum(axis=0).mean()
+        say(f"  head {g}: |sum dV - sum dO|/|sum dO| = {err:.2e}; |sum dK| / mean sum|dK| = {skew:.2e}")
+        assert err < 1e-2 and skew < 1e-2
+    # Keys after the chunk's end were never attended: their gradients stay zero; all attended
+    # pages received gradient.
+    assert np.all(np.abs(dk).reshape(wl.n_pages, -1).max(axis=1) > 0)
+
+
+def test_topk256k_selection_and_full_sparse_step(pkv, big):
+    wl, c, pool, bt, k, v, q, do = big
+    wk = synth.WORKLOADS["topk256k"]
+    n_prior = wl.n_prior(c)
+    pool.zero_grad()
+    qt, dot = t16(q), t16(do)
+    sel = pkv.page_topk_select(pool, bt, n_prior, qt, wk.top_k, wk.n_local)
+    o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, qt, wl.scale, sel=sel)
+    dq = pkv.chunk_attn_bwd(pool, bt, n_prior, qt, o, dot, lse, wl.scale, sel=sel)
+    dk = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy()
+    dv = pool.export(pkv.PKV_DV, bt, 0, wl.n_pages).cpu().numpy()
+    torch.cuda.synchronize()
+    pool.check()
+    sel_np = sel.cpu().numpy()
+    say("topk256k: oracle selection over 2012 candidates")
+    want, scores, _ = oracle.topk_pages(q, k[: n_prior * wl.page], wl.page, wl.h_kv, n_prior, wk.top_k, wk.n_local)
+    assert sel_np.shape == (wl.h_kv, 68)
+    assert np.array_equal(sel_np, want)
+    # Gap between the K-th and (K+1)-th candidate score, for the record.
+    for g in range(wl.h_kv):
+        s = np.sort(scores[g])[::-1]
+        say(f"  head {g}: score gap at K: {s[wk.top_k - 1] - s[wk.top_k]:.3e}")
+    say("topk256k: full sparse oracle (float32), all rows and selected keys")
+    ref = oracle.chunk_backward(q, k, v, do, wl.q0(c), wl.scale, sel=want, page=wl.page, dtype=np.float32)
+    compare("O", host(o), ref["o"], ATOL_O)
+    compare("LSE", lse.cpu().numpy(), ref["lse"], ATOL_LSE, rel=1e-5)
+    compare("dQ", host(dq), ref["dq"], ATOL_GRAD)
+    for g in range(wl.h_kv):
+        keys = ref["keys"][g]
+        compare(f"dK head {g}", dk[keys, g], ref["dk"][g], ATOL_GRAD)
+        compare(f"dV head {g}", dv[keys, g], ref["dv"][g], ATOL_GRAD)
+        untouched = np.setdiff1d(np.arange(wl.context), keys)
+        assert np.all(dk[untouched, g] == 0) and np.all(dv[untouched, g] == 0)

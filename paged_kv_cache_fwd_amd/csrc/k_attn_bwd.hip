@@ -49,24 +49,22 @@ __global__ __launch_bounds__(256) void k_bwd_rowdot(AttnArgs a, const uint16_t* 
 
 // ---------------------------------------------------------------------------------------------
 template <int D>
-struct DqTile {
-  static constexpr int BK = 32;
-  static constexpr int KSTR = D + 8;
-  static constexpr int TSTR = BK + 4;
-  static constexpr int K_EL = BK * KSTR;
-  static constexpr int KT_EL = D * TSTR;
-  static constexpr int STAGE = 2 * K_EL + KT_EL;  // K rows, V rows, K^T
-  static constexpr int KB = D / 64;                // keys per thread in the staging transpose (1 or 2)
+struct DqCfg {
+  static constexpr int NW = 8;                       // waves per workgroup (32 rows each)
+  static constexpr int BK = 32;                      // keys per tile
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
+  static constexpr int CHR = D / 8;
+  static constexpr int TILE = BK * D;                // elements of one K or V tile
+  static constexpr int CHUNKS = BK * CHR;            // 16-byte chunks per tile
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32_t n_rb, int32_t splits,
+__global__ __launch_bounds__(512, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32_t n_rb, int32_t splits,
                                                    const float* __restrict__ dbuf, float* __restrict__ ws_dq) {
-  using T = DqTile<D>;
+  using T = DqCfg<D>;
   constexpr int BK = T::BK;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5, l32 = lane & 31;
   const int32_t n_units = a.n_kvh * splits * n_rb;
@@ -76,102 +74,76 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32
   const int32_t gi = u / (n_rb * splits);
   const int32_t g = a.kvh0 + gi;
   const int32_t G = a.G, CG = a.C * G, P = a.page, H = a.h_kv;
-  const int32_t r0 = rb * 256;
-  const int32_t r_last = min(r0 + 255, CG - 1);
+  const int32_t r0 = rb * 32 * T::NW;
+  const int32_t r_last = min(r0 + 32 * T::NW - 1, CG - 1);
   const int32_t t_min = r0 / G, t_max = r_last / G;
   const int32_t q0 = a.n_prior * P;
-  const int32_t tpp = P / BK;
-  const int32_t n_prior_tiles = list_prior(a) * tpp;
+  const int tsh = (P == 128) ? 2 : 1;  // log2(32-key tiles per page)
+  const int32_t n_prior_tiles = list_prior(a) << tsh;
   const int32_t n_tiles = n_prior_tiles + t_max / BK + 1;
   const int32_t tb = (int32_t)((int64_t)n_tiles * sp / splits);
   const int32_t te = (int32_t)((int64_t)n_tiles * (sp + 1) / splits);
 
-  int32_t row[2], tpos[2], hrow[2];
-  bool rvalid[2];
-  bf16x8 qreg[2][T::KS], doreg[2][T::KS];
-  float lse2[2], dval[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    row[qt] = r0 + wave * 64 + qt * 32 + l32;
-    rvalid[qt] = row[qt] < CG;
-    const int32_t rr = rvalid[qt] ? row[qt] : CG - 1;
-    tpos[qt] = rr / G;
-    hrow[qt] = g * G + (rr - tpos[qt] * G);
-    const int64_t off = ((int64_t)tpos[qt] * a.h_q + hrow[qt]) * D + 8 * lg;
+  const int32_t row = r0 + wave * 32 + l32;
+  const bool rvalid = row < CG;
+  const int32_t rr = rvalid ? row : CG - 1;
+  const int32_t tq = rr / G;
+  const int32_t h = g * G + (rr - tq * G);
+  bf16x8 qreg[T::KS], doreg[T::KS];
+  {
+    const int64_t off = ((int64_t)tq * a.h_q + h) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
       u32x4 x = *reinterpret_cast<const u32x4*>(a.q + off + ks * 16);
       u32x4 y = *reinterpret_cast<const u32x4*>(e.dout + off + ks * 16);
-      if (!rvalid[qt]) {
+      if (!rvalid) {
         x = (u32x4){0u, 0u, 0u, 0u};
         y = (u32x4){0u, 0u, 0u, 0u};
       }
-      qreg[qt][ks] = as_bf16x8(x);
-      doreg[qt][ks] = as_bf16x8(y);
+      qreg[ks] = as_bf16x8(x);
+      doreg[ks] = as_bf16x8(y);
     }
-    const int64_t si = (int64_t)hrow[qt] * a.C + tpos[qt];
-    lse2[qt] = rvalid[qt] ? e.lse[si] * kLog2e : INFINITY;
-    dval[qt] = rvalid[qt] ? dbuf[si] : 0.f;
   }
+  const int64_t si = (int64_t)h * a.C + tq;
+  const float lse2 = rvalid ? e.lse[si] * kLog2e : INFINITY;
+  const float dval = rvalid ? dbuf[si] : 0.f;
 
-  u32x4 kbuf[T::KB], vbuf[T::KB];
-  const int sdc = tid % (D / 8), skb = tid / (D / 8);  // staging: keys skb*KB.., dims sdc*8..
-
-  auto tile_base = [&](int32_t i, int32_t& kpos0) -> const uint16_t* {
-    const int32_t pi = i / tpp, sub = i - (i / tpp) * tpp;
+  auto tile_src = [&](int32_t i, int32_t& kpos0) -> const uint16_t* {
+    const int32_t pi = i >> tsh, sub = i & ((1 << tsh) - 1);
     const int32_t lp = list_page(a, g, pi);
-    kpos0 = (lp < 0 ? 0 : lp) * P + sub * BK;
     const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
     if (ph < 0) {
       kpos0 = -1;
       return nullptr;
     }
+    kpos0 = lp * P + sub * BK;
     return a.kv + (((int64_t)ph * H + g) * 2) * P * D + (int64_t)sub * BK * D;
   };
+  u32x4 kb, vb;
+  const bool stager = tid < T::CHUNKS;
   auto load_tile = [&](int32_t i) {
     int32_t kp;
-    const uint16_t* base = tile_base(i, kp);
-#pragma unroll
-    for (int c = 0; c < T::KB; ++c) {
-      if (base == nullptr) {
-        kbuf[c] = (u32x4){0u, 0u, 0u, 0u};
-        vbuf[c] = (u32x4){0u, 0u, 0u, 0u};
-      } else {
-        const int64_t off = (int64_t)(skb * T::KB + c) * D + sdc * 8;
-        kbuf[c] = *reinterpret_cast<const u32x4*>(base + off);
-        vbuf[c] = *reinterpret_cast<const u32x4*>(base + (int64_t)P * D + off);
-      }
+    const uint16_t* src = tile_src(i, kp);
+    kb = (u32x4){0u, 0u, 0u, 0u};
+    vb = (u32x4){0u, 0u, 0u, 0u};
+    if (src && stager) {
+      kb = reinterpret_cast<const u32x4*>(src)[tid];
+      vb = reinterpret_cast<const u32x4*>(src + (int64_t)P * D)[tid];
     }
   };
   auto store_tile = [&](int stage) {
-    uint16_t* kr = lds + stage * T::STAGE;
-    uint16_t* vr = kr + T::K_EL;
-    uint16_t* kt = vr + T::K_EL;
-#pragma unroll
-    for (int c = 0; c < T::KB; ++c) {
-      const int key = skb * T::KB + c;
-      *reinterpret_cast<u32x4*>(kr + key * T::KSTR + sdc * 8) = kbuf[c];
-      *reinterpret_cast<u32x4*>(vr + key * T::KSTR + sdc * 8) = vbuf[c];
-    }
-#pragma unroll
-    for (int el = 0; el < 8; ++el) {
-      const int sh = 16 * (el & 1);
-      uint16_t* dst = kt + (sdc * 8 + el) * T::TSTR + skb * T::KB;
-      if constexpr (T::KB == 2) {
-        *reinterpret_cast<uint32_t*>(dst) =
-            ((kbuf[0][el >> 1] >> sh) & 0xffffu) | (((kbuf[1][el >> 1] >> sh) & 0xffffu) << 16);
-      } else {
-        *dst = (uint16_t)((kbuf[0][el >> 1] >> sh) & 0xffffu);
-      }
-    }
+    if (!stager) return;
+    uint16_t* kt = lds + stage * 2 * T::TILE;
+    const int r = tid / T::CHR, q = tid % T::CHR;
+    const int off = r * D + ((q ^ swz<D>(r)) << 3);
+    *reinterpret_cast<u32x4*>(kt + off) = kb;
+    *reinterpret_cast<u32x4*>(kt + T::TILE + off) = vb;
   };
 
   const float sl2 = a.scale * kLog2e;
-  f32x16 dq[T::DT][2];
+  f32x16 dq[T::DT];
 #pragma unroll
-  for (int dt = 0; dt < T::DT; ++dt)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) dq[dt][qt] = (f32x16){};
+  for (int dt = 0; dt < T::DT; ++dt) dq[dt] = (f32x16){};
 
   if (tb < te) {
     load_tile(tb);
@@ -182,102 +154,79 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32
   for (int32_t i = tb; i < te; ++i) {
     const int cur = (i - tb) & 1;
     int32_t kpos0;
-    (void)tile_base(i, kpos0);
+    (void)tile_src(i, kpos0);
     if (i + 1 < te) load_tile(i + 1);
-    const uint16_t* kr = lds + cur * T::STAGE;
-    const uint16_t* vr = kr + T::K_EL;
-    const uint16_t* ktl = vr + T::K_EL;
+    const uint16_t* kt = lds + cur * 2 * T::TILE;
+    const uint16_t* vt = kt + T::TILE;
 
-    f32x16 sacc[2], pacc[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      sacc[qt] = (f32x16){};
-      pacc[qt] = (f32x16){};
-    }
+    f32x16 sacc = (f32x16){}, pacc = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
-      const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kr + l32 * T::KSTR + ks * 16 + 8 * lg));
-      const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vr + l32 * T::KSTR + ks * 16 + 8 * lg));
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        sacc[qt] = mfma32(ka, qreg[qt][ks], sacc[qt]);
-        pacc[qt] = mfma32(va, doreg[qt][ks], pacc[qt]);
-      }
+      const int off = toff<D>(l32, ks * 16 + 8 * lg);
+      const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + off));
+      const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + off));
+      sacc = mfma32(ka, qreg[ks], sacc);
+      pacc = mfma32(va, doreg[ks], pacc);
     }
     const bool bad = kpos0 < 0;
     const bool need_mask = bad || (kpos0 + BK - 1 > q0 + t_min);
-    bf16x8 dsb[2][2];  // [qt][half]
+    const int32_t lim = q0 + tq;
+    float ds[16];
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int32_t lim = q0 + tpos[qt];
-      float ds[16];
-#pragma unroll
-      for (int el = 0; el < 16; ++el) {
-        float p = __builtin_amdgcn_exp2f(sacc[qt][el] * sl2 - lse2[qt]);
-        if (need_mask) {
-          const int32_t key = kpos0 + 8 * (el >> 2) + 4 * lg + (el & 3);
-          if (bad || key > lim) p = 0.f;
-        }
-        ds[el] = p * (pacc[qt][el] - dval[qt]);
+    for (int el = 0; el < 16; ++el) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[el], sl2, -lse2));
+      if (need_mask) {
+        const int32_t key = kpos0 + 8 * (el >> 2) + 4 * lg + (el & 3);
+        if (bad || key > lim) p = 0.f;
       }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(ds[hf * 8 + 2 * j], ds[hf * 8 + 2 * j + 1]);
-        dsb[qt][hf] = as_bf16x8(w);
-      }
+      ds[el] = p * (pacc[el] - dval);
     }
-    // dQ^T[dt][qt] += K^T[dt rows][16 keys] dS^T[16 keys][qt]
+    bf16x8 dsb[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int key0 = hf * 16 + 4 * lg;
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = cvt_pk_bf16(ds[hf * 8 + 2 * j], ds[hf * 8 + 2 * j + 1]);
+      dsb[hf] = as_bf16x8(w);
+    }
+    // dQ^T[dt] += K^T[dt rows][16 keys] dS^T[16 keys]
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int k_lo = hf * 16 + 4 * lg;
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) {
-        const uint16_t* src = ktl + (dt * 32 + l32) * T::TSTR + key0;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-        u32x4 w;
-        w[0] = lo[0];
-        w[1] = lo[1];
-        w[2] = hi[0];
-        w[3] = hi[1];
-        const bf16x8 kta = as_bf16x8(w);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) dq[dt][qt] = mfma32(kta, dsb[qt][hf], dq[dt][qt]);
+        const bf16x8 kta = tr_operand<D>(kt, k_lo, k_lo + 8, dt * 32, lane);
+        dq[dt] = mfma32(kta, dsb[hf], dq[dt]);
       }
     }
     if (i + 1 < te) store_tile(cur ^ 1);
     __syncthreads();
   }
 
+  if (!rvalid) return;
+  if (splits == 1) {
+    uint16_t* dp = e.dq + ((int64_t)tq * a.h_q + h) * D;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    if (!rvalid[qt]) continue;
-    if (splits == 1) {
-      uint16_t* dp = e.dq + ((int64_t)tpos[qt] * a.h_q + hrow[qt]) * D;
+    for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt)
+      for (int grp = 0; grp < 4; ++grp) {
+        u32x2 w;
+        w[0] = cvt_pk_bf16(dq[dt][grp * 4 + 0] * a.scale, dq[dt][grp * 4 + 1] * a.scale);
+        w[1] = cvt_pk_bf16(dq[dt][grp * 4 + 2] * a.scale, dq[dt][grp * 4 + 3] * a.scale);
+        *reinterpret_cast<u32x2*>(dp + dt * 32 + grp * 8 + 4 * lg) = w;
+      }
+  } else {
+    const int64_t rows_total = (int64_t)a.n_kvh * CG;
+    float* wp = ws_dq + ((int64_t)sp * rows_total + (int64_t)gi * CG + row) * D;
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          u32x2 w;
-          w[0] = pack_bf16x2(dq[dt][qt][grp * 4 + 0] * a.scale, dq[dt][qt][grp * 4 + 1] * a.scale);
-          w[1] = pack_bf16x2(dq[dt][qt][grp * 4 + 2] * a.scale, dq[dt][qt][grp * 4 + 3] * a.scale);
-          *reinterpret_cast<u32x2*>(dp + dt * 32 + grp * 8 + 4 * lg) = w;
-        }
-    } else {
-      const int64_t rows_total = (int64_t)a.n_kvh * CG;
-      float* wp = ws_dq + ((int64_t)sp * rows_total + (int64_t)gi * CG + row[qt]) * D;
+    for (int dt = 0; dt < T::DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt)
+      for (int grp = 0; grp < 4; ++grp) {
+        f32x4 w;
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          f32x4 w;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w[j] = dq[dt][qt][grp * 4 + j];
-          *reinterpret_cast<f32x4*>(wp + dt * 32 + grp * 8 + 4 * lg) = w;
-        }
-    }
+        for (int j = 0; j < 4; ++j) w[j] = dq[dt][grp * 4 + j];
+        *reinterpret_cast<f32x4*>(wp + dt * 32 + grp * 8 + 4 * lg) = w;
+      }
   }
 }
 
@@ -305,29 +254,35 @@ __global__ __launch_bounds__(256) void k_bwd_dq_reduce(AttnArgs a, int32_t split
   }
   u32x4 out;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out[j] = pack_bf16x2(acc[2 * j] * a.scale, acc[2 * j + 1] * a.scale);
+  for (int j = 0; j < 4; ++j) out[j] = cvt_pk_bf16(acc[2 * j] * a.scale, acc[2 * j + 1] * a.scale);
   *reinterpret_cast<u32x4*>(dq + ((int64_t)t * a.h_q + h) * D + dc * 8) = out;
 }
 
 // ---------------------------------------------------------------------------------------------
 template <int D>
-struct DkvTile {
-  static constexpr int BQ = 64;              // rows per staged block
-  static constexpr int RSTR = D + 8;         // row-major Q / dO stride (bf16)
-  static constexpr int TSTR = BQ + 4;        // transposed Q^T / dO^T stride (bf16)
-  static constexpr int R_EL = BQ * RSTR;
-  static constexpr int T_EL = D * TSTR;
-  static constexpr int STAGE_H = 2 * R_EL + 2 * T_EL;      // bf16 elements
-  static constexpr int STAGE_BYTES = STAGE_H * 2 + 2 * BQ * 4;  // + lse2 and D rows
-  static constexpr int RB = D / 32;          // rows per thread in the staging transpose (4 or 2)
+struct DkvCfg {
+  static constexpr int NW = 4;                 // waves per workgroup, 32 keys each
+  static constexpr int BQ = 64;                // rows per staged block
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
+  static constexpr int CHR = D / 8;
+  static constexpr int TILE = BQ * D;          // elements of one staged Q or dO block
+  static constexpr int CPT = BQ * CHR / (64 * NW);  // 16-byte chunks per thread per tensor
+  static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
 };
+
+// x / G for 0 <= x < 2^24 from a float reciprocal, corrected to the exact quotient.
+__device__ __forceinline__ int32_t div_small(int32_t x, int32_t G, float invG) {
+  int32_t q = (int32_t)((float)x * invG);
+  q -= (q * G > x) ? 1 : 0;
+  q += ((q + 1) * G <= x) ? 1 : 0;
+  return q;
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits,
                                                      const float* __restrict__ dbuf) {
-  using T = DkvTile<D>;
+  using T = DkvCfg<D>;
   constexpr int BQ = T::BQ;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE_BYTES];
 
@@ -339,18 +294,19 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
   const int32_t gi = u / (row_splits * n_ku);
   const int32_t g = a.kvh0 + gi;
   const int32_t G = a.G, CG = a.C * G, P = a.page, H = a.h_kv;
+  const float invG = 1.0f / (float)G;
   const int32_t q0 = a.n_prior * P;
-  const int32_t tpp = P / 32;  // 32-key tiles per page
-  const int32_t n_kt = (list_prior(a) + a.C / P) * tpp;
+  const int tsh = (P == 128) ? 2 : 1;  // log2(32-key tiles per page)
+  const int32_t n_kt = (list_prior(a) + a.C / P) << tsh;
 
   // This wave's 32 keys.
-  const int32_t kt_idx = ku * 4 + wave;
+  const int32_t kt_idx = ku * T::NW + wave;
   bool kvalid = kt_idx < n_kt;
   int32_t kpos0 = 0, gphys = -1, sub = 0;
   const uint16_t* kbase = nullptr;
   if (kvalid) {
-    const int32_t pi = kt_idx / tpp;
-    sub = kt_idx - pi * tpp;
+    const int32_t pi = kt_idx >> tsh;
+    sub = kt_idx & ((1 << tsh) - 1);
     const int32_t lp = list_page(a, g, pi);
     const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
     gphys = phys_page(e.gbt, e.n_gbt, e.n_gpool_pages, lp, a.err);
@@ -361,20 +317,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
   // First row any key of this workgroup can see (keys ascend along the list).
   int32_t wg_kpos_min;
   {
-    const int32_t pi0 = (ku * 4) / tpp;
+    const int32_t pi0 = (ku * T::NW) >> tsh;
     const int32_t lp0 = (pi0 < list_prior(a)) ? -1 : a.n_prior + (pi0 - list_prior(a));
-    wg_kpos_min = (lp0 < 0) ? 0 : lp0 * P + ((ku * 4) - pi0 * tpp) * 32;
+    wg_kpos_min = (lp0 < 0) ? 0 : lp0 * P + (((ku * T::NW) - (pi0 << tsh)) * 32);
   }
   const int32_t n_blk = (CG + BQ - 1) / BQ;
   int32_t blk_b = (int32_t)((int64_t)n_blk * rs / row_splits);
   const int32_t blk_e = (int32_t)((int64_t)n_blk * (rs + 1) / row_splits);
-  if (wg_kpos_min > q0) {
-    const int32_t rmin = G * (wg_kpos_min - q0);
-    blk_b = max(blk_b, rmin / BQ);
-  }
-  // Per-lane causal limit: row r sees key k iff r >= G * (k - q0).
+  if (wg_kpos_min > q0) blk_b = max(blk_b, (G * (wg_kpos_min - q0)) / BQ);
+  // Row r sees key k iff r >= G * (k - q0).
   const int32_t my_rmin = G * (kpos0 + l32 - q0);
   const int32_t wave_rmin = G * (kpos0 - q0);
+  const int32_t wave_rmax = G * (kpos0 + 31 - q0);
 
   bf16x8 kreg[T::KS], vreg[T::KS];
 #pragma unroll
@@ -389,72 +343,57 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
     vreg[ks] = as_bf16x8(y);
   }
 
-  // Staging: thread -> rows srb*RB.., dims sdc*8..
-  const int sdc = tid % (D / 8), srb = tid / (D / 8);
-  u32x4 qbuf[T::RB], dobuf[T::RB];
-  float lbuf = INFINITY, dvb = 0.f;
+  // Staging: thread -> chunks c = tid + 256 j: row c / CHR, chunk c % CHR.
+  u32x4 qb[T::CPT], dob[T::CPT];
+  float lb = INFINITY, db = 0.f;
   auto load_blk = [&](int32_t blk) {
+    const int32_t base = blk * BQ + tid / T::CHR;
+    const int32_t t0 = div_small(base, G, invG);
+    const int32_t rem0 = base - t0 * G;
 #pragma unroll
-    for (int c = 0; c < T::RB; ++c) {
-      const int32_t r = blk * BQ + srb * T::RB + c;
+    for (int j = 0; j < T::CPT; ++j) {
+      const int32_t r = base + j * (64 * T::NW / T::CHR);
+      const int32_t x = rem0 + j * (64 * T::NW / T::CHR);
+      const int32_t dt_ = div_small(x, G, invG);
+      const int32_t t = t0 + dt_, hh = x - dt_ * G;
       if (r < CG) {
-        const int32_t t = r / G, h = g * G + (r - (r / G) * G);
-        const int64_t off = ((int64_t)t * a.h_q + h) * D + sdc * 8;
-        qbuf[c] = *reinterpret_cast<const u32x4*>(a.q + off);
-        dobuf[c] = *reinterpret_cast<const u32x4*>(e.dout + off);
+        const int64_t off = ((int64_t)t * a.h_q + g * G + hh) * D + (tid % T::CHR) * 8;
+        qb[j] = *reinterpret_cast<const u32x4*>(a.q + off);
+        dob[j] = *reinterpret_cast<const u32x4*>(e.dout + off);
       } else {
-        qbuf[c] = (u32x4){0u, 0u, 0u, 0u};
-        dobuf[c] = (u32x4){0u, 0u, 0u, 0u};
+        qb[j] = (u32x4){0u, 0u, 0u, 0u};
+        dob[j] = (u32x4){0u, 0u, 0u, 0u};
       }
     }
     if (tid < BQ) {
       const int32_t r = blk * BQ + tid;
       if (r < CG) {
-        const int32_t t = r / G, h = g * G + (r - (r / G) * G);
-        lbuf = e.lse[(int64_t)h * a.C + t] * kLog2e;
-        dvb = dbuf[(int64_t)h * a.C + t];
+        const int32_t t = div_small(r, G, invG);
+        const int64_t si = (int64_t)(g * G + (r - t * G)) * a.C + t;
+        lb = e.lse[si] * kLog2e;
+        db = dbuf[si];
       } else {
-        lbuf = INFINITY;
-        dvb = 0.f;
+        lb = INFINITY;
+        db = 0.f;
       }
     }
   };
   auto store_blk = [&](int stage) {
-    unsigned char* base = smem + stage * T::STAGE_BYTES;
-    uint16_t* qs = reinterpret_cast<uint16_t*>(base);
-    uint16_t* dos = qs + T::R_EL;
-    uint16_t* qt = dos + T::R_EL;
-    uint16_t* dot = qt + T::T_EL;
-    float* ls = reinterpret_cast<float*>(base + T::STAGE_H * 2);
-    float* dd = ls + BQ;
+    unsigned char* bs = smem + stage * T::STAGE_BYTES;
+    uint16_t* qs = reinterpret_cast<uint16_t*>(bs);
+    uint16_t* ds_ = qs + T::TILE;
+    float* ls = reinterpret_cast<float*>(bs + 2 * T::TILE * 2);
 #pragma unroll
-    for (int c = 0; c < T::RB; ++c) {
-      const int r = srb * T::RB + c;
-      *reinterpret_cast<u32x4*>(qs + r * T::RSTR + sdc * 8) = qbuf[c];
-      *reinterpret_cast<u32x4*>(dos + r * T::RSTR + sdc * 8) = dobuf[c];
-    }
-#pragma unroll
-    for (int el = 0; el < 8; ++el) {
-      const int sh = 16 * (el & 1);
-      const int off = (sdc * 8 + el) * T::TSTR + srb * T::RB;
-      if constexpr (T::RB == 4) {
-        u32x2 w, x;
-        w[0] = ((qbuf[0][el >> 1] >> sh) & 0xffffu) | (((qbuf[1][el >> 1] >> sh) & 0xffffu) << 16);
-        w[1] = ((qbuf[2][el >> 1] >> sh) & 0xffffu) | (((qbuf[3][el >> 1] >> sh) & 0xffffu) << 16);
-        x[0] = ((dobuf[0][el >> 1] >> sh) & 0xffffu) | (((dobuf[1][el >> 1] >> sh) & 0xffffu) << 16);
-        x[1] = ((dobuf[2][el >> 1] >> sh) & 0xffffu) | (((dobuf[3][el >> 1] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(qt + off) = w;
-        *reinterpret_cast<u32x2*>(dot + off) = x;
-      } else {
-        *reinterpret_cast<uint32_t*>(qt + off) =
-            ((qbuf[0][el >> 1] >> sh) & 0xffffu) | (((qbuf[1][el >> 1] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint32_t*>(dot + off) =
-            ((dobuf[0][el >> 1] >> sh) & 0xffffu) | (((dobuf[1][el >> 1] >> sh) & 0xffffu) << 16);
-      }
+    for (int j = 0; j < T::CPT; ++j) {
+      const int c = tid + 64 * T::NW * j;
+      const int r = c / T::CHR, q = c % T::CHR;
+      const int off = r * D + ((q ^ swz<D>(r)) << 3);
+      *reinterpret_cast<u32x4*>(qs + off) = qb[j];
+      *reinterpret_cast<u32x4*>(ds_ + off) = dob[j];
     }
     if (tid < BQ) {
-      ls[tid] = lbuf;
-      dd[tid] = dvb;
+      ls[tid] = lb;
+      ls[BQ + tid] = db;
     }
   };
 
@@ -475,31 +414,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
   for (int32_t blk = blk_b; blk < blk_e; ++blk) {
     const int cur = (blk - blk_b) & 1;
     if (blk + 1 < blk_e) load_blk(blk + 1);
-    const unsigned char* base = smem + cur * T::STAGE_BYTES;
-    const uint16_t* qs = reinterpret_cast<const uint16_t*>(base);
-    const uint16_t* dos = qs + T::R_EL;
-    const uint16_t* qtl = dos + T::R_EL;
-    const uint16_t* dotl = qtl + T::T_EL;
-    const float* ls = reinterpret_cast<const float*>(base + T::STAGE_H * 2);
+    const unsigned char* bs = smem + cur * T::STAGE_BYTES;
+    const uint16_t* qs = reinterpret_cast<const uint16_t*>(bs);
+    const uint16_t* ds_ = qs + T::TILE;
+    const float* ls = reinterpret_cast<const float*>(bs + 2 * T::TILE * 2);
     const float* dd = ls + BQ;
 
     // Skip when this wave's keys are invalid or invisible to every row of the block.
-    const bool active = kvalid && (blk * BQ + BQ - 1 >= wave_rmin);
-    if (active) {
-      const bool need_mask = (blk * BQ < G * (kpos0 + 31 - q0));
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        sacc[rt] = (f32x16){};
-        pacc[rt] = (f32x16){};
-      }
+    if (kvalid && (blk * BQ + BQ - 1 >= wave_rmin)) {
+      const bool need_mask = blk * BQ < wave_rmax;
+      f32x16 sacc[2] = {(f32x16){}, (f32x16){}}, pacc[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const int roff = (rt * 32 + l32) * T::RSTR + ks * 16 + 8 * lg;
-          const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + roff));
-          const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4*>(dos + roff));
+          const int off = toff<D>(rt * 32 + l32, ks * 16 + 8 * lg);
+          const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + off));
+          const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4*>(ds_ + off));
           sacc[rt] = mfma32(qa, kreg[ks], sacc[rt]);
           pacc[rt] = mfma32(da, vreg[ks], pacc[rt]);
         }
@@ -516,7 +447,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int el = grp * 4 + j;
-            float p = __builtin_amdgcn_exp2f(sacc[rt][el] * sl2 - l4[j]);
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rt][el], sl2, -l4[j]));
             if (need_mask && (blk * BQ + rr + j < my_rmin)) p = 0.f;
             pv[el] = p;
             dsv[el] = p * (pacc[rt][el] - d4[j]);
@@ -527,37 +458,27 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
           u32x4 w, x;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            w[j] = pack_bf16x2(pv[hf * 8 + 2 * j], pv[hf * 8 + 2 * j + 1]);
-            x[j] = pack_bf16x2(dsv[hf * 8 + 2 * j], dsv[hf * 8 + 2 * j + 1]);
+            w[j] = cvt_pk_bf16(pv[hf * 8 + 2 * j], pv[hf * 8 + 2 * j + 1]);
+            x[j] = cvt_pk_bf16(dsv[hf * 8 + 2 * j], dsv[hf * 8 + 2 * j + 1]);
           }
           pb[rt][hf] = as_bf16x8(w);
           dsb[rt][hf] = as_bf16x8(x);
         }
       }
-      // dV[keys][d] += P^T[keys][16 rows] dO[16 rows][d]; dK likewise with dS^T and Q.
+      // dV[keys][d] += P^T[keys][16 rows] dO[16 rows][d]; dK[keys][d] += dS^T Q likewise. The B
+      // operands (rows along the contraction) come from transposed reads of the staged blocks,
+      // in the row order of the accumulator layout.
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int r0 = rt * 32 + hf * 16 + 4 * lg;
+          const int k_lo = rt * 32 + hf * 16 + 4 * lg;
 #pragma unroll
           for (int dt = 0; dt < T::DT; ++dt) {
-            const int off = (dt * 32 + l32) * T::TSTR + r0;
-            const u32x2 a0 = *reinterpret_cast<const u32x2*>(dotl + off);
-            const u32x2 a1 = *reinterpret_cast<const u32x2*>(dotl + off + 8);
-            const u32x2 b0 = *reinterpret_cast<const u32x2*>(qtl + off);
-            const u32x2 b1 = *reinterpret_cast<const u32x2*>(qtl + off + 8);
-            u32x4 wd, wq;
-            wd[0] = a0[0];
-            wd[1] = a0[1];
-            wd[2] = a1[0];
-            wd[3] = a1[1];
-            wq[0] = b0[0];
-            wq[1] = b0[1];
-            wq[2] = b1[0];
-            wq[3] = b1[1];
-            dv[dt] = mfma32(pb[rt][hf], as_bf16x8(wd), dv[dt]);
-            dk[dt] = mfma32(dsb[rt][hf], as_bf16x8(wq), dk[dt]);
+            const bf16x8 dob_t = tr_operand<D>(ds_, k_lo, k_lo + 8, dt * 32, lane);
+            const bf16x8 qb_t = tr_operand<D>(qs, k_lo, k_lo + 8, dt * 32, lane);
+            dv[dt] = mfma32(pb[rt][hf], dob_t, dv[dt]);
+            dk[dt] = mfma32(dsb[rt][hf], qb_t, dk[dt]);
           }
         }
     }
@@ -599,7 +520,7 @@ static hipError_t launch_bwd_d(const AttnArgs& a, const BwdExtra& e, const BwdPl
     const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
     {
       TimerScope ts_("k_bwd_dq", s);
-      hipLaunchKernelGGL(k_bwd_dq<D>, dim3(n_units), dim3(256), 0, s, a, e, plan.n_rb, plan.splits, dbuf, ws_dq);
+      hipLaunchKernelGGL(k_bwd_dq<D>, dim3(n_units), dim3(64 * DqCfg<D>::NW), 0, s, a, e, plan.n_rb, plan.splits, dbuf, ws_dq);
     }
     if (plan.splits > 1) {
       const int64_t work = rows_total * (D / 8);
@@ -614,7 +535,7 @@ static hipError_t launch_bwd_d(const AttnArgs& a, const BwdExtra& e, const BwdPl
     const int32_t n_units = a.n_kvh * plan.n_ku * plan.row_splits;
     {
       TimerScope ts_("k_bwd_dkdv", s);
-      hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(n_units), dim3(256), 0, s, a, e, plan.n_ku, plan.row_splits, dbuf);
+      hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(n_units), dim3(64 * DkvCfg<D>::NW), 0, s, a, e, plan.n_ku, plan.row_splits, dbuf);
     }
   }
   return hipGetLastError();

@@ -59,7 +59,8 @@ int check_attn(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_
   if (!aligned16(q)) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
   if (C <= 0 || C % pool->page != 0) return fail(PKV_E_INVALID, "C=%d must be a positive multiple of the page size %d", C, pool->page);
   if (H_q <= 0 || H_q % pool->h_kv != 0) return fail(PKV_E_INVALID, "H_q=%d must be a positive multiple of H_kv=%d", H_q, pool->h_kv);
-  if ((int64_t)C * (H_q / pool->h_kv) > (int64_t)1 << 30) return fail(PKV_E_INVALID, "chunk too large");
+  if ((int64_t)C * (H_q / pool->h_kv) >= (int64_t)1 << 24)
+    return fail(PKV_E_INVALID, "C * H_q / H_kv = %lld rows per KV head must be below 2^24", (long long)C * (H_q / pool->h_kv));
   if (n_prior < 0) return fail(PKV_E_INVALID, "n_prior < 0");
   if (n_bt < 0 || (int64_t)n_prior + C / pool->page > n_bt)
     return fail(PKV_E_RANGE, "pages [0, %d) exceed the block table (%d entries)", n_prior + C / pool->page, n_bt);

@@ -36,6 +36,56 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two floats -> packed bf16 pair (round to nearest even; one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// Row-major bf16 tiles in LDS are stored without padding; the 16-byte chunks of row r are
+// XOR-permuted by swz(r) so that both access patterns used on them are free of bank conflicts:
+// 16 lanes reading 16 consecutive rows at one chunk (MFMA operand along the row), and the
+// transposed 8-byte reads below (4 consecutive rows x 4 chunks per 32 lanes).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+// Element offset of (row r, column c) in a swizzled tile with D columns; c % 4 == 0.
+template <int D>
+__device__ __forceinline__ int toff(int r, int c) {
+  return r * D + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives column
+// N0 + i of rows K0..K0+3 when lane L of the group addresses row K0 + L/4, column N0 + 4*(L%4).
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand whose contraction index runs along the rows of a swizzled row-major tile: lane l
+// gets column n0 + l%32 and rows k_lo..k_lo+3 (slots 0-3) and k_hi..k_hi+3 (slots 4-7).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int k_lo, int k_hi, int n0, int lane) {
+  const int rr = (lane & 15) >> 2;
+  const int cc = n0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const u32x2 a = lds_tr16(tile + toff<D>(k_lo + rr, cc));
+  const u32x2 b = lds_tr16(tile + toff<D>(k_hi + rr, cc));
+  u32x4 w;
+  w[0] = a[0];
+  w[1] = a[1];
+  w[2] = b[0];
+  w[3] = b[1];
+  return as_bf16x8(w);
+}
+
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
 // Record an out-of-range table entry (first writer wins; the value is informational).

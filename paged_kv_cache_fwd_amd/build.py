@@ -17,8 +17,9 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 KERNELS = {
     "k_paging.hip": ["-ffp-contract=off"],
     "k_select.hip": ["-ffp-contract=off"],
-    "k_attn_fwd.hip": [],
-    "k_attn_bwd.hip": [],
+    # MFMA results stay in architectural VGPRs (the softmax and gradient math reads them there).
+    "k_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 HOST = ["pkv_abi.cpp"]
 

@@ -23,10 +23,12 @@
 namespace pkv {
 
 // ---------------------------------------------------------------------------------------------
-// D[h][t] = sum_d dO[t][h][d] * O[t][h][d] for the query heads of KV heads [kvh0, kvh0 + n_kvh).
+// D[h][t] = sum_d dO[t][h][d] * O[t][h][d] for the query heads of KV heads [kvh0, kvh0 + n_kvh),
+// and the log-sum-exp in base 2 (lse * log2 e) that the backward passes exponentiate against.
 template <int D>
 __global__ __launch_bounds__(256) void k_bwd_rowdot(AttnArgs a, const uint16_t* __restrict__ o,
-                                                    const uint16_t* __restrict__ dout, float* __restrict__ dbuf) {
+                                                    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                                                    float* __restrict__ dbuf, float* __restrict__ lse2buf) {
   const int32_t nh = a.n_kvh * a.G;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)a.C * nh) return;
@@ -45,6 +47,7 @@ __global__ __launch_bounds__(256) void k_bwd_rowdot(AttnArgs a, const uint16_t* 
     }
   }
   dbuf[(int64_t)h * a.C + t] = acc;
+  lse2buf[(int64_t)h * a.C + t] = lse[(int64_t)h * a.C + t] * kLog2e;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -61,7 +64,8 @@ struct DqCfg {
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32_t n_rb, int32_t splits,
-                                                   const float* __restrict__ dbuf, float* __restrict__ ws_dq) {
+                                                   const float* __restrict__ dbuf, const float* __restrict__ lse2buf,
+                                                   float* __restrict__ ws_dq) {
   using T = DqCfg<D>;
   constexpr int BK = T::BK;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32
     }
   }
   const int64_t si = (int64_t)h * a.C + tq;
-  const float lse2 = rvalid ? e.lse[si] * kLog2e : INFINITY;
+  const float lse2 = rvalid ? lse2buf[si] : INFINITY;
   const float dval = rvalid ? dbuf[si] : 0.f;
 
   auto tile_src = [&](int32_t i, int32_t& kpos0) -> const uint16_t* {
@@ -265,9 +269,11 @@ struct DkvCfg {
   static constexpr int BQ = 64;                // rows per staged block
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
-  static constexpr int CHR = D / 8;
+  static constexpr int CHR = D / 8;            // 16-byte chunks per row
   static constexpr int TILE = BQ * D;          // elements of one staged Q or dO block
-  static constexpr int CPT = BQ * CHR / (64 * NW);  // 16-byte chunks per thread per tensor
+  static constexpr int SEGS = TILE * 2 / 1024; // 1 KiB segments per block (one wave-wide load each)
+  static constexpr int SEG_PER_WAVE = SEGS / NW;
+  static constexpr int ROWS_PER_SEG = 1024 / (2 * D);
   static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
 };
 
@@ -281,10 +287,10 @@ __device__ __forceinline__ int32_t div_small(int32_t x, int32_t G, float invG) {
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits,
-                                                     const float* __restrict__ dbuf) {
+                                                     const float* __restrict__ dbuf, const float* __restrict__ lse2buf) {
   using T = DkvCfg<D>;
   constexpr int BQ = T::BQ;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * T::STAGE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5, l32 = lane & 31;
   const int32_t n_units = a.n_kvh * n_ku * row_splits;
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
   int32_t blk_b = (int32_t)((int64_t)n_blk * rs / row_splits);
   const int32_t blk_e = (int32_t)((int64_t)n_blk * (rs + 1) / row_splits);
   if (wg_kpos_min > q0) blk_b = max(blk_b, (G * (wg_kpos_min - q0)) / BQ);
-  // Row r sees key k iff r >= G * (k - q0).
+  // Row r sees key k iff r >= G * (k - q0); rows r >= CG do not exist.
   const int32_t my_rmin = G * (kpos0 + l32 - q0);
   const int32_t wave_rmin = G * (kpos0 - q0);
   const int32_t wave_rmax = G * (kpos0 + 31 - q0);
@@ -343,58 +349,58 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
     vreg[ks] = as_bf16x8(y);
   }
 
-  // Staging: thread -> chunks c = tid + 256 j: row c / CHR, chunk c % CHR.
-  u32x4 qb[T::CPT], dob[T::CPT];
-  float lb = INFINITY, db = 0.f;
-  auto load_blk = [&](int32_t blk) {
-    const int32_t base = blk * BQ + tid / T::CHR;
-    const int32_t t0 = div_small(base, G, invG);
-    const int32_t rem0 = base - t0 * G;
+  // Staging with direct global->LDS loads. Wave w fills 1 KiB segments w*SEG_PER_WAVE + j of the
+  // Q and dO blocks; lane L lands at segment offset 16 L = (row L / CHR of the segment, physical
+  // chunk L % CHR), so it fetches the logical chunk that the swizzle places there. Each lane
+  // tracks (token, head) of its rows incrementally from block to block. Rows past the end of the
+  // chunk re-read the last row and are masked out in the compute.
+  const uint16_t* qg = a.q + (int64_t)g * G * D;
+  const uint16_t* dg = e.dout + (int64_t)g * G * D;
+  const int32_t step_q = BQ / G, step_r = BQ - (BQ / G) * G;  // BQ = step_q * G + step_r
+  int32_t st_t[T::SEG_PER_WAVE], st_h[T::SEG_PER_WAVE], st_c[T::SEG_PER_WAVE];
 #pragma unroll
-    for (int j = 0; j < T::CPT; ++j) {
-      const int32_t r = base + j * (64 * T::NW / T::CHR);
-      const int32_t x = rem0 + j * (64 * T::NW / T::CHR);
-      const int32_t dt_ = div_small(x, G, invG);
-      const int32_t t = t0 + dt_, hh = x - dt_ * G;
-      if (r < CG) {
-        const int64_t off = ((int64_t)t * a.h_q + g * G + hh) * D + (tid % T::CHR) * 8;
-        qb[j] = *reinterpret_cast<const u32x4*>(a.q + off);
-        dob[j] = *reinterpret_cast<const u32x4*>(e.dout + off);
-      } else {
-        qb[j] = (u32x4){0u, 0u, 0u, 0u};
-        dob[j] = (u32x4){0u, 0u, 0u, 0u};
-      }
-    }
-    if (tid < BQ) {
-      const int32_t r = blk * BQ + tid;
-      if (r < CG) {
-        const int32_t t = div_small(r, G, invG);
-        const int64_t si = (int64_t)(g * G + (r - t * G)) * a.C + t;
-        lb = e.lse[si] * kLog2e;
-        db = dbuf[si];
-      } else {
-        lb = INFINITY;
-        db = 0.f;
-      }
+  for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
+    const int seg = wave * T::SEG_PER_WAVE + j;
+    const int rl = seg * T::ROWS_PER_SEG + lane / T::CHR;
+    const int32_t r = blk_b * BQ + rl;
+    st_t[j] = div_small(r, G, invG);
+    st_h[j] = r - st_t[j] * G;
+    st_c[j] = ((lane % T::CHR) ^ swz<D>(rl)) * 8;  // logical column of this lane's chunk
+  }
+  int32_t sl_t = 0, sl_h = 0;  // LSE / D row of lane `lane` (waves 0 and 1)
+  {
+    const int32_t r = blk_b * BQ + lane;
+    sl_t = div_small(r, G, invG);
+    sl_h = r - sl_t * G;
+  }
+  const int32_t last_t = (CG - 1) / G, last_h = (CG - 1) - ((CG - 1) / G) * G;
+  auto advance = [&](int32_t& t, int32_t& hh) {
+    hh += step_r;
+    t += step_q;
+    if (hh >= G) {
+      hh -= G;
+      t += 1;
     }
   };
-  auto store_blk = [&](int stage) {
+  auto load_blk = [&](int stage) {
     unsigned char* bs = smem + stage * T::STAGE_BYTES;
-    uint16_t* qs = reinterpret_cast<uint16_t*>(bs);
-    uint16_t* ds_ = qs + T::TILE;
-    float* ls = reinterpret_cast<float*>(bs + 2 * T::TILE * 2);
 #pragma unroll
-    for (int j = 0; j < T::CPT; ++j) {
-      const int c = tid + 64 * T::NW * j;
-      const int r = c / T::CHR, q = c % T::CHR;
-      const int off = r * D + ((q ^ swz<D>(r)) << 3);
-      *reinterpret_cast<u32x4*>(qs + off) = qb[j];
-      *reinterpret_cast<u32x4*>(ds_ + off) = dob[j];
+    for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
+      const int seg = wave * T::SEG_PER_WAVE + j;
+      const bool past = st_t[j] > last_t || (st_t[j] == last_t && st_h[j] > last_h);
+      const int32_t t = past ? last_t : st_t[j], hh = past ? last_h : st_h[j];
+      const int32_t off = (t * a.h_q + hh) * D + st_c[j];
+      g2lds16(qg + off, bs + seg * 1024);
+      g2lds16(dg + off, bs + T::TILE * 2 + seg * 1024);
+      advance(st_t[j], st_h[j]);
     }
-    if (tid < BQ) {
-      ls[tid] = lb;
-      ls[BQ + tid] = db;
+    if (wave < 2) {
+      const bool past = sl_t > last_t || (sl_t == last_t && sl_h > last_h);
+      const int32_t t = past ? last_t : sl_t, hh = past ? last_h : sl_h;
+      const int32_t si = (g * G + hh) * a.C + t;
+      g2lds4(wave == 0 ? (const void*)(lse2buf + si) : (const void*)(dbuf + si), bs + 2 * T::TILE * 2 + wave * BQ * 4);
     }
+    advance(sl_t, sl_h);
   };
 
   const float sl2 = a.scale * kLog2e;
@@ -405,54 +411,64 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
     dv[dt] = (f32x16){};
   }
 
-  if (blk_b < blk_e) {
-    load_blk(blk_b);
-    store_blk(0);
-  }
+  if (blk_b < blk_e) load_blk(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int32_t blk = blk_b; blk < blk_e; ++blk) {
     const int cur = (blk - blk_b) & 1;
-    if (blk + 1 < blk_e) load_blk(blk + 1);
+    if (blk + 1 < blk_e) load_blk(cur ^ 1);
     const unsigned char* bs = smem + cur * T::STAGE_BYTES;
     const uint16_t* qs = reinterpret_cast<const uint16_t*>(bs);
     const uint16_t* ds_ = qs + T::TILE;
     const float* ls = reinterpret_cast<const float*>(bs + 2 * T::TILE * 2);
     const float* dd = ls + BQ;
 
-    // Skip when this wave's keys are invalid or invisible to every row of the block.
-    if (kvalid && (blk * BQ + BQ - 1 >= wave_rmin)) {
-      const bool need_mask = blk * BQ < wave_rmax;
-      f32x16 sacc[2] = {(f32x16){}, (f32x16){}}, pacc[2] = {(f32x16){}, (f32x16){}};
+    // Blocks no key of this wave can see, and invalid key tiles, are masked rather than skipped,
+    // so the loop body has a single path (their contributions are never flushed or are zero).
+    {
+      const bool need_mask = (blk * BQ < wave_rmax) || (blk * BQ + BQ > CG);
+      (void)wave_rmin;
+      const int32_t rlim = CG - blk * BQ;  // rows at or past this index do not exist
 #pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks) {
+      for (int rt = 0; rt < 2; ++rt) {
+        f32x16 sacc = (f32x16){}, pacc = (f32x16){};
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int ks = 0; ks < T::KS; ++ks) {
           const int off = toff<D>(rt * 32 + l32, ks * 16 + 8 * lg);
           const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + off));
           const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4*>(ds_ + off));
-          sacc[rt] = mfma32(qa, kreg[ks], sacc[rt]);
-          pacc[rt] = mfma32(da, vreg[ks], pacc[rt]);
+          sacc = mfma32(qa, kreg[ks], sacc);
+          pacc = mfma32(da, vreg[ks], pacc);
         }
-      }
-      bf16x8 pb[2][2], dsb[2][2];  // [rt][half]
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
         float pv[16], dsv[16];
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           const int rr = rt * 32 + 8 * grp + 4 * lg;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rr);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + rr);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int el = grp * 4 + j;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rt][el], sl2, -l4[j]));
-            if (need_mask && (blk * BQ + rr + j < my_rmin)) p = 0.f;
-            pv[el] = p;
-            dsv[el] = p * (pacc[rt][el] - d4[j]);
+            pv[el] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[el], sl2, -l4[j]));
           }
         }
+        if (need_mask) {
+          // Keep rows lo <= row < hi of this block: lo from the lane's key, hi from the chunk end.
+          const uint32_t lo = (uint32_t)(my_rmin - blk * BQ), span = (uint32_t)(rlim - (my_rmin - blk * BQ));
+#pragma unroll
+          for (int el = 0; el < 16; ++el) {
+            const int rr = rt * 32 + 8 * (el >> 2) + 4 * lg + (el & 3);
+            if ((uint32_t)rr - lo >= span) pv[el] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int rr = rt * 32 + 8 * grp + 4 * lg;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + rr);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dsv[grp * 4 + j] = pv[grp * 4 + j] * (pacc[grp * 4 + j] - d4[j]);
+        }
+        bf16x8 pb[2], dsb[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           u32x4 w, x;
@@ -461,15 +477,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
             w[j] = cvt_pk_bf16(pv[hf * 8 + 2 * j], pv[hf * 8 + 2 * j + 1]);
             x[j] = cvt_pk_bf16(dsv[hf * 8 + 2 * j], dsv[hf * 8 + 2 * j + 1]);
           }
-          pb[rt][hf] = as_bf16x8(w);
-          dsb[rt][hf] = as_bf16x8(x);
+          pb[hf] = as_bf16x8(w);
+          dsb[hf] = as_bf16x8(x);
         }
-      }
-      // dV[keys][d] += P^T[keys][16 rows] dO[16 rows][d]; dK[keys][d] += dS^T Q likewise. The B
-      // operands (rows along the contraction) come from transposed reads of the staged blocks,
-      // in the row order of the accumulator layout.
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
+        // dV[keys][d] += P^T[keys][16 rows] dO[16 rows][d]; dK[keys][d] += dS^T Q likewise. The B
+        // operands (rows along the contraction) come from transposed reads of the staged blocks,
+        // in the row order of the accumulator layout.
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int k_lo = rt * 32 + hf * 16 + 4 * lg;
@@ -477,12 +490,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
           for (int dt = 0; dt < T::DT; ++dt) {
             const bf16x8 dob_t = tr_operand<D>(ds_, k_lo, k_lo + 8, dt * 32, lane);
             const bf16x8 qb_t = tr_operand<D>(qs, k_lo, k_lo + 8, dt * 32, lane);
-            dv[dt] = mfma32(pb[rt][hf], dob_t, dv[dt]);
-            dk[dt] = mfma32(dsb[rt][hf], qb_t, dk[dt]);
+            dv[dt] = mfma32(pb[hf], dob_t, dv[dt]);
+            dk[dt] = mfma32(dsb[hf], qb_t, dk[dt]);
           }
         }
+      }
     }
-    if (blk + 1 < blk_e) store_blk(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -506,37 +520,35 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
 template <int D>
 static hipError_t launch_bwd_d(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, void* ws, hipStream_t s) {
   const int64_t rows_total = (int64_t)a.n_kvh * a.C * a.G;
-  float* dbuf = (float*)ws;  // [H_q][C]
-  float* ws_dq = dbuf + (((size_t)a.h_q * a.C + 63) & ~(size_t)63);
+  const size_t nrow = ((size_t)a.h_q * a.C + 63) & ~(size_t)63;
+  float* dbuf = (float*)ws;        // [H_q][C] row dots
+  float* lse2buf = dbuf + nrow;    // [H_q][C] lse * log2 e
+  float* ws_dq = lse2buf + nrow;
   {
     const int64_t work = (int64_t)a.C * a.n_kvh * a.G;
-    {
-      TimerScope ts_("k_bwd_rowdot", s);
-      hipLaunchKernelGGL(k_bwd_rowdot<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, e.o, e.dout,
-                         dbuf);
-    }
+    TimerScope ts_("k_bwd_rowdot", s);
+    hipLaunchKernelGGL(k_bwd_rowdot<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, e.o, e.dout,
+                       e.lse, dbuf, lse2buf);
   }
   {
     const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
     {
       TimerScope ts_("k_bwd_dq", s);
-      hipLaunchKernelGGL(k_bwd_dq<D>, dim3(n_units), dim3(64 * DqCfg<D>::NW), 0, s, a, e, plan.n_rb, plan.splits, dbuf, ws_dq);
+      hipLaunchKernelGGL(k_bwd_dq<D>, dim3(n_units), dim3(64 * DqCfg<D>::NW), 0, s, a, e, plan.n_rb, plan.splits,
+                         dbuf, lse2buf, ws_dq);
     }
     if (plan.splits > 1) {
       const int64_t work = rows_total * (D / 8);
-      {
-        TimerScope ts_("k_bwd_dq_reduce", s);
-        hipLaunchKernelGGL(k_bwd_dq_reduce<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, plan.splits,
-                           ws_dq, e.dq);
-      }
+      TimerScope ts_("k_bwd_dq_reduce", s);
+      hipLaunchKernelGGL(k_bwd_dq_reduce<D>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a, plan.splits,
+                         ws_dq, e.dq);
     }
   }
   {
     const int32_t n_units = a.n_kvh * plan.n_ku * plan.row_splits;
-    {
-      TimerScope ts_("k_bwd_dkdv", s);
-      hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(n_units), dim3(64 * DkvCfg<D>::NW), 0, s, a, e, plan.n_ku, plan.row_splits, dbuf);
-    }
+    TimerScope ts_("k_bwd_dkdv", s);
+    hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(n_units), dim3(64 * DkvCfg<D>::NW), 0, s, a, e, plan.n_ku,
+                       plan.row_splits, dbuf, lse2buf);
   }
   return hipGetLastError();
 }

@@ -516,7 +516,7 @@ int chunk_attn_fwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, in
 }
 
 static size_t bwd_ws(const pkv_pool* pool, const pkv::BwdPlan& plan, int32_t n_kvh, int32_t C, int32_t H_q) {
-  const size_t dbytes = (((size_t)H_q * C + 63) & ~(size_t)63) * 4;
+  const size_t dbytes = 2 * (((size_t)H_q * C + 63) & ~(size_t)63) * 4;  // row dots + base-2 lse
   const size_t dq = plan.splits > 1 ? (size_t)plan.splits * n_kvh * C * (H_q / pool->h_kv) * pool->d * 4 : 0;
   return align256(dbytes + dq);
 }

@@ -88,6 +88,15 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int k_lo, int
 
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Direct global -> LDS loads (global_load_lds_dwordx4 / _dword): lane L of the wave writes its 16
+// (or 4) bytes to lds_base + 16 L (or 4 L). lds_base must be the same for every lane of the wave.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 4, 0, 0);
+}
+
 // Record an out-of-range table entry (first writer wins; the value is informational).
 __device__ __forceinline__ void flag_error(int32_t* err, int32_t code) {
   if (err) atomicCAS(err, 0, code);

@@ -53,22 +53,23 @@ __global__ __launch_bounds__(256) void k_bwd_rowdot(AttnArgs a, const uint16_t* 
 // ---------------------------------------------------------------------------------------------
 template <int D>
 struct DqCfg {
-  static constexpr int NW = 8;                       // waves per workgroup (32 rows each)
-  static constexpr int BK = 32;                      // keys per tile
+  static constexpr int NW = 4;                       // waves per workgroup (32 rows each)
+  static constexpr int BK = 64;                      // keys per tile
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
   static constexpr int CHR = D / 8;
   static constexpr int TILE = BK * D;                // elements of one K or V tile
-  static constexpr int CHUNKS = BK * CHR;            // 16-byte chunks per tile
+  static constexpr int SEG_PER_WAVE = TILE * 2 / 1024 / NW;
+  static constexpr int ROWS_PER_SEG = 1024 / (2 * D);
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32_t n_rb, int32_t splits,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(AttnArgs a, BwdExtra e, int32_t n_rb, int32_t splits,
                                                    const float* __restrict__ dbuf, const float* __restrict__ lse2buf,
                                                    float* __restrict__ ws_dq) {
   using T = DqCfg<D>;
   constexpr int BK = T::BK;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5, l32 = lane & 31;
   const int32_t n_units = a.n_kvh * splits * n_rb;
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32
   const int32_t r_last = min(r0 + 32 * T::NW - 1, CG - 1);
   const int32_t t_min = r0 / G, t_max = r_last / G;
   const int32_t q0 = a.n_prior * P;
-  const int tsh = (P == 128) ? 2 : 1;  // log2(32-key tiles per page)
+  const int tsh = (P == 128) ? 1 : 0;  // log2(64-key tiles per page)
   const int32_t n_prior_tiles = list_prior(a) << tsh;
   const int32_t n_tiles = n_prior_tiles + t_max / BK + 1;
   const int32_t tb = (int32_t)((int64_t)n_tiles * sp / splits);
@@ -123,25 +124,23 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32
     kpos0 = lp * P + sub * BK;
     return a.kv + (((int64_t)ph * H + g) * 2) * P * D + (int64_t)sub * BK * D;
   };
-  u32x4 kb, vb;
-  const bool stager = tid < T::CHUNKS;
-  auto load_tile = [&](int32_t i) {
+  int32_t seg_off[T::SEG_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
+    const int rl = (wave * T::SEG_PER_WAVE + j) * T::ROWS_PER_SEG + lane / T::CHR;
+    seg_off[j] = rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3);
+  }
+  auto load_tile = [&](int32_t i, int stage) {
     int32_t kp;
     const uint16_t* src = tile_src(i, kp);
-    kb = (u32x4){0u, 0u, 0u, 0u};
-    vb = (u32x4){0u, 0u, 0u, 0u};
-    if (src && stager) {
-      kb = reinterpret_cast<const u32x4*>(src)[tid];
-      vb = reinterpret_cast<const u32x4*>(src + (int64_t)P * D)[tid];
-    }
-  };
-  auto store_tile = [&](int stage) {
-    if (!stager) return;
+    if (src == nullptr) src = a.kv;  // unreadable page: any in-bounds bytes, the tile is masked
     uint16_t* kt = lds + stage * 2 * T::TILE;
-    const int r = tid / T::CHR, q = tid % T::CHR;
-    const int off = r * D + ((q ^ swz<D>(r)) << 3);
-    *reinterpret_cast<u32x4*>(kt + off) = kb;
-    *reinterpret_cast<u32x4*>(kt + T::TILE + off) = vb;
+#pragma unroll
+    for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
+      const int seg = wave * T::SEG_PER_WAVE + j;
+      g2lds16(src + seg_off[j], kt + seg * 512);
+      g2lds16(src + (int64_t)P * D + seg_off[j], kt + T::TILE + seg * 512);
+    }
   };
 
   const float sl2 = a.scale * kLog2e;
@@ -149,61 +148,66 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dq(AttnArgs a, BwdExtra e, int32
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) dq[dt] = (f32x16){};
 
-  if (tb < te) {
-    load_tile(tb);
-    store_tile(0);
-  }
+  if (tb < te) load_tile(tb, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int32_t i = tb; i < te; ++i) {
     const int cur = (i - tb) & 1;
-    int32_t kpos0;
-    (void)tile_src(i, kpos0);
-    if (i + 1 < te) load_tile(i + 1);
+    int32_t kpos_t;
+    (void)tile_src(i, kpos_t);
+    if (i + 1 < te) load_tile(i + 1, cur ^ 1);
     const uint16_t* kt = lds + cur * 2 * T::TILE;
     const uint16_t* vt = kt + T::TILE;
-
-    f32x16 sacc = (f32x16){}, pacc = (f32x16){};
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-      const int off = toff<D>(l32, ks * 16 + 8 * lg);
-      const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + off));
-      const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + off));
-      sacc = mfma32(ka, qreg[ks], sacc);
-      pacc = mfma32(va, doreg[ks], pacc);
-    }
-    const bool bad = kpos0 < 0;
-    const bool need_mask = bad || (kpos0 + BK - 1 > q0 + t_min);
+    const bool bad = kpos_t < 0;
+    const bool need_mask = bad || (kpos_t + BK - 1 > q0 + t_min);
     const int32_t lim = q0 + tq;
-    float ds[16];
+
+    // The two 32-key halves of the tile run one after the other to bound register use.
 #pragma unroll
-    for (int el = 0; el < 16; ++el) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[el], sl2, -lse2));
+    for (int k2 = 0; k2 < 2; ++k2) {
+      f32x16 sacc = (f32x16){}, pacc = (f32x16){};
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const int off = toff<D>(k2 * 32 + l32, ks * 16 + 8 * lg);
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + off));
+        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + off));
+        sacc = mfma32(ka, qreg[ks], sacc);
+        pacc = mfma32(va, doreg[ks], pacc);
+      }
+      float p[16];
+#pragma unroll
+      for (int el = 0; el < 16; ++el) p[el] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[el], sl2, -lse2));
       if (need_mask) {
-        const int32_t key = kpos0 + 8 * (el >> 2) + 4 * lg + (el & 3);
-        if (bad || key > lim) p = 0.f;
+#pragma unroll
+        for (int el = 0; el < 16; ++el) {
+          const int32_t key = kpos_t + k2 * 32 + 8 * (el >> 2) + 4 * lg + (el & 3);
+          if (bad || key > lim) p[el] = 0.f;
+        }
       }
-      ds[el] = p * (pacc[el] - dval);
-    }
-    bf16x8 dsb[2];
+      bf16x8 dsb[2];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      u32x4 w;
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4 w;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = cvt_pk_bf16(ds[hf * 8 + 2 * j], ds[hf * 8 + 2 * j + 1]);
-      dsb[hf] = as_bf16x8(w);
-    }
-    // dQ^T[dt] += K^T[dt rows][16 keys] dS^T[16 keys]
+        for (int j = 0; j < 4; ++j) {
+          const int el = hf * 8 + 2 * j;
+          w[j] = cvt_pk_bf16(p[el] * (pacc[el] - dval), p[el + 1] * (pacc[el + 1] - dval));
+        }
+        dsb[hf] = as_bf16x8(w);
+      }
+      // dQ^T[dt] += K^T[dt rows][16 keys] dS^T[16 keys]
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int k_lo = hf * 16 + 4 * lg;
+      for (int hf = 0; hf < 2; ++hf) {
+        const int k_lo = k2 * 32 + hf * 16 + 4 * lg;
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) {
-        const bf16x8 kta = tr_operand<D>(kt, k_lo, k_lo + 8, dt * 32, lane);
-        dq[dt] = mfma32(kta, dsb[hf], dq[dt]);
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const bf16x8 kta = tr_operand<D>(kt, k_lo, k_lo + 8, dt * 32, lane);
+          dq[dt] = mfma32(kta, dsb[hf], dq[dt]);
+        }
       }
     }
-    if (i + 1 < te) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -265,8 +269,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq_reduce(AttnArgs a, int32_t split
 // ---------------------------------------------------------------------------------------------
 template <int D>
 struct DkvCfg {
-  static constexpr int NW = 4;                 // waves per workgroup, 32 keys each
-  static constexpr int BQ = 64;                // rows per staged block
+  static constexpr int NW = dkdv_waves(D);     // waves per workgroup, 32 keys each
+  static constexpr int BQ = (D == 128) ? 32 : 64;  // rows per staged block
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
   static constexpr int CHR = D / 8;            // 16-byte chunks per row
@@ -275,6 +279,7 @@ struct DkvCfg {
   static constexpr int SEG_PER_WAVE = SEGS / NW;
   static constexpr int ROWS_PER_SEG = 1024 / (2 * D);
   static constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * BQ * 4;
+  static constexpr int VRES = 32 * D;           // resident V rows of one wave's keys (elements)
 };
 
 // x / G for 0 <= x < 2^24 from a float reciprocal, corrected to the exact quotient.
@@ -286,11 +291,12 @@ __device__ __forceinline__ int32_t div_small(int32_t x, int32_t G, float invG) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits,
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits,
                                                      const float* __restrict__ dbuf, const float* __restrict__ lse2buf) {
   using T = DkvCfg<D>;
   constexpr int BQ = T::BQ;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint16_t vres[T::NW * T::VRES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5, l32 = lane & 31;
   const int32_t n_units = a.n_kvh * n_ku * row_splits;
@@ -336,17 +342,23 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
   const int32_t wave_rmin = G * (kpos0 - q0);
   const int32_t wave_rmax = G * (kpos0 + 31 - q0);
 
-  bf16x8 kreg[T::KS], vreg[T::KS];
+  // K of this wave's keys stays in registers (B operand of S = Q K^T); V goes to LDS once (B
+  // operand of dP = dO V^T, read back as rows).
+  bf16x8 kreg[T::KS];
 #pragma unroll
   for (int ks = 0; ks < T::KS; ++ks) {
-    u32x4 x = (u32x4){0u, 0u, 0u, 0u}, y = (u32x4){0u, 0u, 0u, 0u};
-    if (kvalid) {
-      const int64_t off = (int64_t)l32 * D + ks * 16 + 8 * lg;
-      x = *reinterpret_cast<const u32x4*>(kbase + off);
-      y = *reinterpret_cast<const u32x4*>(kbase + (int64_t)P * D + off);
-    }
+    u32x4 x = (u32x4){0u, 0u, 0u, 0u};
+    if (kvalid) x = *reinterpret_cast<const u32x4*>(kbase + (int64_t)l32 * D + ks * 16 + 8 * lg);
     kreg[ks] = as_bf16x8(x);
-    vreg[ks] = as_bf16x8(y);
+  }
+  uint16_t* vmine = vres + wave * T::VRES;
+  {
+    const uint16_t* vsrc = kvalid ? kbase + (int64_t)P * D : a.kv;  // invalid tiles: any bytes
+#pragma unroll
+    for (int sg = 0; sg < T::VRES * 2 / 1024; ++sg) {
+      const int rl = sg * T::ROWS_PER_SEG + lane / T::CHR;
+      g2lds16(vsrc + rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3), vmine + sg * 512);
+    }
   }
 
   // Staging with direct global->LDS loads. Wave w fills 1 KiB segments w*SEG_PER_WAVE + j of the
@@ -367,9 +379,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
     st_h[j] = r - st_t[j] * G;
     st_c[j] = ((lane % T::CHR) ^ swz<D>(rl)) * 8;  // logical column of this lane's chunk
   }
-  int32_t sl_t = 0, sl_h = 0;  // LSE / D row of lane `lane` (waves 0 and 1)
+  // LSE / D rows: element e = wave * 64 + lane < 2 * BQ of the block's [lse2 | D] array.
+  constexpr int LW = (2 * BQ + 63) / 64;  // waves that fetch them
+  const int e_ld = wave * 64 + lane;
+  const bool is_lse = e_ld < BQ;
+  int32_t sl_t = 0, sl_h = 0;
   {
-    const int32_t r = blk_b * BQ + lane;
+    const int32_t r = blk_b * BQ + (is_lse ? e_ld : e_ld - BQ);
     sl_t = div_small(r, G, invG);
     sl_h = r - sl_t * G;
   }
@@ -394,11 +410,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
       g2lds16(dg + off, bs + T::TILE * 2 + seg * 1024);
       advance(st_t[j], st_h[j]);
     }
-    if (wave < 2) {
+    if (wave < LW) {
       const bool past = sl_t > last_t || (sl_t == last_t && sl_h > last_h);
       const int32_t t = past ? last_t : sl_t, hh = past ? last_h : sl_h;
       const int32_t si = (g * G + hh) * a.C + t;
-      g2lds4(wave == 0 ? (const void*)(lse2buf + si) : (const void*)(dbuf + si), bs + 2 * T::TILE * 2 + wave * BQ * 4);
+      g2lds4(is_lse ? (const void*)(lse2buf + si) : (const void*)(dbuf + si), bs + 2 * T::TILE * 2 + wave * 256);
     }
     advance(sl_t, sl_h);
   };
@@ -431,15 +447,16 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkdv(AttnArgs a, BwdExtra e, int
       (void)wave_rmin;
       const int32_t rlim = CG - blk * BQ;  // rows at or past this index do not exist
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
+      for (int rt = 0; rt < BQ / 32; ++rt) {
         f32x16 sacc = (f32x16){}, pacc = (f32x16){};
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) {
           const int off = toff<D>(rt * 32 + l32, ks * 16 + 8 * lg);
           const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + off));
           const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4*>(ds_ + off));
+          const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(vmine + toff<D>(l32, ks * 16 + 8 * lg)));
           sacc = mfma32(qa, kreg[ks], sacc);
-          pacc = mfma32(da, vreg[ks], pacc);
+          pacc = mfma32(da, vb, pacc);
         }
         float pv[16], dsv[16];
 #pragma unroll

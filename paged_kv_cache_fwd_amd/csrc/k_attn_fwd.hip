@@ -7,9 +7,11 @@
 //
 // Work decomposition. The G query heads sharing a KV head are packed into one row space:
 // row r = t*G + hh (t = chunk token, hh = head within the group), so every K/V tile staged in LDS
-// feeds 256 rows. A workgroup = (KV head, key-range split, 256-row block) with 8 waves of 32 rows,
-// two waves per SIMD so one wave's softmax overlaps the other's matrix work. Splits > 1 write
-// normalised partial outputs plus their log-sum-exp, merged by k_fwd_combine.
+// feeds 128 rows. A workgroup = (KV head, key-range split, 128-row block) with 4 waves of 32 rows;
+// two independent workgroups share each CU (two waves per SIMD), so one wave's softmax overlaps
+// the other's matrix work without a shared barrier. K/V tiles go straight from global memory into
+// LDS. Splits > 1 write normalised partial outputs plus their log-sum-exp, merged by
+// k_fwd_combine.
 //
 // Per wave and 64-key tile: S^T (keys x queries) = K Q^T as two 32x32 tiles (A = K rows from
 // LDS, B = Q^T in registers), so each lane owns one query column and its softmax statistics
@@ -24,24 +26,25 @@ namespace pkv {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = 8;                      // waves per workgroup
+  static constexpr int NW = 4;                      // waves per workgroup (32 rows each)
   static constexpr int BK = 64;                     // keys per tile
   static constexpr int KS = D / 16;                 // contraction steps over d
   static constexpr int DT = D / 32;                 // 32-row tiles of O^T
   static constexpr int CHR = D / 8;                 // 16-byte chunks per row
   static constexpr int TILE = BK * D;               // elements of one K or V tile
-  static constexpr int CPT = BK * CHR / (64 * NW);  // chunks per thread per tensor
+  static constexpr int SEG_PER_WAVE = TILE * 2 / 1024 / NW;  // 1 KiB direct-load segments per wave
+  static constexpr int ROWS_PER_SEG = 1024 / (2 * D);
 };
 
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(512, 1) void k_attn_fwd(AttnArgs a, int32_t n_rb, int32_t splits,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a, int32_t n_rb, int32_t splits,
                                                      uint16_t* __restrict__ o, float* __restrict__ lse,
                                                      float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   using T = FwdCfg<D>;
   constexpr int BK = T::BK;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5, l32 = lane & 31;
   const int32_t n_units = a.n_kvh * splits * n_rb;
@@ -91,32 +94,25 @@ __global__ __launch_bounds__(512, 1) void k_attn_fwd(AttnArgs a, int32_t n_rb, i
     return a.kv + (((int64_t)ph * H + g) * 2) * P * D + (int64_t)sub * BK * D;
   };
 
-  u32x4 kb[T::CPT], vb[T::CPT];
-  auto load_tile = [&](int32_t i) {
+  // Direct global->LDS staging: wave w fills 1 KiB segments w*SEG_PER_WAVE + j of the K and V
+  // tiles; lane L lands at (row L / CHR of the segment, physical chunk L % CHR) and so fetches the
+  // logical chunk the swizzle places there.
+  int32_t seg_off[T::SEG_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
+    const int rl = (wave * T::SEG_PER_WAVE + j) * T::ROWS_PER_SEG + lane / T::CHR;
+    seg_off[j] = rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3);
+  }
+  auto load_tile = [&](int32_t i, int stage) {
     int32_t kp;
     const uint16_t* src = tile_src(i, kp);
-#pragma unroll
-    for (int j = 0; j < T::CPT; ++j) {
-      const int c = tid + 64 * T::NW * j;
-      if (src) {
-        kb[j] = reinterpret_cast<const u32x4*>(src)[c];
-        vb[j] = reinterpret_cast<const u32x4*>(src + (int64_t)P * D)[c];
-      } else {
-        kb[j] = (u32x4){0u, 0u, 0u, 0u};
-        vb[j] = (u32x4){0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
+    if (src == nullptr) src = a.kv;  // unreadable page: any in-bounds bytes, the tile is masked
     uint16_t* kt = lds + stage * 2 * T::TILE;
-    uint16_t* vt = kt + T::TILE;
 #pragma unroll
-    for (int j = 0; j < T::CPT; ++j) {
-      const int c = tid + 64 * T::NW * j;
-      const int r = c / T::CHR, q = c % T::CHR;
-      const int off = r * D + ((q ^ swz<D>(r)) << 3);
-      *reinterpret_cast<u32x4*>(kt + off) = kb[j];
-      *reinterpret_cast<u32x4*>(vt + off) = vb[j];
+    for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
+      const int seg = wave * T::SEG_PER_WAVE + j;
+      g2lds16(src + seg_off[j], kt + seg * 512);
+      g2lds16(src + (int64_t)P * D + seg_off[j], kt + T::TILE + seg * 512);
     }
   };
 
@@ -126,17 +122,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_fwd(AttnArgs a, int32_t n_rb, i
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) oacc[dt] = (f32x16){};
 
-  if (tb < te) {
-    load_tile(tb);
-    store_tile(0);
-  }
+  if (tb < te) load_tile(tb, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int32_t i = tb; i < te; ++i) {
     const int cur = (i - tb) & 1;
     int32_t kpos0;
     (void)tile_src(i, kpos0);
-    if (i + 1 < te) load_tile(i + 1);
+    if (i + 1 < te) load_tile(i + 1, cur ^ 1);
     const uint16_t* kt = lds + cur * 2 * T::TILE;
     const uint16_t* vt = kt + T::TILE;
 
@@ -206,7 +200,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_fwd(AttnArgs a, int32_t n_rb, i
         }
       }
 
-    if (i + 1 < te) store_tile(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 

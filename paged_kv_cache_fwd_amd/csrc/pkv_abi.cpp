@@ -149,8 +149,8 @@ int num_cus() {
 
 // Pick the key-range split count: a workgroup costs (its tiles + fixed overhead), and workgroups
 // run one per CU in waves, so minimise waves * per-workgroup cost.
-static int32_t best_split(int64_t base_units, double tiles, double overhead, int32_t max_split) {
-  const int64_t slots = num_cus();
+static int32_t best_split(int64_t base_units, double tiles, double overhead, int32_t max_split, int per_cu) {
+  const int64_t slots = (int64_t)num_cus() * per_cu;
   int32_t best = 1;
   double best_cost = 1e300;
   for (int32_t s = 1; s <= max_split; ++s) {
@@ -167,10 +167,10 @@ static int32_t best_split(int64_t base_units, double tiles, double overhead, int
 FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d) {
   FwdPlan p;
   const int64_t rows = (int64_t)C * G;
-  p.n_rb = (int32_t)((rows + 255) / 256);
+  p.n_rb = (int32_t)((rows + 127) / 128);  // 128 rows per workgroup, two workgroups per CU
   const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
-  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split);
+  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 2);
   p.ws_bytes = p.splits > 1 ? align256((size_t)p.splits * n_kvh * rows * d * 4) + align256((size_t)p.splits * n_kvh * rows * 4) : 0;
   return p;
 }
@@ -178,19 +178,19 @@ FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, i
 BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d) {
   BwdPlan p;
   const int64_t rows = (int64_t)C * G;
-  p.n_rb = (int32_t)((rows + 255) / 256);
-  const double tiles = (double)n_list_pages * (page / 32) + (C / 32 + 1) / 2.0;
+  p.n_rb = (int32_t)((rows + 127) / 128);  // 128 rows per workgroup, two workgroups per CU
+  const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
-  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 4.0, max_split);
+  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 2);
   const int64_t n_kt = (int64_t)(n_list_pages + C / page) * (page / 32);
-  p.n_ku = (int32_t)((n_kt + 3) / 4);
+  const int nw = dkdv_waves(d);
+  p.n_ku = (int32_t)((n_kt + nw - 1) / nw);
   const int64_t n_blk = (rows + 63) / 64;
   const int32_t max_rs = (int32_t)std::min<int64_t>(64, n_blk);
-  p.row_splits = best_split((int64_t)n_kvh * p.n_ku, (double)n_blk, 2.0, max_rs);
+  p.row_splits = best_split((int64_t)n_kvh * p.n_ku, (double)n_blk, 2.0, max_rs, 1);
   // [H_q][C] row dots (H_q = n_kvh*G is enough for the heads computed, but the buffer is indexed by
   // absolute head, so size it for every head the pool can address), then dQ partials.
   p.ws_bytes = 0;  // filled by the caller, which knows H_q
-  (void)d;
   return p;
 }
 

@@ -80,6 +80,8 @@ struct BwdPlan {
 };
 
 int num_cus();
+// Waves (32-key tiles) per workgroup of the key-major dK/dV pass.
+constexpr int dkdv_waves(int d) { return d == 128 ? 8 : 4; }
 FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
 BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
 

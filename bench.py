@@ -68,6 +68,72 @@ def cpu_baseline(wl, k_np, v_np, q_np, do_np, c, tokens):
                       f"{L} visible keys, forward+backward, float32; {flop:.3e} FLOP in {dt:.2f} s"}
 
 
+def bench_host1m(args, pkv, synth, dev, t16):
+    """1M-token sparse step with the prior pages in pinned host memory: selection, per-KV-head H2D
+    gathers on a side stream overlapped with the previous head's forward+backward."""
+    import torch
+    from paged_kv_cache_fwd_amd.host_tier import HostTierStep
+
+    wl = synth.WORKLOADS["host1m"]
+    c = wl.chunks[0]
+    C, P, H_q, H_kv, d = wl.chunk, wl.page, wl.h_q, wl.h_kv, wl.d
+    n_prior = wl.n_prior(c)
+    log(f"[bench] host1m: generating and appending {wl.n_pages} pages into pinned host memory")
+    hpool = pkv.Pool(wl.n_pages, P, H_kv, d, grads=True, host_tier=True)
+    hbt = torch.from_numpy(synth.page_permutation(wl)).to(dev)
+    for p0 in range(0, n_prior, 512):
+        n = min(512, n_prior - p0)
+        k, v = synth.kv_tokens(wl, p0, n)
+        hpool.append(hbt, p0 * P, t16(k), t16(v))
+    step = HostTierStep(hpool, hbt, n_prior, C, H_q, wl.top_k, wl.n_local, dev)
+    k_own, v_own = synth.kv_tokens(wl, n_prior, C // P)
+    k_own, v_own = t16(k_own), t16(v_own)
+    q, do = t16(synth.q_chunk(wl, c)), t16(synth.do_chunk(wl, c))
+    o, dq = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((H_q, C), dtype=torch.float32, device=dev)
+
+    def timed(gather):
+        for _ in range(args.warmup):
+            step.append_own(k_own, v_own)
+            step.run(q, do, wl.scale, o, lse, dq, gather=gather)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step.append_own(k_own, v_own)
+            step.run(q, do, wl.scale, o, lse, dq, gather=gather)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    log("[bench] host1m: steps with H2D gathers on a side stream")
+    ms_host = timed(True)
+    log("[bench] host1m: the same steps with the selected pages already on the device")
+    ms_res = timed(False)
+    # H2D gathers alone.
+    sel = step.sel
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for g in range(H_kv):
+            pkv.paged_kv_gather(hpool, step.dev, hbt, sel[g], g, step.slots[g], dev_bt_out=step.bt[g])
+    torch.cuda.synchronize()
+    ms_gather = (time.perf_counter() - t0) / args.steps * 1e3
+    hpool.check()
+    step.dev.check()
+    h2d_bytes = H_kv * step.n_sel * 2 * P * d * 2
+    pairs = pairs_sparse(C, step.n_sel, P)
+    flop = 14.0 * d * H_q * pairs
+    step.free()
+    hpool.free()
+    log(f"[bench] host1m: {ms_host:.3f} ms/step with gathers, {ms_res:.3f} ms resident, gathers alone {ms_gather:.3f} ms")
+    return {"workload": "host1m: 1M tokens, 8160 prior pages in pinned host memory, top-128 + 8 local per KV head, "
+                        "per-head H2D gathers overlapped with the previous head's fwd+bwd",
+            "value": round(flop / (ms_host * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_host, 4),
+            "flop_per_step": flop, "ms_per_step_pages_resident": round(ms_res, 4),
+            "overlap_overhead": round(ms_host / ms_res - 1.0, 4),
+            "h2d_bytes_per_step": h2d_bytes, "h2d_gather_ms": round(ms_gather, 4),
+            "h2d_GBps": round(h2d_bytes / (ms_gather * 1e-3) / 1e9, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +142,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=256, help="chunk tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
+    ap.add_argument("--no-host1m", action="store_true", help="skip the 1M-token host-tier workload")
     ap.add_argument("--topk-only", action="store_true",
                     help="time only the top-K step (for per-workload profiles; prints no headline value)")
     args = ap.parse_args()
@@ -212,6 +279,8 @@ def main():
                 "select_GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1) if sel_ms > 0 else None,
                 "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}
 
+    host1m = None if args.no_host1m else bench_host1m(args, pkv, synth, dev, t16)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle sample ({args.cpu_tokens} tokens)")
@@ -231,6 +300,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "topk256k": topk,
+        "host1m": host1m,
     }
     print(json.dumps(out), flush=True)
 

@@ -182,12 +182,15 @@ int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt,
  * Host-tier gather (pt 2.D, es 2.B, it 2.C: KV moves between host and GPU memory on dedicated
  * streams from pinned memory). For KV head kvh and i < n_sel, copies the (page, kvh) block of
  * logical page sel_dev[i] (host pool, physical page host_bt_dev[sel_dev[i]]) into the same head's
- * block of device pool page dst_pages_dev[i]. Indices stay on the device; nothing synchronises.
+ * block of device pool page dst_pages_dev[i], and, when dev_bt_out_dev is not NULL, records the
+ * mapping dev_bt_out_dev[sel_dev[i]] = dst_pages_dev[i] (a block table for the device pool; its
+ * other entries are left as they are; entries >= n_dev_bt are skipped and flagged). Indices stay on
+ * the device; nothing synchronises; order it against the compute stream with events.
  * host must be a PKV_HOST_TIER pool and dev a device pool of the same page size, heads and dim.
  */
 int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_dev, int32_t n_host_bt,
                     const int32_t* sel_dev, int32_t n_sel, int32_t kvh, const int32_t* dst_pages_dev,
-                    void* stream);
+                    int32_t* dev_bt_out_dev, int32_t n_dev_bt, void* stream);
 
 /*
  * Per-kernel timing (tracing aid, off by default). While enabled, every kernel launch of the

@@ -71,7 +71,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "chunk_attn_bwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I]),
         "chunk_attn_bwd": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _S,
                                 _P]),
-        "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P]),
+        "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P]),
         "pkv_timing_enable": (_I, [ctypes.c_int]),
         "pkv_timing_collect": (ctypes.c_int, []),
         "pkv_timing_get": (_I, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I),
@@ -245,14 +245,18 @@ def chunk_attn_bwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
 
 
 def paged_kv_gather(host: Pool, dev: Pool, host_bt: torch.Tensor, sel_row: torch.Tensor, kvh: int,
-                    dst_pages: torch.Tensor, stream=None):
+                    dst_pages: torch.Tensor, dev_bt_out: Optional[torch.Tensor] = None, stream=None):
     """Copy the (page, kvh) blocks of the logical pages sel_row from a host-tier pool into the device
-    pool pages dst_pages (both int32 device vectors of equal length)."""
+    pool pages dst_pages (both int32 device vectors of equal length); optionally record
+    dev_bt_out[sel_row[i]] = dst_pages[i]."""
     _need(host_bt, torch.int32, "host_bt")
     _need(sel_row, torch.int32, "sel_row")
     _need(dst_pages, torch.int32, "dst_pages")
+    if dev_bt_out is not None:
+        _need(dev_bt_out, torch.int32, "dev_bt_out")
     _check(load().paged_kv_gather(host.handle, dev.handle, _ptr(host_bt), host_bt.numel(), _ptr(sel_row),
-                                  sel_row.numel(), kvh, _ptr(dst_pages), _stream(stream)))
+                                  sel_row.numel(), kvh, _ptr(dst_pages), _ptr(dev_bt_out),
+                                  0 if dev_bt_out is None else dev_bt_out.numel(), _stream(stream)))
 
 
 def timing_enable(on: bool = True):

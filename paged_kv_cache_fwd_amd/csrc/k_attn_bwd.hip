@@ -130,8 +130,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int rl = (wave * T::SEG_PER_WAVE + j) * T::ROWS_PER_SEG + lane / T::CHR;
     seg_off[j] = rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3);
   }
-  auto load_tile = [&](int32_t i, int stage) {
-    int32_t kp;
+  auto load_tile = [&](int32_t i, int stage, int32_t& kp) {
     const uint16_t* src = tile_src(i, kp);
     if (src == nullptr) src = a.kv;  // unreadable page: any in-bounds bytes, the tile is masked
     uint16_t* kt = lds + stage * 2 * T::TILE;
@@ -148,15 +147,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) dq[dt] = (f32x16){};
 
-  if (tb < te) load_tile(tb, 0);
+  int32_t kpos_next = -1;
+  if (tb < te) load_tile(tb, 0, kpos_next);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int32_t i = tb; i < te; ++i) {
     const int cur = (i - tb) & 1;
-    int32_t kpos_t;
-    (void)tile_src(i, kpos_t);
-    if (i + 1 < te) load_tile(i + 1, cur ^ 1);
+    const int32_t kpos_t = kpos_next;
+    if (i + 1 < te) load_tile(i + 1, cur ^ 1, kpos_next);
     const uint16_t* kt = lds + cur * 2 * T::TILE;
     const uint16_t* vt = kt + T::TILE;
     const bool bad = kpos_t < 0;
@@ -167,6 +166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       f32x16 sacc = (f32x16){}, pacc = (f32x16){};
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         const int off = toff<D>(k2 * 32 + l32, ks * 16 + 8 * lg);
@@ -175,6 +175,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         sacc = mfma32(ka, qreg[ks], sacc);
         pacc = mfma32(va, doreg[ks], pacc);
       }
+      __builtin_amdgcn_s_setprio(0);
       float p[16];
 #pragma unroll
       for (int el = 0; el < 16; ++el) p[el] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[el], sl2, -lse2));
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dsb[hf] = as_bf16x8(w);
       }
       // dQ^T[dt] += K^T[dt rows][16 keys] dS^T[16 keys]
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int k_lo = k2 * 32 + hf * 16 + 4 * lg;
@@ -206,6 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           dq[dt] = mfma32(kta, dsb[hf], dq[dt]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -103,8 +103,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int rl = (wave * T::SEG_PER_WAVE + j) * T::ROWS_PER_SEG + lane / T::CHR;
     seg_off[j] = rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3);
   }
-  auto load_tile = [&](int32_t i, int stage) {
-    int32_t kp;
+  auto load_tile = [&](int32_t i, int stage, int32_t& kp) {
     const uint16_t* src = tile_src(i, kp);
     if (src == nullptr) src = a.kv;  // unreadable page: any in-bounds bytes, the tile is masked
     uint16_t* kt = lds + stage * 2 * T::TILE;
@@ -122,19 +121,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) oacc[dt] = (f32x16){};
 
-  if (tb < te) load_tile(tb, 0);
+  int32_t kpos_next = -1;
+  if (tb < te) load_tile(tb, 0, kpos_next);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int32_t i = tb; i < te; ++i) {
     const int cur = (i - tb) & 1;
-    int32_t kpos0;
-    (void)tile_src(i, kpos0);
-    if (i + 1 < te) load_tile(i + 1, cur ^ 1);
+    const int32_t kpos0 = kpos_next;
+    if (i + 1 < te) load_tile(i + 1, cur ^ 1, kpos_next);
     const uint16_t* kt = lds + cur * 2 * T::TILE;
     const uint16_t* vt = kt + T::TILE;
 
     f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
 #pragma unroll
@@ -143,6 +143,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         sacc[k2] = mfma32(ka, qreg[ks], sacc[k2]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     const bool bad = kpos0 < 0;
     if (bad || kpos0 + BK - 1 > q0 + t_min) {
@@ -188,6 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     // O^T[dt] += V^T[dt rows][16 keys] P^T[16 keys]
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
@@ -199,6 +201,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           oacc[dt] = mfma32(va, pb[k2][hf], oacc[dt]);
         }
       }
+    __builtin_amdgcn_s_setprio(0);
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

@@ -120,14 +120,22 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ hos
                                                 uint16_t* __restrict__ dev_kv, int32_t n_dev_pool, int32_t P,
                                                 int32_t H, int32_t D, const int32_t* __restrict__ host_bt,
                                                 int32_t n_host_bt, const int32_t* __restrict__ sel,
-                                                const int32_t* __restrict__ dst_pages, int32_t kvh, int32_t* err) {
+                                                const int32_t* __restrict__ dst_pages, int32_t kvh,
+                                                int32_t* __restrict__ dev_bt_out, int32_t n_dev_bt, int32_t* err) {
   const int32_t i = blockIdx.x;
-  const int32_t hp = phys_page(host_bt, n_host_bt, n_host_pool, sel[i], err);
+  const int32_t lp = sel[i];
+  const int32_t hp = phys_page(host_bt, n_host_bt, n_host_pool, lp, err);
   const int32_t dp = dst_pages[i];
   if (hp < 0) return;
   if (dp < 0 || dp >= n_dev_pool) {
     flag_error(err, 4);
     return;
+  }
+  if (dev_bt_out != nullptr && threadIdx.x == 0) {
+    if (lp < n_dev_bt)
+      dev_bt_out[lp] = dp;
+    else
+      flag_error(err, 3);
   }
   const int64_t n16 = (int64_t)2 * P * D / 8;  // 16-byte chunks in one (page, head) block
   const u32x4* src = reinterpret_cast<const u32x4*>(host_kv + ((int64_t)hp * H + kvh) * 2 * P * D);
@@ -227,12 +235,13 @@ hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, 
 }
 
 hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
-                         const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages, hipStream_t s) {
+                         const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages,
+                         int32_t* dev_bt_out, int32_t n_dev_bt, hipStream_t s) {
   if (n_sel == 0) return hipSuccess;
   {
     TimerScope ts_("k_gather", s);
     hipLaunchKernelGGL(k_gather, dim3(n_sel), dim3(256), 0, s, host.kv, host.n_pages, dev.kv, dev.n_pages, host.page,
-                       host.h_kv, host.d, host_bt, n_host_bt, sel, dst_pages, kvh, dev.err);
+                       host.h_kv, host.d, host_bt, n_host_bt, sel, dst_pages, kvh, dev_bt_out, n_dev_bt, dev.err);
   }
   return hipGetLastError();
 }

@@ -93,7 +93,7 @@ hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, 
                          int32_t n_pages, void* dst, hipStream_t s);
 hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
                          const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages,
-                         hipStream_t s);
+                         int32_t* dev_bt_out, int32_t n_dev_bt, hipStream_t s);
 size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d);
 hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const uint16_t* q,
                        int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t* sel, void* ws,

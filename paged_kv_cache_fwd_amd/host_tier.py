@@ -1,0 +1,93 @@
+"""Sparse chunk step over a pinned-host page tier (stream orchestration of library calls only).
+
+"Out of the Memory Barrier" summaries, pt 2.D / es 2.B / it 2.C: the KV cache lives in pinned CPU
+memory and moves to the GPU on dedicated streams, overlapped with compute; with sparse attention
+only the selected pages move (pt 2.C, it 2.D).
+
+Per chunk: page_topk_select on the host-tier pool (its representatives are on the device), then for
+each KV head g a side stream gathers g's selected (page, head) blocks into g's device slots
+(paged_kv_gather also writes g's device block table) while the compute stream runs forward and
+backward of head g-1. Gradients go to the host-tier pool's device-resident gradient pages through
+its own block table. Every computation is a library kernel; this module only orders them.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import torch
+
+from . import (Pool, chunk_attn_bwd, chunk_attn_bwd_ws_bytes, chunk_attn_fwd, chunk_attn_fwd_ws_bytes, load,
+               page_topk_select, paged_kv_gather)
+
+
+class HostTierStep:
+    """Reusable buffers and streams for the sparse step of one chunk shape over a host-tier pool."""
+
+    def __init__(self, host: Pool, host_bt: torch.Tensor, n_prior: int, C: int, H_q: int, top_k: int,
+                 n_local: int, device: torch.device):
+        assert host.host_tier
+        self.host, self.host_bt = host, host_bt
+        self.n_prior, self.C, self.H_q = n_prior, C, H_q
+        self.top_k, self.n_local = top_k, n_local
+        P, H = host.page, host.h_kv
+        self.n_own = C // P
+        n_cand = max(n_prior - n_local, 0)
+        self.n_sel = min(top_k, n_cand) + (n_prior - n_cand)
+        n_dev = self.n_own + H * self.n_sel
+        # Device pool: the chunk's own pages first, then n_sel slots per KV head.
+        self.dev = Pool(n_dev, P, H, host.d, grads=False)
+        n_bt = host_bt.numel()
+        base = torch.zeros(n_bt, dtype=torch.int32, device=device)
+        base[n_prior:n_prior + self.n_own] = torch.arange(self.n_own, dtype=torch.int32, device=device)
+        self.own_bt = base.clone()
+        self.bt: List[torch.Tensor] = [base.clone() for _ in range(H)]
+        self.slots = [torch.arange(self.n_own + g * self.n_sel, self.n_own + (g + 1) * self.n_sel, dtype=torch.int32,
+                                   device=device) for g in range(H)]
+        self.sel = torch.empty((H, self.n_sel), dtype=torch.int32, device=device)
+        lib = load()
+        self.ws_t = torch.empty(max(lib.page_topk_ws_bytes(host.handle, n_prior, C, H_q), 1), dtype=torch.uint8,
+                                device=device)
+        self.ws_f = torch.empty(max(chunk_attn_fwd_ws_bytes(self.dev, n_prior, self.n_sel, 1, C, H_q), 1),
+                                dtype=torch.uint8, device=device)
+        self.ws_b = torch.empty(max(chunk_attn_bwd_ws_bytes(self.dev, n_prior, self.n_sel, 1, C, H_q), 1),
+                                dtype=torch.uint8, device=device)
+        self.side = torch.cuda.Stream(device=device)
+        self.ready = [torch.cuda.Event() for _ in range(H)]
+        self.done = [torch.cuda.Event() for _ in range(H)]
+        for ev in self.done:
+            ev.record(torch.cuda.current_stream(device))
+
+    def append_own(self, k: torch.Tensor, v: torch.Tensor):
+        """Append the chunk's own K/V ([C][H_kv][d] bf16) into its device pages."""
+        self.dev.append(self.own_bt, self.n_prior * self.dev.page, k, v)
+
+    def run(self, q: torch.Tensor, dout: torch.Tensor, scale: float, o: torch.Tensor, lse: torch.Tensor,
+            dq: torch.Tensor, gather: bool = True):
+        """One sparse step. With gather=False the slots are assumed filled already (for timing the
+        same selection without host traffic)."""
+        compute = torch.cuda.current_stream(q.device)
+        sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local, sel=self.sel,
+                               ws=self.ws_t)
+        sel_ready = torch.cuda.Event()
+        sel_ready.record(compute)
+        H = self.host.h_kv
+        if gather:
+            with torch.cuda.stream(self.side):
+                self.side.wait_event(sel_ready)
+                for g in range(H):
+                    self.side.wait_event(self.done[g])  # slots of g are free once its last backward ended
+                    paged_kv_gather(self.host, self.dev, self.host_bt, sel[g], g, self.slots[g], dev_bt_out=self.bt[g],
+                                    stream=self.side)
+                    self.ready[g].record(self.side)
+        for g in range(H):
+            if gather:
+                compute.wait_event(self.ready[g])
+            chunk_attn_fwd(self.dev, self.bt[g], self.n_prior, q, scale, sel=sel, kvh0=g, n_kvh=1, o=o, lse=lse,
+                           ws=self.ws_f)
+            chunk_attn_bwd(self.dev, self.bt[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
+                           gpool=self.host, gbt=self.host_bt, dq=dq, ws=self.ws_b)
+            self.done[g].record(compute)
+        return sel
+
+    def free(self):
+        self.dev.free()

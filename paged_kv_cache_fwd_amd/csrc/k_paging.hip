@@ -115,43 +115,48 @@ __global__ __launch_bounds__(256) void k_export_rep(const float* __restrict__ re
   dst[idx] = phys >= 0 ? rep[(int64_t)phys * H * D + idx % ((int64_t)H * D)] : 0.0f;
 }
 
-// Host tier -> device: one workgroup per selected page copies the (page, kvh) K|V block.
+// Host tier -> device: a few workgroups stride over the selected pages, each copying a page's
+// (page, kvh) K|V block with 16-byte loads of the device-mapped pinned host memory. The grid is kept
+// small so the copy holds few CU slots while attention kernels run beside it; the host link, not
+// the CU count, bounds its speed.
+constexpr int kGatherBlocks = 16;
 __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ host_kv, int32_t n_host_pool,
                                                 uint16_t* __restrict__ dev_kv, int32_t n_dev_pool, int32_t P,
                                                 int32_t H, int32_t D, const int32_t* __restrict__ host_bt,
-                                                int32_t n_host_bt, const int32_t* __restrict__ sel,
+                                                int32_t n_host_bt, const int32_t* __restrict__ sel, int32_t n_sel,
                                                 const int32_t* __restrict__ dst_pages, int32_t kvh,
                                                 int32_t* __restrict__ dev_bt_out, int32_t n_dev_bt, int32_t* err) {
-  const int32_t i = blockIdx.x;
-  const int32_t lp = sel[i];
-  const int32_t hp = phys_page(host_bt, n_host_bt, n_host_pool, lp, err);
-  const int32_t dp = dst_pages[i];
-  if (hp < 0) return;
-  if (dp < 0 || dp >= n_dev_pool) {
-    flag_error(err, 4);
-    return;
-  }
-  if (dev_bt_out != nullptr && threadIdx.x == 0) {
-    if (lp < n_dev_bt)
-      dev_bt_out[lp] = dp;
-    else
-      flag_error(err, 3);
-  }
-  const int64_t n16 = (int64_t)2 * P * D / 8;  // 16-byte chunks in one (page, head) block
-  const u32x4* src = reinterpret_cast<const u32x4*>(host_kv + ((int64_t)hp * H + kvh) * 2 * P * D);
-  u32x4* dst = reinterpret_cast<u32x4*>(dev_kv + ((int64_t)dp * H + kvh) * 2 * P * D);
-  constexpr int kUnroll = 8;
-  for (int64_t c0 = threadIdx.x; c0 < n16; c0 += 256 * kUnroll) {
-    u32x4 buf[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = c0 + (int64_t)u * 256;
-      if (c < n16) buf[u] = __builtin_nontemporal_load(src + c);
+  for (int32_t i = blockIdx.x; i < n_sel; i += gridDim.x) {
+    const int32_t lp = sel[i];
+    const int32_t hp = phys_page(host_bt, n_host_bt, n_host_pool, lp, err);
+    const int32_t dp = dst_pages[i];
+    if (hp < 0) continue;
+    if (dp < 0 || dp >= n_dev_pool) {
+      flag_error(err, 4);
+      continue;
     }
+    if (dev_bt_out != nullptr && threadIdx.x == 0) {
+      if (lp < n_dev_bt)
+        dev_bt_out[lp] = dp;
+      else
+        flag_error(err, 3);
+    }
+    const int64_t n16 = (int64_t)2 * P * D / 8;  // 16-byte chunks in one (page, head) block
+    const u32x4* src = reinterpret_cast<const u32x4*>(host_kv + ((int64_t)hp * H + kvh) * 2 * P * D);
+    u32x4* dst = reinterpret_cast<u32x4*>(dev_kv + ((int64_t)dp * H + kvh) * 2 * P * D);
+    constexpr int kUnroll = 8;
+    for (int64_t c0 = threadIdx.x; c0 < n16; c0 += 256 * kUnroll) {
+      u32x4 buf[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = c0 + (int64_t)u * 256;
-      if (c < n16) dst[c] = buf[u];
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = c0 + (int64_t)u * 256;
+        if (c < n16) buf[u] = __builtin_nontemporal_load(src + c);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = c0 + (int64_t)u * 256;
+        if (c < n16) dst[c] = buf[u];
+      }
     }
   }
 }
@@ -240,8 +245,9 @@ hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_
   if (n_sel == 0) return hipSuccess;
   {
     TimerScope ts_("k_gather", s);
-    hipLaunchKernelGGL(k_gather, dim3(n_sel), dim3(256), 0, s, host.kv, host.n_pages, dev.kv, dev.n_pages, host.page,
-                       host.h_kv, host.d, host_bt, n_host_bt, sel, dst_pages, kvh, dev_bt_out, n_dev_bt, dev.err);
+    hipLaunchKernelGGL(k_gather, dim3(n_sel < kGatherBlocks ? n_sel : kGatherBlocks), dim3(256), 0, s, host.kv,
+                       host.n_pages, dev.kv, dev.n_pages, host.page, host.h_kv, host.d, host_bt, n_host_bt, sel, n_sel,
+                       dst_pages, kvh, dev_bt_out, n_dev_bt, dev.err);
   }
   return hipGetLastError();
 }

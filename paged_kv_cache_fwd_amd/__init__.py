@@ -43,11 +43,12 @@ _F = ctypes.c_float
 
 
 def load(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load the compiled library (once). Raises if it was not built."""
+    """Load the compiled library (once). Raises if it was not built. PKV_LIBRARY in the environment
+    names another build of the same library to use instead of the in-tree one."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("PKV_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with `python -m paged_kv_cache_fwd_amd.build` "
                            "or __graft_entry__.build(); there is no fallback implementation")

@@ -38,29 +38,31 @@ def _run(cmd):
     return r.stderr
 
 
-def build(verbose: bool = False, extra_hip_flags=None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_hip_flags=None, out: str = LIB, build_dir: str = BUILD,
+          csrc: str = CSRC) -> str:
+    """Compile every source under `csrc` and link `out` (default: the in-tree libpkv.so)."""
+    os.makedirs(build_dir, exist_ok=True)
     jobs = []
     objs = []
     for src, flags in KERNELS.items():
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
-        jobs.append([HIPCC, *HIP_FLAGS, *flags, *(extra_hip_flags or []), "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *flags, *(extra_hip_flags or []), "-c", os.path.join(csrc, src), "-o", obj])
     for src in HOST:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
         jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
-                     "-I" + os.path.join(ROCM, "include"), "-c", os.path.join(CSRC, src), "-o", obj])
+                     "-I" + os.path.join(ROCM, "include"), "-c", os.path.join(csrc, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         logs = list(ex.map(_run, jobs))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
         for lg in logs:
             if lg.strip():
                 sys.stderr.write(lg)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

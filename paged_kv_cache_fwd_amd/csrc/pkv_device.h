@@ -88,6 +88,14 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int k_lo, int
 
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Wait until at most N of this wave's vector-memory operations are outstanding (they complete in
+// issue order); LDS and scalar counters are not waited on. gfx9 s_waitcnt encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Direct global -> LDS loads (global_load_lds_dwordx4 / _dword): lane L of the wave writes its 16
 // (or 4) bytes to lds_base + 16 L (or 4 L). lds_base must be the same for every lane of the wave.
 __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {

@@ -143,8 +143,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--no-host1m", action="store_true", help="skip the 1M-token host-tier workload")
-    ap.add_argument("--topk-only", action="store_true",
-                    help="time only the top-K step (for per-workload profiles; prints no headline value)")
+    ap.add_argument("--only", choices=("topk", "host1m"),
+                    help="time only this workload (for per-workload profiles; prints no headline value)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="first run one plain streaming kernel (torch.neg on fp32) over this many MiB, as the "
+                         "known-size reference for byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path",
@@ -159,14 +162,27 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     pkv.load()
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration kernel: reads {n * 4} B, writes {n * 4} B")
+        del src, dst
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.only == "host1m":
+        print(json.dumps(bench_host1m(args, pkv, synth, dev, t16)), flush=True)
+        return
     wl = synth.WORKLOADS["dense256k"]
     wlk = synth.WORKLOADS["topk256k"]
     c = wl.chunks[0]
     C, P, H_q, H_kv, d = wl.chunk, wl.page, wl.h_q, wl.h_kv, wl.d
     q0, n_prior, n_pages = wl.q0(c), wl.n_prior(c), wl.n_pages
-
-    def t16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     log(f"[bench] generating {n_pages} pages of K/V ({wl.note})")
     t0 = time.time()
@@ -231,7 +247,7 @@ def main():
 
     pd = pairs_dense(C, q0)
     flop_dense = 14.0 * d * H_q * pd
-    if args.topk_only:
+    if args.only == "topk":
         ps = pairs_sparse(C, n_sel, P)
         ms_topk, kt_topk = run(step_topk, "topk256k")
         print(json.dumps({"workload": "topk256k", "ms_per_step": round(ms_topk, 4),

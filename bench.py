@@ -28,6 +28,30 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 HBM_PEAK_GBS = 8000.0
 
 
+# HBM bytes per launch of the dense 256K step's attention kernels, from one FETCH_SIZE and one
+# WRITE_SIZE rocprofv3 pass each, scaled by what those counters read for a plain 1 GiB streaming
+# kernel (x2.0 fetch, x1.0 write). Valid only for the kernel sources they were taken on.
+TRAFFIC_SOURCES = ("paged_kv_cache_fwd_amd/csrc/k_attn_fwd.hip", "paged_kv_cache_fwd_amd/csrc/k_attn_bwd.hip",
+                   "paged_kv_cache_fwd_amd/csrc/pkv_device.h", "paged_kv_cache_fwd_amd/csrc/pkv_internal.h",
+                   "paged_kv_cache_fwd_amd/csrc/pkv_abi.cpp", "paged_kv_cache_fwd_amd/build.py")
+TRAFFIC_SHA = "269c14f84e2e5951"
+TRAFFIC_BYTES = {"k_attn_fwd": (2.0 * 3289759 * 1024, 231168 * 1024),
+                 "k_bwd_dq": (2.0 * 1242567 * 1024, 229376 * 1024),
+                 "k_bwd_dkdv": (2.0 * 1394619 * 1024, 1048576 * 1024)}
+
+
+def traffic_bytes(kernel):
+    """(fetch, write) bytes per launch if the attention sources are those the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != TRAFFIC_SHA or kernel not in TRAFFIC_BYTES:
+        return None
+    return TRAFFIC_BYTES[kernel]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -269,8 +293,11 @@ def main():
     avg_ms = tot_ms / n_l
     if dom in kernel_flop:
         ach = kernel_flop[dom] / (avg_ms * 1e-3) / 1e12
+        tb = traffic_bytes(dom)
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None if tb is None else int(tb[0] + tb[1]),
+                    "traffic_fetch_write": None if tb is None else [int(tb[0]), int(tb[1])],
                     "avg_launch_ms": round(avg_ms, 4),
                     "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_dense.items()}}
     else:

@@ -20,6 +20,7 @@ KERNELS = {
     # MFMA results stay in architectural VGPRs (the softmax and gradient math reads them there).
     "k_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_attn_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 HOST = ["pkv_abi.cpp"]
 

@@ -183,9 +183,8 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, i
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
   p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 2);
   const int64_t n_kt = (int64_t)(n_list_pages + C / page) * (page / 32);
-  const int nw = dkdv_waves(d);
-  p.n_ku = (int32_t)((n_kt + nw - 1) / nw);
-  const int64_t n_blk = (rows + 63) / 64;
+  p.n_ku = (int32_t)((n_kt + NKT_TILES_PER_WG - 1) / NKT_TILES_PER_WG);
+  const int64_t n_blk = (rows + 31) / 32;
   const int32_t max_rs = (int32_t)std::min<int64_t>(64, n_blk);
   p.row_splits = best_split((int64_t)n_kvh * p.n_ku, (double)n_blk, 2.0, max_rs, 1);
   // [H_q][C] row dots (H_q = n_kvh*G is enough for the heads computed, but the buffer is indexed by
@@ -516,7 +515,8 @@ int chunk_attn_fwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, in
 }
 
 static size_t bwd_ws(const pkv_pool* pool, const pkv::BwdPlan& plan, int32_t n_kvh, int32_t C, int32_t H_q) {
-  const size_t dbytes = 2 * (((size_t)H_q * C + 63) & ~(size_t)63) * 4;  // row dots + base-2 lse
+  // -D, lse * log2 e and -lse / scale, each with 64 padding entries
+  const size_t dbytes = 3 * ((((size_t)H_q * C + 63) & ~(size_t)63) + 64) * 4;
   const size_t dq = plan.splits > 1 ? (size_t)plan.splits * n_kvh * C * (H_q / pool->h_kv) * pool->d * 4 : 0;
   return align256(dbytes + dq);
 }

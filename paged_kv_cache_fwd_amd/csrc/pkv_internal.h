@@ -74,14 +74,14 @@ struct FwdPlan {
 struct BwdPlan {
   int32_t n_rb;        // dQ pass: row blocks of 256 rows per KV head
   int32_t splits;      // dQ pass: key-range splits
-  int32_t n_ku;        // dK/dV pass: key units of 128 keys per KV head
+  int32_t n_ku;        // dK/dV pass: key units of 256 keys per KV head
   int32_t row_splits;  // dK/dV pass: row-range splits
   size_t ws_bytes;
 };
 
 int num_cus();
-// Waves (32-key tiles) per workgroup of the key-major dK/dV pass.
-constexpr int dkdv_waves(int d) { return d == 128 ? 8 : 4; }
+// 32-key tiles per workgroup of the key-major dK/dV pass (4 waves x 2 tiles).
+constexpr int NKT_TILES_PER_WG = 8;
 FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
 BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
 
@@ -100,5 +100,8 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
                        hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, const FwdPlan& plan, uint16_t* o, float* lse, void* ws, hipStream_t s);
 hipError_t launch_bwd(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, void* ws, hipStream_t s);
+template <int D>
+hipError_t launch_dkdv(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, const float* ndbuf,
+                       const float* nlsbuf, int32_t pad_row, hipStream_t s);
 
 }  // namespace pkv

@@ -87,7 +87,14 @@ def cpu_baseline(wl, k_np, v_np, q_np, do_np, c, tokens):
     dt = time.perf_counter() - t0
     pairs = int(sum(q0 + t + 1 for t in rows)) * G
     flop = 14.0 * wl.d * pairs
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"KV head 0 with its {G} query heads, last {tokens} of {wl.chunk} chunk tokens against all "
                       f"{L} visible keys, forward+backward, float32; {flop:.3e} FLOP in {dt:.2f} s"}
 
@@ -141,6 +148,19 @@ def bench_host1m(args, pkv, synth, dev, t16):
             pkv.paged_kv_gather(hpool, step.dev, hbt, sel[g], g, step.slots[g], dev_bt_out=step.bt[g])
     torch.cuda.synchronize()
     ms_gather = (time.perf_counter() - t0) / args.steps * 1e3
+    # Pinned host -> device copy of the same byte count, for the link's practical peak.
+    h2d_bytes_all = H_kv * step.n_sel * 2 * P * d * 2
+    src = torch.empty(h2d_bytes_all, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(h2d_bytes_all, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    ms_memcpy = (time.perf_counter() - t0) / args.steps * 1e3
+    del src, dst
     hpool.check()
     step.dev.check()
     h2d_bytes = H_kv * step.n_sel * 2 * P * d * 2
@@ -155,7 +175,8 @@ def bench_host1m(args, pkv, synth, dev, t16):
             "flop_per_step": flop, "ms_per_step_pages_resident": round(ms_res, 4),
             "overlap_overhead": round(ms_host / ms_res - 1.0, 4),
             "h2d_bytes_per_step": h2d_bytes, "h2d_gather_ms": round(ms_gather, 4),
-            "h2d_GBps": round(h2d_bytes / (ms_gather * 1e-3) / 1e9, 2)}
+            "h2d_GBps": round(h2d_bytes / (ms_gather * 1e-3) / 1e9, 2),
+            "h2d_pinned_memcpy_GBps": round(h2d_bytes / (ms_memcpy * 1e-3) / 1e9, 2)}
 
 
 def main():
@@ -249,6 +270,8 @@ def main():
         pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, sel=s, o=o, lse=lse, ws=ws_f)
         pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, sel=s, dq=dq, ws=ws_b)
 
+    stats = {}
+
     def run(step, name):
         log(f"[bench] {name}: {args.warmup} warmup steps")
         for _ in range(args.warmup):
@@ -258,15 +281,20 @@ def main():
         torch.cuda.synchronize()
         pkv.timing_enable(True)
         log(f"[bench] {name}: {args.steps} timed steps")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        ev[0].record()
+        for k in range(args.steps):
             step()
+            ev[k + 1].record()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         pkv.timing_enable(False)
         kt = pkv.timing_collect()
         pool.check()
+        per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps))
+        stats[name] = {"median_ms": round(per[len(per) // 2], 4), "min_ms": round(per[0], 4)}
         return dt / args.steps * 1e3, kt
 
     pd = pairs_dense(C, q0)
@@ -291,6 +319,12 @@ def main():
     dom = max(kt_dense.items(), key=lambda x: x[1][1])[0]
     n_l, tot_ms = kt_dense[dom]
     avg_ms = tot_ms / n_l
+    def split_ms(kt):
+        fwd = sum(v[1] / v[0] for k, v in kt.items() if k in ("k_attn_fwd", "k_fwd_combine"))
+        bwd = sum(v[1] / v[0] for k, v in kt.items() if k.startswith("k_bwd"))
+        return round(fwd, 4), round(bwd, 4)
+
+    fwd_ms, bwd_ms = split_ms(kt_dense)
     if dom in kernel_flop:
         ach = kernel_flop[dom] / (avg_ms * 1e-3) / 1e12
         tb = traffic_bytes(dom)
@@ -303,6 +337,22 @@ def main():
     else:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": None, "traffic": None, "avg_launch_ms": round(avg_ms, 4)}
+
+    def select_b2b(n=50):
+        """page_topk_select alone, n calls back to back: steady-state per-call time and GB/s."""
+        for _ in range(3):
+            pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        b = C * H_q * d * 2 + (n_prior - n_local) * H_kv * d * 4
+        return {"ms_per_call": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b,
+                "pct_hbm_peak": round(100.0 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
     topk = None
     if not args.no_topk:
@@ -320,6 +370,9 @@ def main():
                 "step_speedup_vs_dense": round(ms_dense / ms_topk, 2),
                 "select_ms": round(sel_ms, 4),
                 "select_GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1) if sel_ms > 0 else None,
+                "select_back_to_back": select_b2b(),
+                "fwd_ms": split_ms(kt_topk)[0], "bwd_ms": split_ms(kt_topk)[1],
+                "step_stats": stats.get("topk256k"),
                 "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}
 
     host1m = None if args.no_host1m else bench_host1m(args, pkv, synth, dev, t16)
@@ -341,6 +394,7 @@ def main():
                    "flop_per_step": flop_dense, "pct_bf16_peak": round(100.0 * tflops_dense / PEAK_BF16_TFLOPS, 2),
                    "step": "append own block + forward + backward (dK/dV accumulated into gradient pages)"},
         "roofline": roofline,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "step_stats": stats.get("dense256k"),
         "cpu_baseline": cpu,
         "topk256k": topk,
         "host1m": host1m,

@@ -134,6 +134,8 @@ int paged_kv_check(pkv_pool* pool);
  * Output sel_dev: [H_kv][n_sel] int32 logical page ids, n_sel = min(top_k, n_cand) + (n_prior -
  * n_cand), also stored to *n_sel_out (host; known without synchronising).
  * q_dev: [C][H_q][head_dim] bf16, C % 64 == 0. ws_dev: at least page_topk_ws_bytes(...) bytes.
+ * Errors: PKV_E_INVALID (shapes), PKV_E_UNSUPPORTED (H_q / H_kv > 128), PKV_E_RANGE (n_prior >
+ * n_bt), PKV_E_NOMEM (workspace too small); nothing is enqueued on error.
  */
 size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int32_t H_q);
 int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,

@@ -38,17 +38,22 @@ __global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ 
                                                    int32_t n_pool, int32_t P, int32_t H, int32_t D,
                                                    const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
                                                    int32_t n_lp, int32_t* err) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)n_lp * H * D) return;
-  const int32_t j = (int32_t)(idx % D);
-  const int32_t g = (int32_t)((idx / D) % H);
-  const int32_t lp = lp0 + (int32_t)(idx / ((int64_t)D * H));
+  // One workgroup per (logical page, KV head): the P x D key block is staged in LDS with coalesced
+  // 16-byte loads, then thread j adds column j in token order.
+  __shared__ __attribute__((aligned(16))) uint16_t kb[128 * 128];
+  const int32_t g = blockIdx.x % H;
+  const int32_t lp = lp0 + blockIdx.x / H;
   const int32_t phys = phys_page(bt, n_bt, n_pool, lp, err);
   if (phys < 0) return;
-  const uint16_t* kp = kv + (((int64_t)phys * H + g) * 2) * P * D + j;
-  float acc = 0.0f;
-  for (int32_t t = 0; t < P; ++t) acc = __fadd_rn(acc, bf16_to_f32(kp[(int64_t)t * D]));
-  rep[((int64_t)phys * H + g) * D + j] = __fmul_rn(acc, 1.0f / (float)P);
+  const uint16_t* kp = kv + (((int64_t)phys * H + g) * 2) * P * D;
+  for (int32_t i = threadIdx.x; i < P * D / 8; i += 256)
+    reinterpret_cast<u32x4*>(kb)[i] = reinterpret_cast<const u32x4*>(kp)[i];
+  __syncthreads();
+  for (int32_t j = threadIdx.x; j < D; j += 256) {
+    float acc = 0.0f;
+    for (int32_t t = 0; t < P; ++t) acc = __fadd_rn(acc, bf16_to_f32(kb[t * D + j]));
+    rep[((int64_t)phys * H + g) * D + j] = __fmul_rn(acc, 1.0f / (float)P);
+  }
 }
 
 // Zero the gradient blocks of logical pages [lp0, lp0 + n_lp) (bt == NULL: physical = logical).
@@ -119,8 +124,11 @@ __global__ __launch_bounds__(256) void k_export_rep(const float* __restrict__ re
 // (page, kvh) K|V block with 16-byte loads of the device-mapped pinned host memory. The grid is kept
 // small so the copy holds few CU slots while attention kernels run beside it; the host link, not
 // the CU count, bounds its speed.
+// 16 workgroups of 256 threads, 8 loads of 16 bytes in flight per thread: a CU sustains about
+// 11 GB/s of reads from device-mapped host memory, so the 16 together saturate the host link.
 constexpr int kGatherBlocks = 16;
-__global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ host_kv, int32_t n_host_pool,
+constexpr int kGatherThreads = 256;
+__global__ __launch_bounds__(kGatherThreads) void k_gather(const uint16_t* __restrict__ host_kv, int32_t n_host_pool,
                                                 uint16_t* __restrict__ dev_kv, int32_t n_dev_pool, int32_t P,
                                                 int32_t H, int32_t D, const int32_t* __restrict__ host_bt,
                                                 int32_t n_host_bt, const int32_t* __restrict__ sel, int32_t n_sel,
@@ -145,16 +153,16 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t* __restrict__ hos
     const u32x4* src = reinterpret_cast<const u32x4*>(host_kv + ((int64_t)hp * H + kvh) * 2 * P * D);
     u32x4* dst = reinterpret_cast<u32x4*>(dev_kv + ((int64_t)dp * H + kvh) * 2 * P * D);
     constexpr int kUnroll = 8;
-    for (int64_t c0 = threadIdx.x; c0 < n16; c0 += 256 * kUnroll) {
+    for (int64_t c0 = threadIdx.x; c0 < n16; c0 += kGatherThreads * kUnroll) {
       u32x4 buf[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int64_t c = c0 + (int64_t)u * 256;
+        const int64_t c = c0 + (int64_t)u * kGatherThreads;
         if (c < n16) buf[u] = __builtin_nontemporal_load(src + c);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int64_t c = c0 + (int64_t)u * 256;
+        const int64_t c = c0 + (int64_t)u * kGatherThreads;
         if (c < n16) dst[c] = buf[u];
       }
     }
@@ -188,11 +196,10 @@ hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, 
   const int32_t lp_a = ((first_full + 1) * P - 1 >= pos0) ? first_full : first_full + 1;
   const int32_t lp_b = (pos0 + n) / P;                    // pages fully ending before pos0 + n
   if (lp_b > lp_a) {
-    const int64_t work = (int64_t)(lp_b - lp_a) * H * D;
     {
       TimerScope ts_("k_page_reps", s);
-      hipLaunchKernelGGL(k_page_reps, dim3(grid_for(work)), dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, P, H, D,
-                         bt, n_bt, lp_a, lp_b - lp_a, pool.err);
+      hipLaunchKernelGGL(k_page_reps, dim3((unsigned)((lp_b - lp_a) * H)), dim3(256), 0, s, pool.kv, pool.rep,
+                         pool.n_pages, P, H, D, bt, n_bt, lp_a, lp_b - lp_a, pool.err);
     }
   }
   return hipGetLastError();
@@ -245,7 +252,7 @@ hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_
   if (n_sel == 0) return hipSuccess;
   {
     TimerScope ts_("k_gather", s);
-    hipLaunchKernelGGL(k_gather, dim3(n_sel < kGatherBlocks ? n_sel : kGatherBlocks), dim3(256), 0, s, host.kv,
+    hipLaunchKernelGGL(k_gather, dim3(n_sel < kGatherBlocks ? n_sel : kGatherBlocks), dim3(kGatherThreads), 0, s, host.kv,
                        host.n_pages, dev.kv, dev.n_pages, host.page, host.h_kv, host.d, host_bt, n_host_bt, sel, n_sel,
                        dst_pages, kvh, dev_bt_out, n_dev_bt, dev.err);
   }

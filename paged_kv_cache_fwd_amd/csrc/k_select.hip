@@ -30,20 +30,35 @@ __global__ __launch_bounds__(256) void k_qsum_part(const uint16_t* __restrict__ 
   part[idx] = acc;
 }
 
-// qsum[g][j]: one thread per (g, j).
-__global__ __launch_bounds__(256) void k_qsum(const float* __restrict__ part, int32_t H_kv, int32_t G, int32_t D,
-                                              int32_t nb, float* __restrict__ qsum) {
-  const int32_t idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= H_kv * D) return;
-  const int32_t j = idx % D, g = idx / D;
-  float qs = 0.0f;
-  for (int32_t hh = 0; hh < G; ++hh) {
+// qsum[g][j], one workgroup per KV head g: hsum[hh][j] = sum_b part[gG+hh][b][j] by threads
+// (hh, j) with the part values fetched 16 at a time ahead of the in-order adds, then
+// qsum[g][j] = sum_hh hsum[hh][j] in order by threads j.
+constexpr int kQsumThreads = 1024;
+__global__ __launch_bounds__(kQsumThreads) void k_qsum(const float* __restrict__ part, int32_t H_kv, int32_t G,
+                                                       int32_t D, int32_t nb, float* __restrict__ qsum) {
+  extern __shared__ float hsum[];  // [G][D]
+  const int32_t g = blockIdx.x;
+  for (int32_t idx = threadIdx.x; idx < G * D; idx += kQsumThreads) {
+    const int32_t hh = idx / D, j = idx % D;
     const float* ph = part + ((int64_t)(g * G + hh) * nb) * D + j;
     float hs = 0.0f;
-    for (int32_t b = 0; b < nb; ++b) hs = __fadd_rn(hs, ph[(int64_t)b * D]);
-    qs = __fadd_rn(qs, hs);
+    int32_t b = 0;
+    for (; b + 16 <= nb; b += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = ph[(int64_t)(b + u) * D];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) hs = __fadd_rn(hs, v[u]);
+    }
+    for (; b < nb; ++b) hs = __fadd_rn(hs, ph[(int64_t)b * D]);
+    hsum[idx] = hs;
   }
-  qsum[idx] = qs;
+  __syncthreads();
+  for (int32_t j = threadIdx.x; j < D; j += kQsumThreads) {
+    float qs = 0.0f;
+    for (int32_t hh = 0; hh < G; ++hh) qs = __fadd_rn(qs, hsum[hh * D + j]);
+    qsum[(int64_t)g * D + j] = qs;
+  }
 }
 
 // score[g][p] for candidate logical pages p < n_cand; an unreadable page scores NaN (ranks last).
@@ -119,18 +134,32 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
         if ((key & mask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0, rem = s_remaining;
-        for (int dg = 255; dg >= 0; --dg) {
-          const uint32_t c = hist[dg];
-          if (cum + c >= rem) {
-            s_prefix = prefix | ((uint64_t)dg << shift);
-            s_remaining = rem - cum;
-            break;
-          }
-          cum += c;
+      if (tid < 64) {
+        // Wave 0 finds the digit where the running count from the top reaches `remaining`:
+        // lane l owns digits 4l..4l+3; suffix sums over lanes, then a walk down the lane's own 4.
+        const uint32_t rem = s_remaining;
+        uint32_t c[4], own = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[i] = hist[4 * tid + i];
+          own += c[i];
         }
-        s_mask = mask | ((uint64_t)255 << shift);
+        uint32_t suf = own;  // sum over lanes >= tid
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t v = __shfl_down(suf, off, 64);
+          if (tid + off < 64) suf += v;
+        }
+        uint32_t cum = suf - own;  // digits above this lane's
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          if (cum < rem && cum + c[i] >= rem) {
+            s_prefix = prefix | ((uint64_t)(4 * tid + i) << shift);
+            s_remaining = rem - cum;
+          }
+          cum += c[i];
+        }
+        if (tid == 0) s_mask = mask | ((uint64_t)255 << shift);
       }
       __syncthreads();
     }
@@ -193,7 +222,7 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
     }
     {
       TimerScope ts_("k_qsum", s);
-      hipLaunchKernelGGL(k_qsum, dim3((unsigned)((H * D + 255) / 256)), dim3(256), 0, s, part, H, G, D, nb, qsum);
+      hipLaunchKernelGGL(k_qsum, dim3((unsigned)H), dim3(kQsumThreads), (size_t)G * D * 4, s, part, H, G, D, nb, qsum);
     }
     {
       TimerScope ts_("k_scores", s);

@@ -473,6 +473,7 @@ int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, 
   if (C <= 0 || C % 64 != 0) return fail(PKV_E_INVALID, "C=%d must be a positive multiple of 64", C);
   if (H_q <= 0 || H_q % pool->h_kv != 0) return fail(PKV_E_INVALID, "H_q=%d must be a multiple of H_kv=%d", H_q, pool->h_kv);
   if (top_k < 0 || n_local < 0 || n_prior < 0) return fail(PKV_E_INVALID, "top_k, n_local, n_prior must be >= 0");
+  if (H_q / pool->h_kv > 128) return fail(PKV_E_UNSUPPORTED, "H_q/H_kv=%d exceeds 128", H_q / pool->h_kv);
   if (n_prior > n_bt) return fail(PKV_E_RANGE, "n_prior=%d exceeds the block table (%d)", n_prior, n_bt);
   const int32_t n_cand = n_prior > n_local ? n_prior - n_local : 0;
   const int32_t kk = std::min(top_k, n_cand);

@@ -68,17 +68,25 @@ class HostTierStep:
         compute = torch.cuda.current_stream(q.device)
         sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local, sel=self.sel,
                                ws=self.ws_t)
-        sel_ready = torch.cuda.Event()
-        sel_ready.record(compute)
         H = self.host.h_kv
-        if gather:
+
+        def enqueue_gather(g, after=None):
+            # Events are waited on at their latest record: `after` is this step's selection, done[g]
+            # the previous step's backward of head g (recorded again only later in this step).
             with torch.cuda.stream(self.side):
-                self.side.wait_event(sel_ready)
-                for g in range(H):
-                    self.side.wait_event(self.done[g])  # slots of g are free once its last backward ended
-                    paged_kv_gather(self.host, self.dev, self.host_bt, sel[g], g, self.slots[g], dev_bt_out=self.bt[g],
-                                    stream=self.side)
-                    self.ready[g].record(self.side)
+                self.side.wait_event(self.done[g])  # slots of g are free once its last backward ended
+                if after is not None:
+                    self.side.wait_event(after)
+                paged_kv_gather(self.host, self.dev, self.host_bt, sel[g], g, self.slots[g], dev_bt_out=self.bt[g],
+                                stream=self.side)
+                self.ready[g].record(self.side)
+
+        if gather:
+            sel_ready = torch.cuda.Event()
+            sel_ready.record(compute)
+            enqueue_gather(0, sel_ready)
+            for g in range(1, H):
+                enqueue_gather(g)
         for g in range(H):
             if gather:
                 compute.wait_event(self.ready[g])

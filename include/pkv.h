@@ -133,7 +133,8 @@ int paged_kv_check(pkv_pool* pool);
  *   sorted ascending, followed by the n_local most recent prior pages [n_cand, n_prior).
  * Output sel_dev: [H_kv][n_sel] int32 logical page ids, n_sel = min(top_k, n_cand) + (n_prior -
  * n_cand), also stored to *n_sel_out (host; known without synchronising).
- * q_dev: [C][H_q][head_dim] bf16, C % 64 == 0. ws_dev: at least page_topk_ws_bytes(...) bytes.
+ * q_dev: [C][H_q][head_dim] bf16, 16-byte aligned, C % 64 == 0. ws_dev: at least
+ * page_topk_ws_bytes(...) bytes.
  * Errors: PKV_E_INVALID (shapes), PKV_E_UNSUPPORTED (H_q / H_kv > 128), PKV_E_RANGE (n_prior >
  * n_bt), PKV_E_NOMEM (workspace too small); nothing is enqueued on error.
  */

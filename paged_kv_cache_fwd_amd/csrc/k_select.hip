@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qsum, 
     const f32x4* r = reinterpret_cast<const f32x4*>(rep + ((int64_t)phys * H_kv + g) * D);
     const float* qs = qsum + (int64_t)g * D;
     acc = 0.0f;
+#pragma unroll 8
     for (int32_t j4 = 0; j4 < D / 4; ++j4) {
       const f32x4 rv = r[j4];
       acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 0], rv[0]));
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
                                                       int32_t* __restrict__ sel) {
   __shared__ uint32_t hist[256];
   __shared__ uint64_t s_prefix, s_mask;
-  __shared__ uint32_t s_remaining;
+  __shared__ uint32_t s_remaining, s_done;
   __shared__ uint32_t wave_tot[kSelThreads / 64];
   const int32_t g = blockIdx.x;
   const int32_t tid = threadIdx.x;
@@ -123,6 +124,7 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
       s_prefix = 0;
       s_mask = 0;
       s_remaining = (uint32_t)K;
+      s_done = 0u;
     }
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
@@ -156,12 +158,15 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
           if (cum < rem && cum + c[i] >= rem) {
             s_prefix = prefix | ((uint64_t)(4 * tid + i) << shift);
             s_remaining = rem - cum;
+            // Every key of this digit is taken: keys >= prefix (lower digits zero) are the set.
+            if (cum + c[i] == rem) s_done = 1u;
           }
           cum += c[i];
         }
         if (tid == 0) s_mask = mask | ((uint64_t)255 << shift);
       }
       __syncthreads();
+      if (s_done) break;
     }
     threshold = s_prefix;
   }

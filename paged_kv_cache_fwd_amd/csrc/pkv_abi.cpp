@@ -470,6 +470,7 @@ int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, 
                      int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes, void* stream) {
   if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
   if (!bt_dev || !q_dev || !n_sel_out) return fail(PKV_E_INVALID, "NULL block table, q or n_sel_out");
+  if (!aligned16(q_dev)) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
   if (C <= 0 || C % 64 != 0) return fail(PKV_E_INVALID, "C=%d must be a positive multiple of 64", C);
   if (H_q <= 0 || H_q % pool->h_kv != 0) return fail(PKV_E_INVALID, "H_q=%d must be a multiple of H_kv=%d", H_q, pool->h_kv);
   if (top_k < 0 || n_local < 0 || n_prior < 0) return fail(PKV_E_INVALID, "top_k, n_local, n_prior must be >= 0");

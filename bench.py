@@ -5,7 +5,8 @@ Workload (one step = the whole hot path over one synthetic batch, inputs residen
   dense256k  append the final 4096-token chunk's K/V into its pages, forward, backward
              (28 query / 4 KV heads, d=128, page 128, 2016 prior pages + the causal own block);
   topk256k   the same plus page selection (top-64 by mean-key score + 4 most recent pages), with
-             forward and backward over the selected pages only.
+             forward and backward over the selected pages only;
+  local256k  a local layer: the most recent prior page and the causal own block (top_k = 0).
 The headline value is the dense step's algorithmic TFLOP/s (forward 4*d*H_q*pairs, backward
 10*d*H_q*pairs); the top-K step is reported beside it.
 
@@ -26,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "chunk attn fwd+bwd TFLOP/s (and % bf16 peak) at 256K ctx, dense and top-K paged"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 HBM_PEAK_GBS = 8000.0
+LOCAL_WINDOW = 1  # pages kept by a local (sliding-window) layer
 
 
 # HBM bytes per launch of the dense 256K step's attention kernels, from one FETCH_SIZE and one
@@ -249,12 +251,11 @@ def main():
     top_k, n_local = wlk.top_k, wlk.n_local
     n_sel = min(top_k, n_prior - n_local) + n_local
     sel = torch.empty((H_kv, n_sel), dtype=torch.int32, device=dev)
-    ws_f = torch.empty(max(pkv.chunk_attn_fwd_ws_bytes(pool, n_prior, -1, H_kv, C, H_q),
-                           pkv.chunk_attn_fwd_ws_bytes(pool, n_prior, n_sel, H_kv, C, H_q), 1),
-                       dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(pkv.chunk_attn_bwd_ws_bytes(pool, n_prior, -1, H_kv, C, H_q),
-                           pkv.chunk_attn_bwd_ws_bytes(pool, n_prior, n_sel, H_kv, C, H_q), 1),
-                       dtype=torch.uint8, device=dev)
+    sel_l = torch.empty((H_kv, LOCAL_WINDOW), dtype=torch.int32, device=dev)
+    ws_f = torch.empty(max(max(pkv.chunk_attn_fwd_ws_bytes(pool, n_prior, ns, H_kv, C, H_q)
+                               for ns in (-1, n_sel, LOCAL_WINDOW)), 1), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(max(pkv.chunk_attn_bwd_ws_bytes(pool, n_prior, ns, H_kv, C, H_q)
+                               for ns in (-1, n_sel, LOCAL_WINDOW)), 1), dtype=torch.uint8, device=dev)
     ws_t = torch.empty(max(pkv.load().page_topk_ws_bytes(pool.handle, n_prior, C, H_q), 1), dtype=torch.uint8,
                        device=dev)
     torch.cuda.synchronize()
@@ -263,6 +264,12 @@ def main():
         pool.append(bt, q0, k_own, v_own)
         pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, o=o, lse=lse, ws=ws_f)
         pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, dq=dq, ws=ws_b)
+
+    def step_local():
+        pool.append(bt, q0, k_own, v_own)
+        s = pkv.page_topk_select(pool, bt, n_prior, q, 0, LOCAL_WINDOW, sel=sel_l, ws=ws_t)
+        pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, sel=s, o=o, lse=lse, ws=ws_f)
+        pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, sel=s, dq=dq, ws=ws_b)
 
     def step_topk():
         pool.append(bt, q0, k_own, v_own)
@@ -375,6 +382,20 @@ def main():
                 "step_stats": stats.get("topk256k"),
                 "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}
 
+    local = None
+    if not args.no_topk:
+        ms_local, kt_local = run(step_local, "local256k")
+        flop_local = 14.0 * d * H_q * pairs_sparse(C, LOCAL_WINDOW, P)
+        log(f"[bench] local256k: {ms_local:.3f} ms/step, {flop_local / (ms_local * 1e-3) / 1e12:.1f} TFLOP/s")
+        local = {"workload": f"local256k: window of the {LOCAL_WINDOW} most recent prior page(s) "
+                             f"({LOCAL_WINDOW * P} tokens) + causal own block, selected with top_k = 0",
+                 "value": round(flop_local / (ms_local * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                 "ms_per_step": round(ms_local, 4), "flop_per_step": flop_local,
+                 "fwd_ms": split_ms(kt_local)[0], "bwd_ms": split_ms(kt_local)[1],
+                 "mixed_pair_ms": round(ms_local + topk["ms_per_step"], 4),
+                 "mixed_pair_note": "one local layer + one top-K layer (alternating policies), per pair",
+                 "step_stats": stats.get("local256k")}
+
     host1m = None if args.no_host1m else bench_host1m(args, pkv, synth, dev, t16)
 
     cpu = None
@@ -397,6 +418,7 @@ def main():
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "step_stats": stats.get("dense256k"),
         "cpu_baseline": cpu,
         "topk256k": topk,
+        "local256k": local,
         "host1m": host1m,
     }
     print(json.dumps(out), flush=True)

@@ -149,7 +149,8 @@ int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, 
  *   dense (sel_dev == NULL): every key at position <= q0 + t, i.e. logical pages [0, n_prior)
  *                            plus the chunk's own block;
  *   sparse: the pages sel_dev[g*n_sel + i], i < n_sel (ascending logical ids < n_prior), plus
- *           the own block, causally.
+ *           the own block, causally. A selection of no page (n_sel == 0: the own block only)
+ *           still passes a non-NULL sel_dev, which is then not read.
  * with softmax(scale * q.k). The own block (logical pages [n_prior, n_prior + C/page_size)) must
  * already be appended. Only KV heads [kvh0, kvh0 + n_kvh) and their query heads are computed.
  * Outputs: o_dev [C][H_q][head_dim] bf16 and lse_dev [H_q][C] fp32 for those heads.

@@ -96,6 +96,14 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _sel_ptr(sel: Optional[torch.Tensor], other: torch.Tensor):
+    """Selection pointer: NULL means dense, so an empty selection (no prior page) passes another
+    valid device pointer instead; with n_sel = 0 it is never read."""
+    if sel is None:
+        return None
+    return ctypes.c_void_p(sel.data_ptr() if sel.numel() > 0 else other.data_ptr())
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -212,7 +220,7 @@ def chunk_attn_fwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
         lse = torch.empty((H_q, C), dtype=torch.float32, device=q.device)
     nb = lib.chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
     ws = _ws(nb, q.device, ws)
-    _check(lib.chunk_attn_fwd(pool.handle, _ptr(bt), bt.numel(), n_prior, _ptr(sel), max(n_sel, 0), kvh0, n_kvh,
+    _check(lib.chunk_attn_fwd(pool.handle, _ptr(bt), bt.numel(), n_prior, _sel_ptr(sel, bt), max(n_sel, 0), kvh0, n_kvh,
                               _ptr(q), C, H_q, float(scale), _ptr(o), _ptr(lse), _ptr(ws), nb, _stream(stream)))
     return o, lse
 
@@ -240,7 +248,7 @@ def chunk_attn_bwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
     nb = lib.chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
     ws = _ws(nb, q.device, ws)
     _check(lib.chunk_attn_bwd(pool.handle, _ptr(bt), bt.numel(), gpool.handle, _ptr(gbt), gbt.numel(), n_prior,
-                              _ptr(sel), max(n_sel, 0), kvh0, n_kvh, _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), C,
+                              _sel_ptr(sel, bt), max(n_sel, 0), kvh0, n_kvh, _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), C,
                               H_q, float(scale), _ptr(dq), _ptr(ws), nb, _stream(stream)))
     return dq
 

@@ -109,6 +109,18 @@ def test_selection_rule_hand_example():
     assert oracle.n_selected(0, 64, 4) == 0
 
 
+def test_local_only_selection():
+    """top_k = 0 keeps exactly the n_local most recent prior pages whatever the scores (local
+    sliding-window layers); n_local = 0 as well leaves no prior page (own block only)."""
+    rng = np.random.default_rng(9)
+    s = rng.standard_normal((2, 10)).astype(np.float32)
+    assert oracle.select_pages(s, 12, 0, 2).tolist() == [[10, 11], [10, 11]]
+    assert oracle.n_selected(12, 0, 2) == 2
+    assert oracle.select_pages(s, 10, 0, 0).shape == (2, 0)
+    assert oracle.n_selected(10, 0, 0) == 0
+    assert oracle.select_pages(np.zeros((2, 0), np.float32), 1, 0, 3).tolist() == [[0], [0]]
+
+
 def test_selection_all_when_k_covers_candidates_and_nesting():
     rng = np.random.default_rng(5)
     s = rng.standard_normal((3, 40)).astype(np.float32)

@@ -181,6 +181,54 @@ def bench_host1m(args, pkv, synth, dev, t16):
             "h2d_pinned_memcpy_GBps": round(h2d_bytes / (ms_memcpy * 1e-3) / 1e9, 2)}
 
 
+def bench_recurrent(args, pkv, dev):
+    """Chunk-recurrent training of one attention layer with Qwen2.5-7B attention shapes (d_model
+    3584, 28/4 heads, d=128, 4096-token chunks), float32 projections, dense attention: step time,
+    the library kernels' share, and peak torch memory beyond the inputs at two context lengths
+    (it stays flat: only the paged cache, allocated by the library, grows with the context)."""
+    import torch
+    from paged_kv_cache_fwd_amd.recurrent import ChunkRecurrentAttention
+
+    out = {}
+    for n_chunks in (4, 8):
+        C, dm = 4096, 3584
+        layer = ChunkRecurrentAttention(dm, 28, 4, 128, 128, C, C * n_chunks, seed=0)
+        g = torch.Generator().manual_seed(7)
+        xs = [torch.randn(C, dm, generator=g).to(dev) for _ in range(n_chunks)]
+        rs = [torch.randn(C, dm, generator=g).to(dev) / 64.0 for _ in range(n_chunks)]
+
+        def loss_fn(y, i):
+            return (y * rs[i]).sum()
+
+        layer.train_step(xs, loss_fn)  # warm-up
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        pkv.timing_enable(True)
+        t0 = time.perf_counter()
+        layer.train_step(xs, loss_fn)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3
+        pkv.timing_enable(False)
+        kt = pkv.timing_collect()
+        # Beyond the inputs (and the returned dx, one input-sized tensor per chunk).
+        peak = torch.cuda.max_memory_allocated() - base - n_chunks * C * dm * 4
+        lib_ms = sum(v[1] for v in kt.values())
+        pool_bytes = layer.n_pages * 4 * 2 * 128 * 128 * (2 + 4)
+        ctx = C * n_chunks
+        log(f"[bench] recurrent {ctx // 1024}K: {ms:.1f} ms/step, library kernels {lib_ms:.1f} ms, "
+            f"peak torch memory beyond inputs and dx {peak / 2**20:.0f} MiB, pool {pool_bytes / 2**20:.0f} MiB")
+        out[f"{ctx // 1024}k"] = {"ms_per_step": round(ms, 2), "tokens_per_s": round(ctx / (ms * 1e-3), 1),
+                                  "library_kernel_ms": round(lib_ms, 2),
+                                  "peak_torch_bytes_beyond_inputs_and_dx": int(peak), "pool_bytes": pool_bytes}
+        layer.free()
+        del xs, rs, layer
+        torch.cuda.empty_cache()
+    out["note"] = ("one attention layer (Qwen2.5-7B shapes), forward over 4096-token chunks then reverse "
+                   "backward with recomputation; float32 projections via torch, attention in the library")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +238,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--no-host1m", action="store_true", help="skip the 1M-token host-tier workload")
+    ap.add_argument("--no-recurrent", action="store_true", help="skip the chunk-recurrent layer driver")
     ap.add_argument("--only", choices=("topk", "host1m"),
                     help="time only this workload (for per-workload profiles; prints no headline value)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -397,6 +446,7 @@ def main():
                  "step_stats": stats.get("local256k")}
 
     host1m = None if args.no_host1m else bench_host1m(args, pkv, synth, dev, t16)
+    recurrent = None if args.no_recurrent else bench_recurrent(args, pkv, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -420,6 +470,7 @@ def main():
         "topk256k": topk,
         "local256k": local,
         "host1m": host1m,
+        "recurrent_layer": recurrent,
     }
     print(json.dumps(out), flush=True)
 

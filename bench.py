@@ -168,8 +168,26 @@ def bench_host1m(args, pkv, synth, dev, t16):
     h2d_bytes = H_kv * step.n_sel * 2 * P * d * 2
     pairs = pairs_sparse(C, step.n_sel, P)
     flop = 14.0 * d * H_q * pairs
+    n_sel_1m = step.n_sel
     step.free()
     hpool.free()
+
+    # The same steps with the gradient pages in pinned host memory too: each head's backward
+    # accumulates into device slots that the side stream adds to the host pages.
+    log("[bench] host1m: refilling with gradient pages in host memory")
+    hpool = pkv.Pool(wl.n_pages, P, H_kv, d, grads=True, host_tier=True, host_grads=True)
+    for p0 in range(0, n_prior, 512):
+        n = min(512, n_prior - p0)
+        k, v = synth.kv_tokens(wl, p0, n)
+        hpool.append(hbt, p0 * P, t16(k), t16(v))
+    step = HostTierStep(hpool, hbt, n_prior, C, H_q, wl.top_k, wl.n_local, dev)
+    ms_host_grads = timed(True)
+    hpool.check()
+    step.dev.check()
+    step.free()
+    hpool.free()
+    offload_bytes = (H_kv * n_sel_1m + H_kv * (C // P)) * 2 * P * d * 4  # fp32 dK+dV blocks, read and written
+    log(f"[bench] host1m: {ms_host_grads:.3f} ms/step with gradient pages in host memory")
     log(f"[bench] host1m: {ms_host:.3f} ms/step with gathers, {ms_res:.3f} ms resident, gathers alone {ms_gather:.3f} ms")
     return {"workload": "host1m: 1M tokens, 8160 prior pages in pinned host memory, top-128 + 8 local per KV head, "
                         "per-head H2D gathers overlapped with the previous head's fwd+bwd",
@@ -178,7 +196,11 @@ def bench_host1m(args, pkv, synth, dev, t16):
             "overlap_overhead": round(ms_host / ms_res - 1.0, 4),
             "h2d_bytes_per_step": h2d_bytes, "h2d_gather_ms": round(ms_gather, 4),
             "h2d_GBps": round(h2d_bytes / (ms_gather * 1e-3) / 1e9, 2),
-            "h2d_pinned_memcpy_GBps": round(h2d_bytes / (ms_memcpy * 1e-3) / 1e9, 2)}
+            "h2d_pinned_memcpy_GBps": round(h2d_bytes / (ms_memcpy * 1e-3) / 1e9, 2),
+            "ms_per_step_host_grads": round(ms_host_grads, 4),
+            "host_grads_overhead": round(ms_host_grads / ms_host - 1.0, 4),
+            "host_grads_overhead_vs_resident": round(ms_host_grads / ms_res - 1.0, 4),
+            "grad_offload_bytes_per_step": offload_bytes}
 
 
 def bench_recurrent(args, pkv, dev):

@@ -52,6 +52,7 @@ extern "C" {
 
 #define PKV_GRADS 1u      /* allocate fp32 gradient pages (zero-initialised) on the device */
 #define PKV_HOST_TIER 2u  /* keep the bf16 KV pages in pinned, device-mapped host memory */
+#define PKV_HOST_GRADS 4u /* with PKV_GRADS: keep the fp32 gradient pages in pinned host memory */
 
 /* paged_kv_export / paged_kv_import selectors */
 #define PKV_K 0
@@ -73,11 +74,30 @@ const char* pkv_last_error(void);
  * Paged KV cache with gradients kept in pages too: pt 2.B, es 2.B ("paged memory manager"), it 2.B.
  * flags: PKV_GRADS adds fp32 gradient pages (zeroed); PKV_HOST_TIER places the KV pages in pinned
  * host memory that kernels read over the host link (pt 2.D, es 2.B "asynchronous CPU offloading",
- * it 2.C); gradients and representatives of such a pool stay on the device.
+ * it 2.C); gradients and representatives of such a pool stay on the device unless PKV_HOST_GRADS
+ * (with PKV_GRADS) places the gradient pages in pinned, device-mapped host memory too (pt 2.D: the
+ * gradients of the KV cache move to CPU memory as well). Backward passes never accumulate into
+ * host gradient pages directly: they accumulate into a device pool's pages, which
+ * paged_kv_grad_offload then adds to the host pages.
  * The pool owns all its memory; paged_kv_free releases it.
  */
 int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n_kv_heads,
                    int32_t head_dim, uint32_t flags);
+
+/*
+ * Gradient offload for a host tier (pt 2.D / es 2.B "asynchronous CPU offloading": the KV cache
+ * and its gradients move between GPU and CPU memory on dedicated streams). For each of the n
+ * logical pages lp = lp_dev[i] and KV heads g in [kvh0, kvh0 + n_kvh):
+ *   host grad[host_bt[lp]][g] += dev grad[dev_bt[lp]][g]   (dK and dV blocks, fp32)
+ *   dev grad[dev_bt[lp]][g] = 0                           (the device page is ready for reuse)
+ * host must have PKV_GRADS | PKV_HOST_GRADS, dev PKV_GRADS without PKV_HOST_GRADS. The host pages are
+ * read and written over the host link by the kernel; lp_dev lists distinct pages. Calls that
+ * touch the same host page must not overlap (order them on one stream). Out-of-range table
+ * entries are skipped and recorded (paged_kv_check on either pool).
+ */
+int paged_kv_grad_offload(pkv_pool* host, const int32_t* host_bt_dev, int32_t n_host_bt, pkv_pool* dev,
+                          const int32_t* dev_bt_dev, int32_t n_dev_bt, const int32_t* lp_dev, int32_t n,
+                          int32_t kvh0, int32_t n_kvh, void* stream);
 
 /* Synchronise the device and release the pool. NULL is a no-op returning PKV_OK. */
 int paged_kv_free(pkv_pool* pool);

@@ -17,14 +17,15 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK, PKV_E_INVALID, PKV_E_UNSUPPORTED, PKV_E_NOMEM, PKV_E_RANGE, PKV_E_HIP, PKV_E_STATE, PKV_E_DEVICE = \
     0, -1, -2, -3, -4, -5, -6, -7
-PKV_GRADS, PKV_HOST_TIER = 1, 2
+PKV_GRADS, PKV_HOST_TIER, PKV_HOST_GRADS = 1, 2, 4
 PKV_K, PKV_V, PKV_DK, PKV_DV, PKV_REP = 0, 1, 2, 3, 4
 
 EXPORTED = (
     "pkv_version", "pkv_last_error", "paged_kv_alloc", "paged_kv_free", "paged_kv_info", "paged_kv_data",
     "paged_kv_append", "paged_kv_zero_grad", "paged_kv_export", "paged_kv_check", "page_topk_ws_bytes",
     "page_topk_select", "chunk_attn_fwd_ws_bytes", "chunk_attn_fwd", "chunk_attn_bwd_ws_bytes",
-    "chunk_attn_bwd", "paged_kv_gather", "pkv_timing_enable", "pkv_timing_collect", "pkv_timing_get",
+    "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "pkv_timing_enable", "pkv_timing_collect",
+    "pkv_timing_get",
 )
 
 
@@ -73,6 +74,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "chunk_attn_bwd": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _S,
                                 _P]),
         "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P]),
+        "paged_kv_grad_offload": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _P]),
         "pkv_timing_enable": (_I, [ctypes.c_int]),
         "pkv_timing_collect": (ctypes.c_int, []),
         "pkv_timing_get": (_I, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I),
@@ -119,14 +121,14 @@ class Pool:
     """A paged KV pool (pages of K|V in bf16, optional fp32 gradient pages, fp32 page reps)."""
 
     def __init__(self, n_pages: int, page_size: int, n_kv_heads: int, head_dim: int, grads: bool = True,
-                 host_tier: bool = False):
+                 host_tier: bool = False, host_grads: bool = False):
         lib = load()
         h = ctypes.c_void_p()
-        flags = (PKV_GRADS if grads else 0) | (PKV_HOST_TIER if host_tier else 0)
+        flags = (PKV_GRADS if grads else 0) | (PKV_HOST_TIER if host_tier else 0) | (PKV_HOST_GRADS if host_grads else 0)
         _check(lib.paged_kv_alloc(ctypes.byref(h), n_pages, page_size, n_kv_heads, head_dim, flags))
         self.handle = h
         self.n_pages, self.page, self.h_kv, self.d = n_pages, page_size, n_kv_heads, head_dim
-        self.grads, self.host_tier = grads, host_tier
+        self.grads, self.host_tier, self.host_grads = grads, host_tier, host_grads
 
     def free(self):
         if self.handle:
@@ -266,6 +268,18 @@ def paged_kv_gather(host: Pool, dev: Pool, host_bt: torch.Tensor, sel_row: torch
     _check(load().paged_kv_gather(host.handle, dev.handle, _ptr(host_bt), host_bt.numel(), _ptr(sel_row),
                                   sel_row.numel(), kvh, _ptr(dst_pages), _ptr(dev_bt_out),
                                   0 if dev_bt_out is None else dev_bt_out.numel(), _stream(stream)))
+
+
+def paged_kv_grad_offload(host: Pool, host_bt: torch.Tensor, dev: Pool, dev_bt: torch.Tensor, lps: torch.Tensor,
+                          kvh0: int = 0, n_kvh: Optional[int] = None, stream=None):
+    """host grad[host_bt[lp]][g] += dev grad[dev_bt[lp]][g] and the device block is cleared, for the
+    logical pages lps (int32, distinct) and KV heads [kvh0, kvh0 + n_kvh)."""
+    _need(host_bt, torch.int32, "host_bt")
+    _need(dev_bt, torch.int32, "dev_bt")
+    _need(lps, torch.int32, "lps")
+    n_kvh = host.h_kv - kvh0 if n_kvh is None else n_kvh
+    _check(load().paged_kv_grad_offload(host.handle, _ptr(host_bt), host_bt.numel(), dev.handle, _ptr(dev_bt),
+                                        dev_bt.numel(), _ptr(lps), lps.numel(), kvh0, n_kvh, _stream(stream)))
 
 
 def timing_enable(on: bool = True):

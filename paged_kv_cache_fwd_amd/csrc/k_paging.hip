@@ -169,6 +169,51 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather(const uint16_t* __res
   }
 }
 
+// Gradient offload: host[host_bt[lp]][g] += dev[dev_bt[lp]][g], then the device block is cleared.
+// Workgroups stride over the (page, head) blocks; each fp32 block is 2*P*D floats. The host block
+// is read and written over the host link (device-mapped pinned memory), 8 x 16 bytes in flight
+// per thread.
+constexpr int kOffloadBlocks = 32;
+__global__ __launch_bounds__(256) void k_grad_offload(float* __restrict__ host_grad, int32_t n_host_pool,
+                                                      float* __restrict__ dev_grad, int32_t n_dev_pool, int32_t P,
+                                                      int32_t H, int32_t D, const int32_t* __restrict__ host_bt,
+                                                      int32_t n_host_bt, const int32_t* __restrict__ dev_bt,
+                                                      int32_t n_dev_bt, const int32_t* __restrict__ lps, int32_t n,
+                                                      int32_t kvh0, int32_t n_kvh, int32_t* host_err,
+                                                      int32_t* dev_err) {
+  const int64_t n_blocks = (int64_t)n * n_kvh;
+  const int64_t n16 = (int64_t)2 * P * D / 4;  // 16-byte chunks per (page, head) block
+  for (int64_t bi = blockIdx.x; bi < n_blocks; bi += gridDim.x) {
+    const int32_t lp = lps[bi / n_kvh];
+    const int32_t g = kvh0 + (int32_t)(bi % n_kvh);
+    const int32_t hp = phys_page(host_bt, n_host_bt, n_host_pool, lp, host_err);
+    const int32_t dp = phys_page(dev_bt, n_dev_bt, n_dev_pool, lp, dev_err);
+    if (hp < 0 || dp < 0) continue;
+    f32x4* hb = reinterpret_cast<f32x4*>(host_grad + ((int64_t)hp * H + g) * 2 * P * D);
+    f32x4* db = reinterpret_cast<f32x4*>(dev_grad + ((int64_t)dp * H + g) * 2 * P * D);
+    constexpr int kUnroll = 8;
+    for (int64_t c0 = threadIdx.x; c0 < n16; c0 += 256 * kUnroll) {
+      f32x4 hv[kUnroll], dv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = c0 + (int64_t)u * 256;
+        if (c < n16) {
+          hv[u] = __builtin_nontemporal_load(hb + c);
+          dv[u] = db[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = c0 + (int64_t)u * 256;
+        if (c < n16) {
+          hb[c] = hv[u] + dv[u];
+          db[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+}
+
 static inline unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t pos0, int32_t n,
@@ -255,6 +300,20 @@ hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_
     hipLaunchKernelGGL(k_gather, dim3(n_sel < kGatherBlocks ? n_sel : kGatherBlocks), dim3(kGatherThreads), 0, s, host.kv,
                        host.n_pages, dev.kv, dev.n_pages, host.page, host.h_kv, host.d, host_bt, n_host_bt, sel, n_sel,
                        dst_pages, kvh, dev_bt_out, n_dev_bt, dev.err);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_offload(const pkv_pool& host, const int32_t* host_bt, int32_t n_host_bt, const pkv_pool& dev,
+                               const int32_t* dev_bt, int32_t n_dev_bt, const int32_t* lp, int32_t n, int32_t kvh0,
+                               int32_t n_kvh, hipStream_t s) {
+  const int64_t n_blocks = (int64_t)n * n_kvh;
+  if (n_blocks == 0) return hipSuccess;
+  {
+    TimerScope ts_("k_grad_offload", s);
+    hipLaunchKernelGGL(k_grad_offload, dim3((unsigned)(n_blocks < kOffloadBlocks ? n_blocks : kOffloadBlocks)),
+                       dim3(256), 0, s, host.grad, host.n_pages, dev.grad, dev.n_pages, host.page, host.h_kv, host.d,
+                       host_bt, n_host_bt, dev_bt, n_dev_bt, lp, n, kvh0, n_kvh, host.err, dev.err);
   }
   return hipGetLastError();
 }

@@ -248,7 +248,8 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
   if (!supported(page_size, head_dim))
     return fail(PKV_E_UNSUPPORTED, "page_size %d / head_dim %d not supported (both must be 64 or 128)", page_size,
                 head_dim);
-  if (flags & ~(PKV_GRADS | PKV_HOST_TIER)) return fail(PKV_E_INVALID, "unknown flags 0x%x", flags);
+  if (flags & ~(PKV_GRADS | PKV_HOST_TIER | PKV_HOST_GRADS)) return fail(PKV_E_INVALID, "unknown flags 0x%x", flags);
+  if ((flags & PKV_HOST_GRADS) && !(flags & PKV_GRADS)) return fail(PKV_E_INVALID, "PKV_HOST_GRADS needs PKV_GRADS");
   pkv_pool* p = new (std::nothrow) pkv_pool();
   if (!p) return fail(PKV_E_NOMEM, "out of host memory");
   p->n_pages = n_pages;
@@ -259,6 +260,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
   p->kv = nullptr;
   p->kv_host = nullptr;
   p->grad = nullptr;
+  p->grad_host = nullptr;
   p->rep = nullptr;
   p->err = nullptr;
   hipError_t e = hipGetDevice(&p->device);
@@ -269,7 +271,8 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
   auto cleanup = [&]() {
     if (p->kv_host) (void)hipHostFree(p->kv_host);
     else if (p->kv) (void)hipFree(p->kv);
-    if (p->grad) (void)hipFree(p->grad);
+    if (p->grad_host) (void)hipHostFree(p->grad_host);
+    else if (p->grad) (void)hipFree(p->grad);
     if (p->rep) (void)hipFree(p->rep);
     if (p->err) (void)hipFree(p->err);
     delete p;
@@ -308,7 +311,24 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
       return hip_fail(e, "hipMemset(kv)");
     }
   }
-  if (flags & PKV_GRADS) {
+  if (flags & PKV_HOST_GRADS) {
+    e = hipHostMalloc(&p->grad_host, grad_bytes(*p), hipHostMallocMapped | hipHostMallocPortable);
+    if (e != hipSuccess) {
+      p->grad_host = nullptr;
+      (void)hipGetLastError();
+      cleanup();
+      return fail(PKV_E_NOMEM, "hipHostMalloc(%zu bytes) for gradient pages: %s", grad_bytes(*p),
+                  hipGetErrorString(e));
+    }
+    void* gptr = nullptr;
+    e = hipHostGetDevicePointer(&gptr, p->grad_host, 0);
+    if (e != hipSuccess) {
+      cleanup();
+      return hip_fail(e, "hipHostGetDevicePointer(grad)");
+    }
+    p->grad = (float*)gptr;
+    memset(p->grad_host, 0, grad_bytes(*p));
+  } else if (flags & PKV_GRADS) {
     e = hipMalloc((void**)&p->grad, grad_bytes(*p));
     if (e != hipSuccess) {
       p->grad = nullptr;
@@ -345,7 +365,8 @@ int paged_kv_free(pkv_pool* pool) {
   hipError_t e = hipDeviceSynchronize();
   if (pool->kv_host) (void)hipHostFree(pool->kv_host);
   else if (pool->kv) (void)hipFree(pool->kv);
-  if (pool->grad) (void)hipFree(pool->grad);
+  if (pool->grad_host) (void)hipHostFree(pool->grad_host);
+  else if (pool->grad) (void)hipFree(pool->grad);
   if (pool->rep) (void)hipFree(pool->rep);
   if (pool->err) (void)hipFree(pool->err);
   delete pool;
@@ -540,6 +561,8 @@ int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, pk
   if (rc != PKV_OK) return rc;
   if (!gpool) return fail(PKV_E_INVALID, "gradient pool is NULL");
   if (!gpool->grad) return fail(PKV_E_STATE, "gradient pool has no gradient pages");
+  if (gpool->flags & PKV_HOST_GRADS)
+    return fail(PKV_E_STATE, "gradient pages in host memory: accumulate into a device pool, then paged_kv_grad_offload");
   if (gpool->page != pool->page || gpool->h_kv != pool->h_kv || gpool->d != pool->d)
     return fail(PKV_E_INVALID, "gradient pool shape differs from the KV pool");
   if (!gbt_dev) return fail(PKV_E_INVALID, "gradient block table is NULL");
@@ -583,6 +606,25 @@ int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_
   hipError_t e = pkv::launch_gather(*host, *dev, host_bt_dev, n_host_bt, sel_dev, n_sel, kvh, dst_pages_dev,
                                     dev_bt_out_dev, n_dev_bt, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_grad_offload(pkv_pool* host, const int32_t* host_bt_dev, int32_t n_host_bt, pkv_pool* dev,
+                          const int32_t* dev_bt_dev, int32_t n_dev_bt, const int32_t* lp_dev, int32_t n,
+                          int32_t kvh0, int32_t n_kvh, void* stream) {
+  if (!host || !dev) return fail(PKV_E_INVALID, "NULL pool");
+  if (!(host->flags & PKV_HOST_GRADS)) return fail(PKV_E_STATE, "destination pool has no host gradient pages");
+  if (!dev->grad || (dev->flags & PKV_HOST_GRADS)) return fail(PKV_E_STATE, "source pool needs device gradient pages");
+  if (host->page != dev->page || host->h_kv != dev->h_kv || host->d != dev->d)
+    return fail(PKV_E_INVALID, "pool shapes differ");
+  if (kvh0 < 0 || n_kvh <= 0 || kvh0 + n_kvh > host->h_kv)
+    return fail(PKV_E_INVALID, "KV head range [%d, %d) outside [0, %d)", kvh0, kvh0 + n_kvh, host->h_kv);
+  if (n < 0 || n_host_bt < 0 || n_dev_bt < 0) return fail(PKV_E_INVALID, "negative count");
+  if (n > 0 && (!host_bt_dev || !dev_bt_dev || !lp_dev)) return fail(PKV_E_INVALID, "NULL table");
+  hipError_t e = pkv::launch_grad_offload(*host, host_bt_dev, n_host_bt, *dev, dev_bt_dev, n_dev_bt, lp_dev, n, kvh0,
+                                          n_kvh, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gradient offload launch");
   ok();
   return PKV_OK;
 }

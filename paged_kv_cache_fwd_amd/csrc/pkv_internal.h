@@ -14,7 +14,8 @@ struct pkv_pool {
   int device;
   uint16_t* kv;       // device address of the bf16 KV pages (device-mapped pinned host for host tier)
   void* kv_host;      // host allocation of a host-tier pool (NULL otherwise)
-  float* grad;        // fp32 gradient pages (NULL without PKV_GRADS)
+  float* grad;        // fp32 gradient pages (NULL without PKV_GRADS; device-mapped host for PKV_HOST_GRADS)
+  void* grad_host;    // host allocation of PKV_HOST_GRADS gradient pages (NULL otherwise)
   float* rep;         // fp32 representative key per (page, head)
   int32_t* err;       // device word: nonzero once a kernel met an out-of-range table entry
 };
@@ -94,6 +95,9 @@ hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, 
 hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
                          const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages,
                          int32_t* dev_bt_out, int32_t n_dev_bt, hipStream_t s);
+hipError_t launch_grad_offload(const pkv_pool& host, const int32_t* host_bt, int32_t n_host_bt, const pkv_pool& dev,
+                               const int32_t* dev_bt, int32_t n_dev_bt, const int32_t* lp, int32_t n, int32_t kvh0,
+                               int32_t n_kvh, hipStream_t s);
 size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d);
 hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const uint16_t* q,
                        int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t* sel, void* ws,

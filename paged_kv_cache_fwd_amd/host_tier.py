@@ -8,7 +8,9 @@ Per chunk: page_topk_select on the host-tier pool (its representatives are on th
 each KV head g a side stream gathers g's selected (page, head) blocks into g's device slots
 (paged_kv_gather also writes g's device block table) while the compute stream runs forward and
 backward of head g-1. Gradients go to the host-tier pool's device-resident gradient pages through
-its own block table. Every computation is a library kernel; this module only orders them.
+its own block table, or, when the host pool keeps its gradient pages in host memory, into device
+slots that the side stream then adds to the host pages (pt 2.D: the gradients of the KV cache
+move to CPU memory too). Every computation is a library kernel; this module only orders them.
 """
 from __future__ import annotations
 
@@ -17,7 +19,7 @@ from typing import List, Optional
 import torch
 
 from . import (Pool, chunk_attn_bwd, chunk_attn_bwd_ws_bytes, chunk_attn_fwd, chunk_attn_fwd_ws_bytes, load,
-               page_topk_select, paged_kv_gather)
+               page_topk_select, paged_kv_gather, paged_kv_grad_offload)
 
 
 class HostTierStep:
@@ -34,8 +36,10 @@ class HostTierStep:
         n_cand = max(n_prior - n_local, 0)
         self.n_sel = min(top_k, n_cand) + (n_prior - n_cand)
         n_dev = self.n_own + H * self.n_sel
-        # Device pool: the chunk's own pages first, then n_sel slots per KV head.
-        self.dev = Pool(n_dev, P, H, host.d, grads=False)
+        # Device pool: the chunk's own pages first, then n_sel slots per KV head. With gradient pages
+        # in host memory the device pool carries gradient slots that the backward accumulates into.
+        self.host_grads = host.host_grads
+        self.dev = Pool(n_dev, P, H, host.d, grads=self.host_grads)
         n_bt = host_bt.numel()
         base = torch.zeros(n_bt, dtype=torch.int32, device=device)
         base[n_prior:n_prior + self.n_own] = torch.arange(self.n_own, dtype=torch.int32, device=device)
@@ -44,6 +48,7 @@ class HostTierStep:
         self.slots = [torch.arange(self.n_own + g * self.n_sel, self.n_own + (g + 1) * self.n_sel, dtype=torch.int32,
                                    device=device) for g in range(H)]
         self.sel = torch.empty((H, self.n_sel), dtype=torch.int32, device=device)
+        self.own_lps = torch.arange(n_prior, n_prior + self.n_own, dtype=torch.int32, device=device)
         lib = load()
         self.ws_t = torch.empty(max(lib.page_topk_ws_bytes(host.handle, n_prior, C, H_q), 1), dtype=torch.uint8,
                                 device=device)
@@ -54,7 +59,11 @@ class HostTierStep:
         self.side = torch.cuda.Stream(device=device)
         self.ready = [torch.cuda.Event() for _ in range(H)]
         self.done = [torch.cuda.Event() for _ in range(H)]
-        for ev in self.done:
+        # Gradient offloads run on a stream of their own, so the next step's gathers need not queue
+        # behind them; the next backward of head g waits for its offload (own pages: head 0's).
+        self.off = torch.cuda.Stream(device=device) if self.host_grads else None
+        self.off_done = [torch.cuda.Event() for _ in range(H)]
+        for ev in self.done + self.off_done:
             ev.record(torch.cuda.current_stream(device))
 
     def append_own(self, k: torch.Tensor, v: torch.Tensor):
@@ -64,7 +73,13 @@ class HostTierStep:
     def run(self, q: torch.Tensor, dout: torch.Tensor, scale: float, o: torch.Tensor, lse: torch.Tensor,
             dq: torch.Tensor, gather: bool = True):
         """One sparse step. With gather=False the slots are assumed filled already (for timing the
-        same selection without host traffic)."""
+        same selection without host traffic; not with gradient pages in host memory).
+
+        Gradient pages in host memory: head g's backward accumulates into its device slots, and an
+        offload stream then adds them to the host pages and clears them (paged_kv_grad_offload), the
+        chunk's own pages after the last head. The next step's backward of head g waits for that
+        offload, so a slot is cleared before it is reused."""
+        assert gather or not self.host_grads
         compute = torch.cuda.current_stream(q.device)
         sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local, sel=self.sel,
                                ws=self.ws_t)
@@ -92,9 +107,25 @@ class HostTierStep:
                 compute.wait_event(self.ready[g])
             chunk_attn_fwd(self.dev, self.bt[g], self.n_prior, q, scale, sel=sel, kvh0=g, n_kvh=1, o=o, lse=lse,
                            ws=self.ws_f)
-            chunk_attn_bwd(self.dev, self.bt[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
-                           gpool=self.host, gbt=self.host_bt, dq=dq, ws=self.ws_b)
+            if self.host_grads:
+                compute.wait_event(self.off_done[g])  # the previous step's offload of these slots
+                if g == 0:
+                    compute.wait_event(self.off_done[H - 1])  # and of the own pages (after head H-1)
+                chunk_attn_bwd(self.dev, self.bt[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
+                               gpool=self.dev, gbt=self.bt[g], dq=dq, ws=self.ws_b)
+            else:
+                chunk_attn_bwd(self.dev, self.bt[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
+                               gpool=self.host, gbt=self.host_bt, dq=dq, ws=self.ws_b)
             self.done[g].record(compute)
+            if self.host_grads:
+                with torch.cuda.stream(self.off):
+                    self.off.wait_event(self.done[g])
+                    paged_kv_grad_offload(self.host, self.host_bt, self.dev, self.bt[g], sel[g], kvh0=g, n_kvh=1,
+                                          stream=self.off)
+                    if g == H - 1:  # every head's backward has added to the own pages
+                        paged_kv_grad_offload(self.host, self.host_bt, self.dev, self.own_bt, self.own_lps,
+                                              stream=self.off)
+                    self.off_done[g].record(self.off)
         return sel
 
     def free(self):

@@ -51,9 +51,11 @@ def compare(name, got, want, atol, rel=REL_FRO, nondegenerate=True):
         assert np.linalg.norm(got) >= 0.5 * nw, f"{name}: output norm collapsed"
 
 
-def fill_pool(pkv, wl, n_pages, bt_np, grads=True, host_tier=False, pool_pages=None, chunk_tokens=65536):
+def fill_pool(pkv, wl, n_pages, bt_np, grads=True, host_tier=False, pool_pages=None, chunk_tokens=65536,
+              host_grads=False):
     """Create a pool holding logical pages [0, n_pages) of the workload, appended in pieces."""
-    pool = pkv.Pool(pool_pages or len(bt_np), wl.page, wl.h_kv, wl.d, grads=grads, host_tier=host_tier)
+    pool = pkv.Pool(pool_pages or len(bt_np), wl.page, wl.h_kv, wl.d, grads=grads, host_tier=host_tier,
+                    host_grads=host_grads)
     bt = i32(bt_np)
     per = max(chunk_tokens // wl.page, 1)
     for p0 in range(0, n_pages, per):

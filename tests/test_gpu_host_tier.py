@@ -76,6 +76,53 @@ def test_host_tier_small_full_parity(pkv):
     compare("O host tier vs resident", host(res["o"]), host(res["o_res"]), 1e-2, rel=1e-2)
 
 
+def test_host_grads_small_parity_and_accumulation(pkv):
+    """Gradient pages in host memory: after one step they hold the oracle's dK/dV (selected and own
+    pages, added from the device slots by paged_kv_grad_offload); a second identical step doubles
+    them; the device slots end cleared."""
+    from paged_kv_cache_fwd_amd.host_tier import HostTierStep
+    wl = synth.Workload("host-small", 14, 2, 128, 128, 128 * 24, 384, (7,), offset_std=0.5, seed=22)
+    c, top_k, n_local = 7, 6, 2
+    n_prior, C, P = wl.n_prior(c), wl.chunk, wl.page
+    say("host gradient pages: 24 pages, 21 prior, top-6 + 2 local, two steps")
+    bt_np = synth.page_permutation(wl)
+    hpool, hbt = fill_pool(pkv, wl, wl.n_pages, bt_np, host_tier=True, host_grads=True)
+    step = HostTierStep(hpool, hbt, n_prior, C, wl.h_q, top_k, n_local, torch.device("cuda:0"))
+    assert step.host_grads
+    k_own, v_own = synth.kv_tokens(wl, n_prior, C // P)
+    step.append_own(t16(k_own), t16(v_own))
+    q, do = t16(synth.q_chunk(wl, c)), t16(synth.do_chunk(wl, c))
+    o, dq = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((wl.h_q, C), dtype=torch.float32, device=q.device)
+    hpool.zero_grad()
+    sel = step.run(q, do, wl.scale, o, lse, dq)
+    torch.cuda.synchronize()
+    dk1 = hpool.export(pkv.PKV_DK, hbt, 0, wl.n_pages).cpu().numpy()
+    dv1 = hpool.export(pkv.PKV_DV, hbt, 0, wl.n_pages).cpu().numpy()
+    step.run(q, do, wl.scale, o, lse, dq)
+    torch.cuda.synchronize()
+    dk2 = hpool.export(pkv.PKV_DK, hbt, 0, wl.n_pages).cpu().numpy()
+    slots = step.dev.export(pkv.PKV_DK, torch.arange(step.dev.n_pages, dtype=torch.int32, device=q.device), 0,
+                            step.dev.n_pages).cpu().numpy()
+    hpool.check()
+    step.dev.check()
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    qn, don = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+    want, _, _ = oracle.topk_pages(qn, k[: n_prior * P], P, wl.h_kv, n_prior, top_k, n_local)
+    assert np.array_equal(sel.cpu().numpy(), want)
+    ref = oracle.chunk_backward(qn, k, v, don, wl.q0(c), wl.scale, sel=want, page=P)
+    for g in range(wl.h_kv):
+        keys = ref["keys"][g]
+        compare(f"host dK head {g}", dk1[keys, g], ref["dk"][g], ATOL_GRAD)
+        compare(f"host dV head {g}", dv1[keys, g], ref["dv"][g], ATOL_GRAD)
+        untouched = np.setdiff1d(np.arange(wl.context), keys)
+        assert not np.any(dk1[untouched, g]) and not np.any(dv1[untouched, g])
+    compare("second step doubles dK", dk2, 2.0 * dk1, 1e-5, rel=1e-5)
+    assert not np.any(slots)
+    step.free()
+    hpool.free()
+
+
 def test_host_tier_1m_matches_resident(pkv):
     """1M tokens: 8192 pages (8160 prior) in pinned host memory, top-128 + 8 local."""
     wl = synth.WORKLOADS["host1m"]

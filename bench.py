@@ -34,12 +34,12 @@ LOCAL_WINDOW = 1  # pages kept by a local (sliding-window) layer
 # WRITE_SIZE rocprofv3 pass each, scaled by what those counters read for a plain 1 GiB streaming
 # kernel (x2.0 fetch, x1.0 write). Valid only for the kernel sources they were taken on.
 TRAFFIC_SOURCES = ("paged_kv_cache_fwd_amd/csrc/k_attn_fwd.hip", "paged_kv_cache_fwd_amd/csrc/k_attn_bwd.hip",
-                   "paged_kv_cache_fwd_amd/csrc/pkv_device.h", "paged_kv_cache_fwd_amd/csrc/pkv_internal.h",
+                   "paged_kv_cache_fwd_amd/csrc/k_attn_dkdv.hip", "paged_kv_cache_fwd_amd/csrc/pkv_device.h", "paged_kv_cache_fwd_amd/csrc/pkv_internal.h",
                    "paged_kv_cache_fwd_amd/csrc/pkv_abi.cpp", "paged_kv_cache_fwd_amd/build.py")
-TRAFFIC_SHA = "269c14f84e2e5951"
-TRAFFIC_BYTES = {"k_attn_fwd": (2.0 * 3289759 * 1024, 231168 * 1024),
-                 "k_bwd_dq": (2.0 * 1242567 * 1024, 229376 * 1024),
-                 "k_bwd_dkdv": (2.0 * 1394619 * 1024, 1048576 * 1024)}
+TRAFFIC_SHA = "be304e1cd435a505"
+TRAFFIC_BYTES = {"k_attn_fwd": (2.0 * 3185396 * 1024, 231168 * 1024),
+                 "k_bwd_dq": (2.0 * 1179736 * 1024, 229376 * 1024),
+                 "k_bwd_dkdv": (2.0 * 1400368 * 1024, 1069056 * 1024)}
 
 
 def traffic_bytes(kernel):

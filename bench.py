@@ -203,6 +203,100 @@ def bench_host1m(args, pkv, synth, dev, t16):
             "grad_offload_bytes_per_step": offload_bytes}
 
 
+def bench_dense_host(args, pkv, synth, dev, t16):
+    """Dense 1M-token steps over two layers whose KV and gradient pages live in pinned host memory:
+    each step's forward+backward runs on one device pool while a copy engine loads the next layer's
+    pages into the other and another writes the finished layer's gradient pages home."""
+    import torch
+    from paged_kv_cache_fwd_amd.host_tier import DenseLayerPrefetch
+
+    wl = synth.WORKLOADS["host1m"]
+    c = wl.chunks[0]
+    C, P, H_q, H_kv, d = wl.chunk, wl.page, wl.h_q, wl.h_kv, wl.d
+    n_prior, N = wl.n_prior(c), wl.n_pages
+    log(f"[bench] dense1m-host: generating {N} pages (device-resident pool)")
+    res = pkv.Pool(N, P, H_kv, d, grads=True)
+    bt = torch.from_numpy(synth.page_permutation(wl)).to(dev)
+    for p0 in range(0, N, 512):
+        n = min(512, N - p0)
+        k, v = synth.kv_tokens(wl, p0, n)
+        res.append(bt, p0 * P, t16(k), t16(v))
+    log("[bench] dense1m-host: two layers of KV + gradient pages in pinned host memory")
+    hosts = [pkv.Pool(N, P, H_kv, d, grads=True, host_tier=True, host_grads=True) for _ in range(2)]
+    for h in hosts:
+        pkv.paged_kv_copy(res, h, pkv.PKV_COPY_KV)
+    q, do = t16(synth.q_chunk(wl, c)), t16(synth.do_chunk(wl, c))
+    o, dq = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((H_q, C), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(max(pkv.chunk_attn_fwd_ws_bytes(res, n_prior, -1, H_kv, C, H_q), 1), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(max(pkv.chunk_attn_bwd_ws_bytes(res, n_prior, -1, H_kv, C, H_q), 1), dtype=torch.uint8,
+                       device=dev)
+    n_steps = max(args.steps, 6)
+
+    def timed(step):
+        for i in range(2):
+            step(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(n_steps):
+            step(i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / n_steps * 1e3
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(n_steps))
+        return wall, per[len(per) // 2]
+
+    def step_res(i):
+        pkv.chunk_attn_fwd(res, bt, n_prior, q, wl.scale, o=o, lse=lse, ws=ws_f)
+        pkv.chunk_attn_bwd(res, bt, n_prior, q, o, do, lse, wl.scale, dq=dq, ws=ws_b)
+
+    log(f"[bench] dense1m-host: {n_steps} steps with all pages on the device")
+    wall_res, med_res = timed(step_res)
+    run = DenseLayerPrefetch(hosts, dev)
+
+    def step_host(i):
+        run.run(i % 2, (i + 1) % 2, bt, n_prior, q, do, wl.scale, o, lse, dq)
+
+    log(f"[bench] dense1m-host: {n_steps} steps alternating two host-resident layers")
+    wall_host, med_host = timed(step_host)
+    # Each direction alone, for the link's rate.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    pkv.paged_kv_copy(hosts[0], run.dev[0], pkv.PKV_COPY_KV | pkv.PKV_COPY_GRAD)
+    torch.cuda.synchronize()
+    ms_h2d = (time.perf_counter() - t0) * 1e3
+    t0 = time.perf_counter()
+    pkv.paged_kv_copy(run.dev[0], hosts[0], pkv.PKV_COPY_GRAD)
+    torch.cuda.synchronize()
+    ms_d2h = (time.perf_counter() - t0) * 1e3
+    for h in hosts:
+        h.check()
+    run.free()
+    for h in hosts:
+        h.free()
+    res.free()
+    kv_b, gr_b = N * H_kv * 2 * P * d * 2, N * H_kv * 2 * P * d * 4
+    flop = 14.0 * d * H_q * pairs_dense(C, wl.q0(c))
+    log(f"[bench] dense1m-host: {med_host:.2f} ms/step (wall {wall_host:.2f}) vs {med_res:.2f} resident "
+        f"(wall {wall_res:.2f}); H2D {ms_h2d:.1f} ms, D2H {ms_d2h:.1f} ms per layer alone")
+    return {"workload": "dense1m-host: final 4096-token chunk over 8160 prior pages + own block, 28/4 heads, d=128, "
+                        "dense; two layers whose KV and gradient pages live in pinned host memory, each step "
+                        "overlapping the next layer's page load and the finished layer's gradient write-back",
+            "value": round(flop / (med_host * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(med_host, 3), "ms_per_step_wall": round(wall_host, 3),
+            "ms_per_step_resident": round(med_res, 3), "ms_per_step_resident_wall": round(wall_res, 3),
+            "overhead": round(med_host / med_res - 1.0, 4), "overhead_wall": round(wall_host / wall_res - 1.0, 4),
+            "flop_per_step": flop, "steps": n_steps,
+            "h2d_bytes_per_step": kv_b + gr_b, "d2h_bytes_per_step": gr_b,
+            "h2d_alone_ms": round(ms_h2d, 2), "h2d_GBps": round((kv_b + gr_b) / (ms_h2d * 1e-3) / 1e9, 2),
+            "d2h_alone_ms": round(ms_d2h, 2), "d2h_GBps": round(gr_b / (ms_d2h * 1e-3) / 1e9, 2),
+            "note": "ms_per_step is the median interval between steps on the compute stream; the wall figure "
+                    "also counts draining the last write-back"}
+
+
 def bench_recurrent(args, pkv, dev):
     """Chunk-recurrent training of one attention layer with Qwen2.5-7B attention shapes (d_model
     3584, 28/4 heads, d=128, 4096-token chunks), float32 projections, dense attention: step time,
@@ -261,7 +355,9 @@ def main():
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--no-host1m", action="store_true", help="skip the 1M-token host-tier workload")
     ap.add_argument("--no-recurrent", action="store_true", help="skip the chunk-recurrent layer driver")
-    ap.add_argument("--only", choices=("topk", "host1m"),
+    ap.add_argument("--no-densehost", action="store_true",
+                    help="skip the dense 1M-token workload over host-resident layers")
+    ap.add_argument("--only", choices=("topk", "host1m", "densehost"),
                     help="time only this workload (for per-workload profiles; prints no headline value)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run one plain streaming kernel (torch.neg on fp32) over this many MiB, as the "
@@ -295,6 +391,9 @@ def main():
 
     if args.only == "host1m":
         print(json.dumps(bench_host1m(args, pkv, synth, dev, t16)), flush=True)
+        return
+    if args.only == "densehost":
+        print(json.dumps(bench_dense_host(args, pkv, synth, dev, t16)), flush=True)
         return
     wl = synth.WORKLOADS["dense256k"]
     wlk = synth.WORKLOADS["topk256k"]
@@ -468,6 +567,7 @@ def main():
                  "step_stats": stats.get("local256k")}
 
     host1m = None if args.no_host1m else bench_host1m(args, pkv, synth, dev, t16)
+    dense_host = None if args.no_densehost else bench_dense_host(args, pkv, synth, dev, t16)
     recurrent = None if args.no_recurrent else bench_recurrent(args, pkv, dev)
 
     cpu = None
@@ -492,6 +592,7 @@ def main():
         "topk256k": topk,
         "local256k": local,
         "host1m": host1m,
+        "dense1m_host": dense_host,
         "recurrent_layer": recurrent,
     }
     print(json.dumps(out), flush=True)

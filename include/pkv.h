@@ -54,6 +54,10 @@ extern "C" {
 #define PKV_HOST_TIER 2u  /* keep the bf16 KV pages in pinned, device-mapped host memory */
 #define PKV_HOST_GRADS 4u /* with PKV_GRADS: keep the fp32 gradient pages in pinned host memory */
 
+/* paged_kv_copy selectors (bit mask) */
+#define PKV_COPY_KV 1u   /* the bf16 KV pages */
+#define PKV_COPY_GRAD 2u /* the fp32 gradient pages */
+
 /* paged_kv_export / paged_kv_import selectors */
 #define PKV_K 0
 #define PKV_V 1
@@ -98,6 +102,23 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
 int paged_kv_grad_offload(pkv_pool* host, const int32_t* host_bt_dev, int32_t n_host_bt, pkv_pool* dev,
                           const int32_t* dev_bt_dev, int32_t n_dev_bt, const int32_t* lp_dev, int32_t n,
                           int32_t kvh0, int32_t n_kvh, void* stream);
+
+/*
+ * Bulk page copy between two pools of the same page size, heads and dim, for dense attention over a
+ * host tier (pt 2.D: with dense or local attention the next block is fetched while the current one
+ * is computed; es 2.B: transfers overlap the next layer's compute). Copies physical pages
+ * [first_page, first_page + n_pages) of src into the same physical pages of dst: the KV pages if
+ * what has PKV_COPY_KV, the gradient pages if it has PKV_COPY_GRAD (both pools need gradient pages
+ * then). Physical page numbers are kept, so one block table serves both pools. Either pool may live
+ * in host or device memory; each range is one contiguous hipMemcpyAsync on stream, which the
+ * runtime serves with its copy engines (no compute units). Nothing synchronises; src and dst must
+ * be different pools, and the caller orders the copy against kernels that touch either range.
+ * n_pages = 0 is a no-op. Errors: PKV_E_INVALID (NULL pool, same pool, shape mismatch, range
+ * outside either pool, unknown bits), PKV_E_STATE (PKV_COPY_GRAD on a pool without gradients),
+ * PKV_E_HIP (the copy could not be enqueued).
+ */
+int paged_kv_copy(const pkv_pool* src, pkv_pool* dst, uint32_t what, int32_t first_page, int32_t n_pages,
+                  void* stream);
 
 /* Synchronise the device and release the pool. NULL is a no-op returning PKV_OK. */
 int paged_kv_free(pkv_pool* pool);

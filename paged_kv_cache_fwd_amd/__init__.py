@@ -18,13 +18,14 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 PKV_OK, PKV_E_INVALID, PKV_E_UNSUPPORTED, PKV_E_NOMEM, PKV_E_RANGE, PKV_E_HIP, PKV_E_STATE, PKV_E_DEVICE = \
     0, -1, -2, -3, -4, -5, -6, -7
 PKV_GRADS, PKV_HOST_TIER, PKV_HOST_GRADS = 1, 2, 4
+PKV_COPY_KV, PKV_COPY_GRAD = 1, 2
 PKV_K, PKV_V, PKV_DK, PKV_DV, PKV_REP = 0, 1, 2, 3, 4
 
 EXPORTED = (
     "pkv_version", "pkv_last_error", "paged_kv_alloc", "paged_kv_free", "paged_kv_info", "paged_kv_data",
     "paged_kv_append", "paged_kv_zero_grad", "paged_kv_export", "paged_kv_check", "page_topk_ws_bytes",
     "page_topk_select", "chunk_attn_fwd_ws_bytes", "chunk_attn_fwd", "chunk_attn_bwd_ws_bytes",
-    "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "pkv_timing_enable", "pkv_timing_collect",
+    "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "paged_kv_copy", "pkv_timing_enable", "pkv_timing_collect",
     "pkv_timing_get",
 )
 
@@ -75,6 +76,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                                 _P]),
         "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P]),
         "paged_kv_grad_offload": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _P]),
+        "paged_kv_copy": (_I, [_P, _P, _U, _I, _I, _P]),
         "pkv_timing_enable": (_I, [ctypes.c_int]),
         "pkv_timing_collect": (ctypes.c_int, []),
         "pkv_timing_get": (_I, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I),
@@ -280,6 +282,13 @@ def paged_kv_grad_offload(host: Pool, host_bt: torch.Tensor, dev: Pool, dev_bt: 
     n_kvh = host.h_kv - kvh0 if n_kvh is None else n_kvh
     _check(load().paged_kv_grad_offload(host.handle, _ptr(host_bt), host_bt.numel(), dev.handle, _ptr(dev_bt),
                                         dev_bt.numel(), _ptr(lps), lps.numel(), kvh0, n_kvh, _stream(stream)))
+
+
+def paged_kv_copy(src: Pool, dst: Pool, what: int, first_page: int = 0, n_pages: Optional[int] = None, stream=None):
+    """Copy physical pages [first_page, first_page + n_pages) of src into the same pages of dst:
+    KV pages with PKV_COPY_KV, gradient pages with PKV_COPY_GRAD (host or device pools alike)."""
+    n_pages = min(src.n_pages, dst.n_pages) - first_page if n_pages is None else n_pages
+    _check(load().paged_kv_copy(src.handle, dst.handle, what, first_page, n_pages, _stream(stream)))
 
 
 def timing_enable(on: bool = True):

@@ -629,4 +629,42 @@ int paged_kv_grad_offload(pkv_pool* host, const int32_t* host_bt_dev, int32_t n_
   return PKV_OK;
 }
 
+int paged_kv_copy(const pkv_pool* src, pkv_pool* dst, uint32_t what, int32_t first_page, int32_t n_pages,
+                  void* stream) {
+  if (!src || !dst) return fail(PKV_E_INVALID, "NULL pool");
+  if (src == dst) return fail(PKV_E_INVALID, "source and destination are the same pool");
+  if (what & ~(PKV_COPY_KV | PKV_COPY_GRAD)) return fail(PKV_E_INVALID, "unknown copy bits 0x%x", what);
+  if (src->page != dst->page || src->h_kv != dst->h_kv || src->d != dst->d)
+    return fail(PKV_E_INVALID, "pool shapes differ");
+  if (first_page < 0 || n_pages < 0 || (int64_t)first_page + n_pages > src->n_pages ||
+      (int64_t)first_page + n_pages > dst->n_pages)
+    return fail(PKV_E_INVALID, "pages [%d, %d) outside a pool (%d and %d pages)", first_page,
+                first_page + n_pages, src->n_pages, dst->n_pages);
+  if ((what & PKV_COPY_GRAD) && (!src->grad || !dst->grad))
+    return fail(PKV_E_STATE, "gradient copy needs gradient pages in both pools");
+  if (n_pages == 0 || what == 0) {
+    ok();
+    return PKV_OK;
+  }
+  // Host allocations are addressed by their host pointers, so the runtime sees pinned host memory
+  // and uses a copy engine.
+  const size_t page_elems = (size_t)src->h_kv * 2 * src->page * src->d;
+  if (what & PKV_COPY_KV) {
+    const size_t bytes = page_elems * sizeof(uint16_t);
+    const char* s = (const char*)(src->kv_host ? src->kv_host : (void*)src->kv) + bytes * first_page;
+    char* d = (char*)(dst->kv_host ? dst->kv_host : (void*)dst->kv) + bytes * first_page;
+    hipError_t e = hipMemcpyAsync(d, s, bytes * n_pages, hipMemcpyDefault, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (KV pages)");
+  }
+  if (what & PKV_COPY_GRAD) {
+    const size_t bytes = page_elems * sizeof(float);
+    const char* s = (const char*)(src->grad_host ? src->grad_host : (void*)src->grad) + bytes * first_page;
+    char* d = (char*)(dst->grad_host ? dst->grad_host : (void*)dst->grad) + bytes * first_page;
+    hipError_t e = hipMemcpyAsync(d, s, bytes * n_pages, hipMemcpyDefault, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (gradient pages)");
+  }
+  ok();
+  return PKV_OK;
+}
+
 }  // extern "C"

@@ -14,12 +14,12 @@ move to CPU memory too). Every computation is a library kernel; this module only
 """
 from __future__ import annotations
 
-from typing import List, Optional
+from typing import List, Optional, Sequence
 
 import torch
 
-from . import (Pool, chunk_attn_bwd, chunk_attn_bwd_ws_bytes, chunk_attn_fwd, chunk_attn_fwd_ws_bytes, load,
-               page_topk_select, paged_kv_gather, paged_kv_grad_offload)
+from . import (PKV_COPY_GRAD, PKV_COPY_KV, Pool, chunk_attn_bwd, chunk_attn_bwd_ws_bytes, chunk_attn_fwd,
+               chunk_attn_fwd_ws_bytes, load, page_topk_select, paged_kv_copy, paged_kv_gather, paged_kv_grad_offload)
 
 
 class HostTierStep:
@@ -130,3 +130,82 @@ class HostTierStep:
 
     def free(self):
         self.dev.free()
+
+
+class DenseLayerPrefetch:
+    """Dense chunk steps over a stack of layers whose KV and gradient pages live in pinned host memory.
+
+    pt 2.D: with dense (or local) attention the next block is fetched while the current one is
+    computed; es 2.B: the transfers overlap the next layer's computation. Here a block is one layer's
+    whole page pool. Two device pools alternate: while layer l's forward and backward run on one,
+    a load stream fills the other with the next layer's KV and gradient pages (paged_kv_copy, a copy
+    engine), and a write-back stream copies layer l's gradient pages home once its backward is done.
+    Physical page numbers are the same on host and device, so the layer's block table serves both.
+
+    A step is the chunk's forward and backward with its own K/V already in the pages, as in the
+    reverse pass of the chunk-recurrent loop; gradients add to the host pages' running sums."""
+
+    def __init__(self, hosts: Sequence[Pool], device: torch.device):
+        h0 = hosts[0]
+        for h in hosts:
+            assert h.host_tier and h.host_grads, "layers need KV and gradient pages in host memory"
+            assert (h.n_pages, h.page, h.h_kv, h.d) == (h0.n_pages, h0.page, h0.h_kv, h0.d)
+        self.hosts = list(hosts)
+        self.dev = [Pool(h0.n_pages, h0.page, h0.h_kv, h0.d, grads=True) for _ in range(2)]
+        self.load_s = torch.cuda.Stream(device=device)
+        self.wb_s = torch.cuda.Stream(device=device)
+        self.loaded = [torch.cuda.Event() for _ in range(2)]
+        self.written = [torch.cuda.Event() for _ in range(2)]
+        self.computed = [torch.cuda.Event() for _ in range(2)]
+        for ev in self.written:
+            ev.record(torch.cuda.current_stream(device))
+        self.layer_written = [torch.cuda.Event() for _ in hosts]  # last write-back of each layer
+        self.buf_layer = [None, None]  # layer whose pages a device pool holds (or is receiving)
+        self.cur = 0                   # device pool of the next step
+        self.ws_f = self.ws_b = None
+
+    def prefetch(self, layer: int, buf: Optional[int] = None):
+        """Enqueue the copy of layer's KV and gradient pages into device pool buf (default: the pool
+        after the current one), once that pool's previous gradients and the layer's own latest
+        gradients have been written back (a layer run twice in a row is then not overlapped)."""
+        j = (self.cur ^ 1) if buf is None else buf
+        with torch.cuda.stream(self.load_s):
+            self.load_s.wait_event(self.written[j])
+            self.load_s.wait_event(self.layer_written[layer])
+            paged_kv_copy(self.hosts[layer], self.dev[j], PKV_COPY_KV | PKV_COPY_GRAD, stream=self.load_s)
+            self.loaded[j].record(self.load_s)
+        self.buf_layer[j] = layer
+
+    def run(self, layer: int, next_layer: Optional[int], bt: torch.Tensor, n_prior: int, q: torch.Tensor,
+            dout: torch.Tensor, scale: float, o: torch.Tensor, lse: torch.Tensor, dq: torch.Tensor):
+        """Forward + backward of one chunk of `layer` (bt: its logical-to-physical block table). The
+        pages of next_layer (if given) are fetched meanwhile into the other device pool."""
+        compute = torch.cuda.current_stream(q.device)
+        j = self.cur
+        if self.buf_layer[j] != layer:
+            self.prefetch(layer, j)
+        if next_layer is not None:
+            self.prefetch(next_layer, j ^ 1)
+        dev = self.dev[j]
+        C, H_q = q.shape[0], q.shape[1]
+        if self.ws_f is None:
+            self.ws_f = torch.empty(max(chunk_attn_fwd_ws_bytes(dev, n_prior, -1, dev.h_kv, C, H_q), 1),
+                                    dtype=torch.uint8, device=q.device)
+            self.ws_b = torch.empty(max(chunk_attn_bwd_ws_bytes(dev, n_prior, -1, dev.h_kv, C, H_q), 1),
+                                    dtype=torch.uint8, device=q.device)
+        compute.wait_event(self.loaded[j])
+        chunk_attn_fwd(dev, bt, n_prior, q, scale, o=o, lse=lse, ws=self.ws_f)
+        chunk_attn_bwd(dev, bt, n_prior, q, o, dout, lse, scale, dq=dq, ws=self.ws_b)
+        self.computed[j].record(compute)
+        with torch.cuda.stream(self.wb_s):
+            self.wb_s.wait_event(self.computed[j])
+            paged_kv_copy(dev, self.hosts[layer], PKV_COPY_GRAD, stream=self.wb_s)
+            self.written[j].record(self.wb_s)
+            self.layer_written[layer].record(self.wb_s)
+        self.cur = j ^ 1
+        if next_layer is None:
+            self.buf_layer[j ^ 1] = None
+
+    def free(self):
+        for d in self.dev:
+            d.free()

@@ -36,6 +36,7 @@ from .selection import (
     select_pages,
     n_selected,
     topk_pages,
+    topk_pages_per_query_page,
 )
 
 __all__ = [

@@ -9,6 +9,8 @@ for LLMs with Million-Token Contexts" (gist.science pt / es / it).
 * pt 2.B / es 2.B / it 2.B: keys, values and their gradients live in pages; backward adds the
   key/value gradients in place.
 * pt 2.C / es 2.B / it 2.D: page-level sparse attention attends only to selected key pages.
+  pt 2.C picks the pages for each query page: a selection may hold one page list per KV head
+  (shared by the whole chunk) or one per (KV head, query page of ``page`` chunk tokens).
 
 The pages never write the attention formula. The reading used here is standard scaled
 dot-product softmax attention with grouped query heads:
@@ -97,6 +99,24 @@ def _prep(q, kseq, vseq, dtype):
     return q, k, v
 
 
+def _key_sets(q0, C, page, sel, g, rows):
+    """(visible key tokens, positions into ``rows``) for KV head g.
+
+    sel None or sel[g] one-dimensional: one key set for every row. sel[g] two-dimensional
+    ([C/page][n_sel], pt 2.C): the rows of query page i (chunk tokens [i*page, (i+1)*page)) see
+    the pages sel[g][i] plus the own block."""
+    if sel is None or np.ndim(sel[g]) == 1:
+        yield visible_keys(q0, C, page if page else 1, None if sel is None else sel[g]), np.arange(len(rows))
+        return
+    lists = np.asarray(sel[g])
+    assert page and lists.shape[0] * page == C, "one page list per query page"
+    qpage = rows // page
+    for i in range(lists.shape[0]):
+        pos = np.nonzero(qpage == i)[0]
+        if len(pos):
+            yield visible_keys(q0, C, page, lists[i]), pos
+
+
 def _row_blocks(rows, block):
     for i in range(0, len(rows), block):
         yield rows[i:i + block]
@@ -108,7 +128,8 @@ def chunk_forward(q, kseq, vseq, q0, scale, sel=None, page=None, rows=None,
 
     q: [C][H_q][d]; kseq, vseq: [L][H_kv][d] logical key/value tokens with L >= q0 + C (bf16 bits
     or floats). sel: None for dense, else [H_kv][n_sel] selected logical prior pages (page size
-    ``page``). rows: optional chunk token indices to evaluate (default: all C).
+    ``page``), or [H_kv][C/page][n_sel] with one list per query page. rows: optional chunk token
+    indices to evaluate (default: all C).
 
     Returns O [R][H_q][d] and LSE [H_q][R] (natural log, including the scale), R = len(rows).
     """
@@ -120,15 +141,16 @@ def chunk_forward(q, kseq, vseq, q0, scale, sel=None, page=None, rows=None,
     out = np.zeros((len(rows), H_q, d), dtype=dtype)
     lse = np.zeros((H_q, len(rows)), dtype=dtype)
     for g in range(H_kv):
-        kidx = visible_keys(q0, C, page if page else 1, None if sel is None else sel[g])
-        kg, vg = k[kidx, g, :], v[kidx, g, :]
-        for hh in range(G):
-            h = g * G + hh
-            for i0 in range(0, len(rows), block):
-                r = rows[i0:i0 + block]
-                o, l_, _ = group_forward(q[r, h, :], q0 + r, kg, vg, kidx, scale)
-                out[i0:i0 + block, h, :] = o
-                lse[h, i0:i0 + block] = l_
+        for kidx, pos in _key_sets(q0, C, page, sel, g, rows):
+            kg, vg = k[kidx, g, :], v[kidx, g, :]
+            for hh in range(G):
+                h = g * G + hh
+                for i0 in range(0, len(pos), block):
+                    pb = pos[i0:i0 + block]
+                    r = rows[pb]
+                    o, l_, _ = group_forward(q[r, h, :], q0 + r, kg, vg, kidx, scale)
+                    out[pb, h, :] = o
+                    lse[h, pb] = l_
     return out, lse
 
 
@@ -138,7 +160,8 @@ def chunk_backward(q, kseq, vseq, do, q0, scale, sel=None, page=None, rows=None,
 
     Same arguments as ``chunk_forward`` plus do [C][H_q][d]. Returns a dict with
       dq:   [R][H_q][d] for the evaluated rows,
-      keys: list over KV heads of the visible logical key tokens,
+      keys: list over KV heads of the visible logical key tokens (with one page list per query
+            page: the ascending union over the lists),
       dk, dv: lists over KV heads of [N_g][d] gradients of those keys from this chunk,
       o, lse: the forward outputs of the evaluated rows.
     When ``rows`` is a subset, dk/dv hold only those rows' contributions.
@@ -154,21 +177,25 @@ def chunk_backward(q, kseq, vseq, do, q0, scale, sel=None, page=None, rows=None,
     lse_all = np.zeros((H_q, len(rows)), dtype=dtype)
     keys, dks, dvs = [], [], []
     for g in range(H_kv):
-        kidx = visible_keys(q0, C, page if page else 1, None if sel is None else sel[g])
-        kg, vg = k[kidx, g, :], v[kidx, g, :]
-        dkg = np.zeros_like(kg)
-        dvg = np.zeros_like(vg)
-        for hh in range(G):
-            h = g * G + hh
-            for i0 in range(0, len(rows), block):
-                r = rows[i0:i0 + block]
-                dq_, dk_, dv_, o_, l_ = group_backward(q[r, h, :], q0 + r, do[r, h, :], kg, vg, kidx, scale)
-                dq[i0:i0 + block, h, :] = dq_
-                o_all[i0:i0 + block, h, :] = o_
-                lse_all[h, i0:i0 + block] = l_
-                dkg += dk_
-                dvg += dv_
-        keys.append(kidx)
+        sets = list(_key_sets(q0, C, page, sel, g, rows))
+        allk = sets[0][0] if len(sets) == 1 else np.unique(np.concatenate([ks for ks, _ in sets]))
+        dkg = np.zeros((len(allk), d), dtype=dtype)
+        dvg = np.zeros((len(allk), d), dtype=dtype)
+        for kidx, pos in sets:
+            at = np.searchsorted(allk, kidx) if len(sets) > 1 else np.arange(len(kidx))
+            kg, vg = k[kidx, g, :], v[kidx, g, :]
+            for hh in range(G):
+                h = g * G + hh
+                for i0 in range(0, len(pos), block):
+                    pb = pos[i0:i0 + block]
+                    r = rows[pb]
+                    dq_, dk_, dv_, o_, l_ = group_backward(q[r, h, :], q0 + r, do[r, h, :], kg, vg, kidx, scale)
+                    dq[pb, h, :] = dq_
+                    o_all[pb, h, :] = o_
+                    lse_all[h, pb] = l_
+                    dkg[at] += dk_
+                    dvg[at] += dv_
+        keys.append(allk)
         dks.append(dkg)
         dvs.append(dvg)
     return {"dq": dq, "keys": keys, "dk": dks, "dv": dvs, "o": o_all, "lse": lse_all}

@@ -13,6 +13,9 @@ Readings where the pages are silent:
   query summary is the sum of its queries over tokens and the group's heads; a page's
   representative is its mean key; score = plain dot product. Positive scale factors do not change
   the ranking, so sums are used where means would only rescale.
+* pt 2.C instead picks pages for each query page: ``topk_pages_per_query_page`` applies the same
+  summary and ranking to every page of queries on its own, giving one list per (KV head, query
+  page), still shared by the KV head's query heads.
 * The n_local most recent prior pages are always kept and take no part in the ranking; top-K is
   taken over the remaining older pages; ties go to the lower logical page id; a NaN score ranks
   below every other score; the result is sorted ascending.
@@ -115,3 +118,23 @@ def topk_pages(q, kseq_prior, page: int, h_kv: int, n_prior: int, top_k: int, n_
     n_cand = max(n_prior - n_local, 0)
     sc = page_scores(qs, reps[:n_cand])
     return select_pages(sc, n_prior, top_k, n_local), sc, reps
+
+
+def topk_pages_per_query_page(q, kseq_prior, page: int, h_kv: int, n_prior: int, top_k: int, n_local: int):
+    """Selection per query page (pt 2.C: the most relevant key pages for each page of queries).
+
+    The chunk's queries are cut into query pages of ``page`` tokens. Each query page is summarised
+    and ranks the candidates exactly as a whole chunk does in ``topk_pages``, over its own tokens
+    only (same fixed float32 order; page is a multiple of 64).
+    Returns (sel [H_kv][C/page][n_sel] int32, scores [H_kv][C/page][n_cand] float32, reps)."""
+    x = np.asarray(q)
+    C = x.shape[0]
+    assert C % page == 0 and page % 64 == 0
+    reps = page_reps(page_key_sums(kseq_prior, page), page)[:n_prior]
+    n_cand = max(n_prior - n_local, 0)
+    sels, scs = [], []
+    for i in range(C // page):
+        sc = page_scores(query_sum(x[i * page:(i + 1) * page], h_kv), reps[:n_cand])
+        sels.append(select_pages(sc, n_prior, top_k, n_local))
+        scs.append(sc)
+    return np.stack(sels, axis=1), np.stack(scs, axis=1), reps

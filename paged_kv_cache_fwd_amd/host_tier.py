@@ -60,14 +60,21 @@ class HostTierStep:
         self.ready = [torch.cuda.Event() for _ in range(H)]
         self.done = [torch.cuda.Event() for _ in range(H)]
         # Gradient offloads run on a stream of their own, so the next step's gathers need not queue
-        # behind them; the next backward of head g waits for its offload (own pages: head 0's).
+        # behind them; the next backward of head g waits for head g's offload.
         self.off = torch.cuda.Stream(device=device) if self.host_grads else None
         self.off_done = [torch.cuda.Event() for _ in range(H)]
-        for ev in self.done + self.off_done:
+        self.own_done = torch.cuda.Event()  # the last head's own-page offload
+        for ev in self.done + self.off_done + [self.own_done]:
             ev.record(torch.cuda.current_stream(device))
 
     def append_own(self, k: torch.Tensor, v: torch.Tensor):
-        """Append the chunk's own K/V ([C][H_kv][d] bf16) into its device pages."""
+        """Append the chunk's own K/V ([C][H_kv][d] bf16) into its device pages.
+
+        The append also clears the pages' device gradient blocks, so with gradient pages in host
+        memory it first waits for the last head's offload of them (the offload stream runs in
+        order, so every earlier head's has finished too)."""
+        if self.host_grads:
+            torch.cuda.current_stream(k.device).wait_event(self.own_done)
         self.dev.append(self.own_bt, self.n_prior * self.dev.page, k, v)
 
     def run(self, q: torch.Tensor, dout: torch.Tensor, scale: float, o: torch.Tensor, lse: torch.Tensor,
@@ -76,8 +83,8 @@ class HostTierStep:
         same selection without host traffic; not with gradient pages in host memory).
 
         Gradient pages in host memory: head g's backward accumulates into its device slots, and an
-        offload stream then adds them to the host pages and clears them (paged_kv_grad_offload), the
-        chunk's own pages after the last head. The next step's backward of head g waits for that
+        offload stream then adds them, and head g's blocks of the chunk's own pages, to the host pages
+        and clears them (paged_kv_grad_offload). The next step's backward of head g waits for that
         offload, so a slot is cleared before it is reused."""
         assert gather or not self.host_grads
         compute = torch.cuda.current_stream(q.device)
@@ -108,9 +115,7 @@ class HostTierStep:
             chunk_attn_fwd(self.dev, self.bt[g], self.n_prior, q, scale, sel=sel, kvh0=g, n_kvh=1, o=o, lse=lse,
                            ws=self.ws_f)
             if self.host_grads:
-                compute.wait_event(self.off_done[g])  # the previous step's offload of these slots
-                if g == 0:
-                    compute.wait_event(self.off_done[H - 1])  # and of the own pages (after head H-1)
+                compute.wait_event(self.off_done[g])  # the previous step's offload of head g's blocks
                 chunk_attn_bwd(self.dev, self.bt[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
                                gpool=self.dev, gbt=self.bt[g], dq=dq, ws=self.ws_b)
             else:
@@ -120,11 +125,13 @@ class HostTierStep:
             if self.host_grads:
                 with torch.cuda.stream(self.off):
                     self.off.wait_event(self.done[g])
+                    # Only head g's backward writes head g's blocks of the own pages. They go first:
+                    # the next chunk's append waits for them, not for the selected pages.
+                    paged_kv_grad_offload(self.host, self.host_bt, self.dev, self.own_bt, self.own_lps, kvh0=g,
+                                          n_kvh=1, stream=self.off)
+                    self.own_done.record(self.off)
                     paged_kv_grad_offload(self.host, self.host_bt, self.dev, self.bt[g], sel[g], kvh0=g, n_kvh=1,
                                           stream=self.off)
-                    if g == H - 1:  # every head's backward has added to the own pages
-                        paged_kv_grad_offload(self.host, self.host_bt, self.dev, self.own_bt, self.own_lps,
-                                              stream=self.off)
                     self.off_done[g].record(self.off)
         return sel
 

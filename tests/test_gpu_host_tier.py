@@ -102,6 +102,13 @@ def test_host_grads_small_parity_and_accumulation(pkv):
     step.run(q, do, wl.scale, o, lse, dq)
     torch.cuda.synchronize()
     dk2 = hpool.export(pkv.PKV_DK, hbt, 0, wl.n_pages).cpu().numpy()
+    # Two more steps back to back, each re-appending the own block (which clears its device gradient
+    # blocks) while the previous step's offload may still be running.
+    for _ in range(2):
+        step.append_own(t16(k_own), t16(v_own))
+        step.run(q, do, wl.scale, o, lse, dq)
+    torch.cuda.synchronize()
+    dk4 = hpool.export(pkv.PKV_DK, hbt, 0, wl.n_pages).cpu().numpy()
     slots = step.dev.export(pkv.PKV_DK, torch.arange(step.dev.n_pages, dtype=torch.int32, device=q.device), 0,
                             step.dev.n_pages).cpu().numpy()
     hpool.check()
@@ -118,6 +125,7 @@ def test_host_grads_small_parity_and_accumulation(pkv):
         untouched = np.setdiff1d(np.arange(wl.context), keys)
         assert not np.any(dk1[untouched, g]) and not np.any(dv1[untouched, g])
     compare("second step doubles dK", dk2, 2.0 * dk1, 1e-5, rel=1e-5)
+    compare("four steps quadruple dK", dk4, 4.0 * dk1, 1e-5, rel=1e-5)
     assert not np.any(slots)
     step.free()
     hpool.free()

@@ -26,8 +26,11 @@ def _full_grads(res, L, H_kv, d):
     return dk, dv
 
 
-def _torch_reference(q, k, v, do, q0, scale, kidx_per_g, H_q, H_kv):
-    """Independent reference with torch SDPA (math path) + autograd, float64."""
+def _torch_reference(q, k, v, do, q0, scale, kidx_per_g, H_q, H_kv, row_sets=None):
+    """Independent reference with torch SDPA (math path) + autograd, float64.
+
+    kidx_per_g[g]: key tokens every row may see; or, with row_sets, row_sets[g] is a list of
+    (rows, key tokens) pairs giving each row its own key set."""
     C, _, d = q.shape
     L = k.shape[0]
     G = H_q // H_kv
@@ -38,9 +41,12 @@ def _torch_reference(q, k, v, do, q0, scale, kidx_per_g, H_q, H_kv):
     for h in range(H_q):
         g = h // G
         allowed = torch.zeros(C, L, dtype=torch.bool)
-        kid = torch.tensor(kidx_per_g[g])
         qpos = torch.arange(C) + q0
-        allowed[:, kid] = True
+        if row_sets is None:
+            allowed[:, torch.tensor(kidx_per_g[g])] = True
+        else:
+            for rws, ks in row_sets[g]:
+                allowed[torch.tensor(rws)[:, None], torch.tensor(ks)[None, :]] = True
         allowed &= torch.arange(L)[None, :] <= qpos[:, None]
         o = torch.nn.functional.scaled_dot_product_attention(
             tq[:, h, :][None, None], tk[:, g, :][None, None], tv[:, g, :][None, None],
@@ -239,3 +245,57 @@ def test_bf16_bits_accepted():
     assert w.dtype == np.float32
     assert np.array_equal(w.view(np.uint32) & 0xFFFF, np.zeros_like(bits, dtype=np.uint32))
     assert np.max(np.abs(w - x)) <= np.max(np.abs(x)) * 2 ** -7
+
+
+def test_per_query_page_lists_match_torch_sdpa_and_autograd():
+    """One page list per query page (pt 2.C): every row sees its own query page's pages plus the
+    own block, checked against SDPA with the per-row mask written out."""
+    rng = np.random.default_rng(11)
+    H_q, H_kv, d, P, C = 4, 2, 8, 4, 16
+    n_prior = 10
+    q0 = n_prior * P
+    L = q0 + C
+    q, k, v, do = _rand((C, H_q, d), rng), _rand((L, H_kv, d), rng), _rand((L, H_kv, d), rng), _rand((C, H_q, d), rng)
+    scale = 0.37
+    sel = np.array([[[1, 4, 7], [0, 2, 9], [5, 6, 8], [1, 3, 4]],
+                    [[0, 8, 9], [2, 3, 7], [4, 5, 9], [0, 1, 6]]])
+    o, lse = oracle.chunk_forward(q, k, v, q0, scale, sel=sel, page=P)
+    res = oracle.chunk_backward(q, k, v, do, q0, scale, sel=sel, page=P)
+    row_sets = [[(list(range(i * P, (i + 1) * P)), oracle.visible_keys(q0, C, P, sel[g][i])) for i in range(C // P)]
+                for g in range(H_kv)]
+    to, tdq, tdk, tdv = _torch_reference(q, k, v, do, q0, scale, None, H_q, H_kv, row_sets=row_sets)
+    dk, dv = _full_grads(res, L, H_kv, d)
+    assert np.max(np.abs(o - to)) < 1e-12
+    assert np.max(np.abs(res["o"] - to)) < 1e-12
+    assert np.max(np.abs(res["dq"] - tdq)) < 1e-12
+    assert np.max(np.abs(dk - tdk)) < 1e-12
+    assert np.max(np.abs(dv - tdv)) < 1e-12
+    # Keys no list selects get no gradient; the reported keys are the union, ascending.
+    for g in range(H_kv):
+        want = np.union1d(np.concatenate([oracle.visible_keys(q0, C, P, sel[g][i]) for i in range(C // P)]), [])
+        assert np.array_equal(res["keys"][g], want)
+    # A row subset returns the same rows.
+    rows = np.array([1, 6, 13])
+    o2, lse2 = oracle.chunk_forward(q, k, v, q0, scale, sel=sel, page=P, rows=rows)
+    assert np.max(np.abs(o2 - o[rows])) < 1e-13 and np.max(np.abs(lse2 - lse[:, rows])) < 1e-13
+
+
+def test_per_query_page_identical_lists_equal_one_list():
+    rng = np.random.default_rng(12)
+    H_q, H_kv, d, P, C = 4, 2, 8, 4, 16
+    n_prior = 10
+    q0 = n_prior * P
+    L = q0 + C
+    q, k, v, do = _rand((C, H_q, d), rng), _rand((L, H_kv, d), rng), _rand((L, H_kv, d), rng), _rand((C, H_q, d), rng)
+    sel2 = [[1, 4, 7], [0, 8, 9]]
+    sel3 = np.repeat(np.array(sel2)[:, None, :], C // P, axis=1)
+    o2, l2 = oracle.chunk_forward(q, k, v, q0, 0.3, sel=sel2, page=P)
+    o3, l3 = oracle.chunk_forward(q, k, v, q0, 0.3, sel=sel3, page=P)
+    assert np.max(np.abs(o2 - o3)) < 1e-13 and np.max(np.abs(l2 - l3)) < 1e-13
+    r2 = oracle.chunk_backward(q, k, v, do, q0, 0.3, sel=sel2, page=P)
+    r3 = oracle.chunk_backward(q, k, v, do, q0, 0.3, sel=sel3, page=P)
+    assert np.max(np.abs(r2["dq"] - r3["dq"])) < 1e-13
+    for g in range(H_kv):
+        assert np.array_equal(r2["keys"][g], r3["keys"][g])
+        assert np.max(np.abs(r2["dk"][g] - r3["dk"][g])) < 1e-12
+        assert np.max(np.abs(r2["dv"][g] - r3["dv"][g])) < 1e-12

@@ -166,3 +166,58 @@ def test_duplicate_pages_tie_to_lower_id():
         assert sc[g, 2] == sc[g, 9]
         best = sel[g, 0]
         assert best != 9
+
+
+def test_per_query_page_single_page_equals_chunk_selection():
+    """A chunk of one query page selects exactly what the whole-chunk rule selects."""
+    wl = synth.WORKLOADS["topk256k"]
+    n_prior = 40
+    kk, _ = synth.kv_tokens(wl, 0, n_prior)
+    q = synth.q_chunk(wl, 63)[: wl.page]
+    want, sc, _ = oracle.topk_pages(q, kk, wl.page, wl.h_kv, n_prior, 8, 2)
+    got, sc3, _ = oracle.topk_pages_per_query_page(q, kk, wl.page, wl.h_kv, n_prior, 8, 2)
+    assert got.shape == (wl.h_kv, 1, 10)
+    assert np.array_equal(got[:, 0], want)
+    assert np.array_equal(sc3[:, 0], sc)
+
+
+def test_per_query_page_hand_built():
+    """Query page i points at key page 2 + 2i: each query page picks its own page (pt 2.C)."""
+    P, d, n_prior = 64, 8, 6
+    k = np.zeros((n_prior * P, 1, d), np.float32)
+    for p in range(n_prior):
+        k[p * P:(p + 1) * P, 0, p] = 1.0          # every key of page p is e_p: rep = e_p
+    q = np.zeros((2 * P, 1, d), np.float32)
+    q[:P, 0, 2] = 1.0                              # query page 0 -> e_2
+    q[P:, 0, 4] = 1.0                              # query page 1 -> e_4
+    sel, sc, _ = oracle.topk_pages_per_query_page(q, k, P, 1, n_prior, 1, 0)
+    assert sel.tolist() == [[[2], [4]]]
+    assert sc[0, 0, 2] == 64.0 and sc[0, 1, 4] == 64.0
+    sel, _, _ = oracle.topk_pages_per_query_page(q, k, P, 1, n_prior, 1, 1)
+    assert sel.tolist() == [[[2, 5], [4, 5]]]
+    # The whole-chunk rule sees 64 e_2 + 64 e_4: a tie between pages 2 and 4, lower id wins.
+    whole, _, _ = oracle.topk_pages(q, k, P, 1, n_prior, 1, 0)
+    assert whole.tolist() == [[2]]
+
+
+def test_per_query_page_against_float64_bruteforce():
+    wl = synth.WORKLOADS["topk256k"]
+    n_prior, K, n_local = 96, 16, 4
+    kk, _ = synth.kv_tokens(wl, 0, n_prior)
+    q = synth.q_chunk(wl, 63)[: 4 * wl.page]
+    sel, _, _ = oracle.topk_pages_per_query_page(q, kk, wl.page, wl.h_kv, n_prior, K, n_local)
+    assert sel.shape == (wl.h_kv, 4, K + n_local)
+    kf = synth.bf16_widen(kk).astype(np.float64).reshape(n_prior, wl.page, wl.h_kv, wl.d).mean(axis=1)
+    qf = synth.bf16_widen(q).astype(np.float64).reshape(4, wl.page, wl.h_kv, wl.group, wl.d).sum(axis=(1, 3))
+    checked = 0
+    for g in range(wl.h_kv):
+        for i in range(4):
+            s64 = kf[: n_prior - n_local, g, :] @ qf[i, g]
+            order = sorted(range(n_prior - n_local), key=lambda p: (-s64[p], p))
+            gap = s64[order[K - 1]] - s64[order[K]]
+            if gap > 1e-6 * np.max(np.abs(s64)):
+                assert sorted(order[:K]) + list(range(n_prior - n_local, n_prior)) == sel[g, i].tolist()
+                checked += 1
+    assert checked >= 10
+    # Different query pages do pick different pages on this data.
+    assert any(not np.array_equal(sel[g, 0], sel[g, i]) for g in range(wl.h_kv) for i in range(1, 4))

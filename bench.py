@@ -357,7 +357,7 @@ def main():
     ap.add_argument("--no-recurrent", action="store_true", help="skip the chunk-recurrent layer driver")
     ap.add_argument("--no-densehost", action="store_true",
                     help="skip the dense 1M-token workload over host-resident layers")
-    ap.add_argument("--only", choices=("topk", "host1m", "densehost"),
+    ap.add_argument("--only", choices=("topk", "qpage", "host1m", "densehost"),
                     help="time only this workload (for per-workload profiles; prints no headline value)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run one plain streaming kernel (torch.neg on fp32) over this many MiB, as the "
@@ -422,12 +422,15 @@ def main():
     n_sel = min(top_k, n_prior - n_local) + n_local
     sel = torch.empty((H_kv, n_sel), dtype=torch.int32, device=dev)
     sel_l = torch.empty((H_kv, LOCAL_WINDOW), dtype=torch.int32, device=dev)
-    ws_f = torch.empty(max(max(pkv.chunk_attn_fwd_ws_bytes(pool, n_prior, ns, H_kv, C, H_q)
-                               for ns in (-1, n_sel, LOCAL_WINDOW)), 1), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(max(max(pkv.chunk_attn_bwd_ws_bytes(pool, n_prior, ns, H_kv, C, H_q)
-                               for ns in (-1, n_sel, LOCAL_WINDOW)), 1), dtype=torch.uint8, device=dev)
-    ws_t = torch.empty(max(pkv.load().page_topk_ws_bytes(pool.handle, n_prior, C, H_q), 1), dtype=torch.uint8,
-                       device=dev)
+    n_qp = C // P
+    sel_q = torch.empty((H_kv, n_qp, n_sel), dtype=torch.int32, device=dev)
+    shapes = ((-1, 1), (n_sel, 1), (LOCAL_WINDOW, 1), (n_sel, n_qp))
+    ws_f = torch.empty(max(max(pkv.chunk_attn_fwd_ws_bytes(pool, n_prior, ns, H_kv, C, H_q, nl)
+                               for ns, nl in shapes), 1), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(max(pkv.chunk_attn_bwd_ws_bytes(pool, n_prior, ns, H_kv, C, H_q, nl)
+                               for ns, nl in shapes), 1), dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(max(pkv.load().page_topk_ws_bytes(pool.handle, n_prior, C, H_q, n_qp), 1),
+                       dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step_dense():
@@ -444,6 +447,12 @@ def main():
     def step_topk():
         pool.append(bt, q0, k_own, v_own)
         s = pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
+        pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, sel=s, o=o, lse=lse, ws=ws_f)
+        pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, sel=s, dq=dq, ws=ws_b)
+
+    def step_qpage():
+        pool.append(bt, q0, k_own, v_own)
+        s = pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel_q, ws=ws_t, per_query_page=True)
         pkv.chunk_attn_fwd(pool, bt, n_prior, q, wl.scale, sel=s, o=o, lse=lse, ws=ws_f)
         pkv.chunk_attn_bwd(pool, bt, n_prior, q, o, do, lse, wl.scale, sel=s, dq=dq, ws=ws_b)
 
@@ -482,6 +491,14 @@ def main():
         print(json.dumps({"workload": "topk256k", "ms_per_step": round(ms_topk, 4),
                           "TFLOP/s": round(14.0 * d * H_q * ps / (ms_topk * 1e-3) / 1e12, 2),
                           "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}), flush=True)
+        pool.free()
+        return
+    if args.only == "qpage":
+        ps = pairs_sparse(C, n_sel, P)
+        ms_qp, kt_qp = run(step_qpage, "qpage256k")
+        print(json.dumps({"workload": "qpage256k", "ms_per_step": round(ms_qp, 4),
+                          "TFLOP/s": round(14.0 * d * H_q * ps / (ms_qp * 1e-3) / 1e12, 2),
+                          "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_qp.items()}}), flush=True)
         pool.free()
         return
     ms_dense, kt_dense = run(step_dense, "dense256k")
@@ -552,6 +569,24 @@ def main():
                 "step_stats": stats.get("topk256k"),
                 "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}
 
+    qpage = None
+    if not args.no_topk:
+        # Same pair count as the shared-list step: every query page attends to n_sel prior pages.
+        ms_qp, kt_qp = run(step_qpage, "qpage256k")
+        log(f"[bench] qpage256k: {ms_qp:.3f} ms/step, {flop_topk / (ms_qp * 1e-3) / 1e12:.1f} TFLOP/s")
+        for kname, (n, ms) in sorted(kt_qp.items(), key=lambda x: -x[1][1]):
+            log(f"[bench]   {kname:18s} launches {n:4d}  avg {ms / n:.3f} ms")
+        qpage = {"workload": f"qpage256k: top-64 + 4 local pages of 2016 chosen per query page ({n_qp} query "
+                             "pages x 4 KV heads), + own block",
+                 "value": round(flop_topk / (ms_qp * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                 "ms_per_step": round(ms_qp, 4), "flop_per_step": flop_topk,
+                 "vs_shared_list_step": round(ms_qp / ms_topk, 3),
+                 "select_ms": round(sum(v[1] / v[0] for k, v in kt_qp.items()
+                                        if k in ("k_qsum_part", "k_qsum", "k_scores", "k_topk")), 4),
+                 "fwd_ms": split_ms(kt_qp)[0], "bwd_ms": split_ms(kt_qp)[1],
+                 "step_stats": stats.get("qpage256k"),
+                 "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_qp.items()}}
+
     local = None
     if not args.no_topk:
         ms_local, kt_local = run(step_local, "local256k")
@@ -590,6 +625,7 @@ def main():
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "step_stats": stats.get("dense256k"),
         "cpu_baseline": cpu,
         "topk256k": topk,
+        "qpage256k": qpage,
         "local256k": local,
         "host1m": host1m,
         "dense1m_host": dense_host,

@@ -172,36 +172,46 @@ int paged_kv_check(pkv_pool* pool);
  *            candidate logical pages p in [0, n_cand), n_cand = max(n_prior - n_local, 0);
  *   the min(top_k, n_cand) best candidates by (score descending, page id ascending; NaN lowest),
  *   sorted ascending, followed by the n_local most recent prior pages [n_cand, n_prior).
- * Output sel_dev: [H_kv][n_sel] int32 logical page ids, n_sel = min(top_k, n_cand) + (n_prior -
- * n_cand), also stored to *n_sel_out (host; known without synchronising).
+ * n_lists = 1 gives one selection per KV head for the whole chunk. n_lists = C / page_size gives
+ * one per (KV head, query page) (pt 2.C: the most relevant key pages for each page of queries):
+ * the chunk's tokens [i*page_size, (i+1)*page_size) form query page i, whose summary qsum_{g,i}
+ * follows the order above over its own tokens only, and which ranks the candidates on its own.
+ * Output sel_dev: [H_kv][n_lists][n_sel] int32 logical page ids, n_sel = min(top_k, n_cand) +
+ * (n_prior - n_cand), also stored to *n_sel_out (host; known without synchronising).
  * q_dev: [C][H_q][head_dim] bf16, 16-byte aligned, C % 64 == 0. ws_dev: at least
- * page_topk_ws_bytes(...) bytes.
- * Errors: PKV_E_INVALID (shapes), PKV_E_UNSUPPORTED (H_q / H_kv > 128), PKV_E_RANGE (n_prior >
- * n_bt), PKV_E_NOMEM (workspace too small); nothing is enqueued on error.
+ * page_topk_ws_bytes(...) bytes (same n_lists).
+ * Errors: PKV_E_INVALID (shapes, n_lists other than 1 or C / page_size), PKV_E_UNSUPPORTED
+ * (H_q / H_kv > 128), PKV_E_RANGE (n_prior > n_bt), PKV_E_NOMEM (workspace too small); nothing
+ * is enqueued on error.
  */
-size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int32_t H_q);
+size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int32_t H_q, int32_t n_lists);
 int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
                      const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
-                     int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes, void* stream);
+                     int32_t n_lists, int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes,
+                     void* stream);
 
 /*
  * Forward attention of one query chunk over the paged cache (pt 2.A, 2.B; es 2.B custom kernels).
  * Query head h (KV head g = h / G) at chunk row t (position q0 + t) attends to
  *   dense (sel_dev == NULL): every key at position <= q0 + t, i.e. logical pages [0, n_prior)
  *                            plus the chunk's own block;
- *   sparse: the pages sel_dev[g*n_sel + i], i < n_sel (ascending logical ids < n_prior), plus
- *           the own block, causally. A selection of no page (n_sel == 0: the own block only)
- *           still passes a non-NULL sel_dev, which is then not read.
+ *   sparse: the pages sel_dev[(g*n_lists + l)*n_sel + i], i < n_sel (ascending logical ids <
+ *           n_prior), plus the own block, causally, where l = 0 when n_lists == 1 and l = t /
+ *           page_size (the row's query page, pt 2.C) when n_lists == C / page_size. A selection
+ *           of no page (n_sel == 0: the own block only) still passes a non-NULL sel_dev, which
+ *           is then not read. Dense calls take n_lists = 1.
  * with softmax(scale * q.k). The own block (logical pages [n_prior, n_prior + C/page_size)) must
  * already be appended. Only KV heads [kvh0, kvh0 + n_kvh) and their query heads are computed.
  * Outputs: o_dev [C][H_q][head_dim] bf16 and lse_dev [H_q][C] fp32 for those heads.
  * ws_dev: at least chunk_attn_fwd_ws_bytes(...) bytes of device scratch (may be NULL if 0). The
- * *_ws_bytes queries take n_sel < 0 for dense calls.
+ * *_ws_bytes queries take n_sel < 0 for dense calls, and the call's n_lists.
+ * Errors: PKV_E_INVALID (shapes, alignment, n_sel or n_lists out of range), PKV_E_RANGE (block
+ * table too short), PKV_E_STATE (host-tier pool), PKV_E_NOMEM (workspace too small).
  */
-size_t chunk_attn_fwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh,
-                               int32_t C, int32_t H_q);
+size_t chunk_attn_fwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_lists,
+                               int32_t n_kvh, int32_t C, int32_t H_q);
 int chunk_attn_fwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
-                   const int32_t* sel_dev, int32_t n_sel, int32_t kvh0, int32_t n_kvh,
+                   const int32_t* sel_dev, int32_t n_sel, int32_t n_lists, int32_t kvh0, int32_t n_kvh,
                    const uint16_t* q_dev, int32_t C, int32_t H_q, float scale,
                    uint16_t* o_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
@@ -210,15 +220,15 @@ int chunk_attn_fwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, in
  * accumulation into gradient pages). Probabilities are recomputed from q, the pages and lse.
  * dq_dev [C][H_q][head_dim] bf16 is written. dK and dV of every attended key are ADDED (fp32) into
  * the gradient pages of gpool through gbt_dev (gpool may equal pool and gbt_dev may equal bt_dev;
- * gpool must have PKV_GRADS). sel_dev/n_sel must equal the forward's. o_dev, dout_dev:
+ * gpool must have PKV_GRADS). sel_dev/n_sel/n_lists must equal the forward's. o_dev, dout_dev:
  * [C][H_q][head_dim] bf16; lse_dev as written by chunk_attn_fwd.
  * Calls that add into the same gradient pages commute (fp32 atomic adds).
  */
-size_t chunk_attn_bwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh,
-                               int32_t C, int32_t H_q);
+size_t chunk_attn_bwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_lists,
+                               int32_t n_kvh, int32_t C, int32_t H_q);
 int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt,
                    pkv_pool* gpool, const int32_t* gbt_dev, int32_t n_gbt, int32_t n_prior,
-                   const int32_t* sel_dev, int32_t n_sel, int32_t kvh0, int32_t n_kvh,
+                   const int32_t* sel_dev, int32_t n_sel, int32_t n_lists, int32_t kvh0, int32_t n_kvh,
                    const uint16_t* q_dev, const uint16_t* o_dev, const uint16_t* dout_dev,
                    const float* lse_dev, int32_t C, int32_t H_q, float scale, uint16_t* dq_dev,
                    void* ws_dev, size_t ws_bytes, void* stream);

@@ -67,12 +67,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "paged_kv_zero_grad": (_I, [_P, _P, _I, _P]),
         "paged_kv_export": (_I, [_P, _I, _P, _I, _I, _I, _P, _P]),
         "paged_kv_check": (_I, [_P]),
-        "page_topk_ws_bytes": (_S, [_P, _I, _I, _I]),
-        "page_topk_select": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, ctypes.POINTER(_I), _P, _S, _P]),
-        "chunk_attn_fwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I]),
-        "chunk_attn_fwd": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
-        "chunk_attn_bwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I]),
-        "chunk_attn_bwd": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _S,
+        "page_topk_ws_bytes": (_S, [_P, _I, _I, _I, _I]),
+        "page_topk_select": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), _P, _S, _P]),
+        "chunk_attn_fwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I, _I]),
+        "chunk_attn_fwd": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _I, _I, _F, _P, _P, _P, _S, _P]),
+        "chunk_attn_bwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I, _I]),
+        "chunk_attn_bwd": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _S,
                                 _P]),
         "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P]),
         "paged_kv_grad_offload": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _P]),
@@ -178,53 +178,76 @@ def _ws(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tenso
 
 
 def page_topk_select(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, top_k: int, n_local: int,
-                     sel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
-    """Returns sel [H_kv][n_sel] int32 (logical page ids, ascending per head)."""
+                     sel: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None,
+                     per_query_page: bool = False):
+    """Returns sel [H_kv][n_sel] int32 (logical page ids, ascending per head), or with
+    per_query_page one list per query page: [H_kv][C / page][n_sel]. A given sel buffer must be
+    contiguous and large enough; the result is a view of its first elements."""
     lib = load()
     _need(bt, torch.int32, "bt")
     _need(q, torch.bfloat16, "q")
     C, H_q, _ = q.shape
     n_cand = max(n_prior - n_local, 0)
     n_sel = min(top_k, n_cand) + (n_prior - n_cand)
+    n_lists = C // pool.page if per_query_page else 1
+    shape = (pool.h_kv, n_lists, n_sel) if per_query_page else (pool.h_kv, n_sel)
+    need = pool.h_kv * n_lists * n_sel
     if sel is None:
-        sel = torch.empty((pool.h_kv, max(n_sel, 0)), dtype=torch.int32, device=q.device)
-    nb = lib.page_topk_ws_bytes(pool.handle, n_prior, C, H_q)
+        sel = torch.empty(shape, dtype=torch.int32, device=q.device)
+    _need(sel, torch.int32, "sel")
+    if sel.numel() < need:
+        raise ValueError(f"sel holds {sel.numel()} entries, {need} needed")
+    nb = lib.page_topk_ws_bytes(pool.handle, n_prior, C, H_q, n_lists)
     ws = _ws(nb, q.device, ws)
     out_n = _I(0)
     _check(lib.page_topk_select(pool.handle, _ptr(bt), bt.numel(), n_prior, _ptr(q), C, H_q, top_k, n_local,
-                                _ptr(sel), ctypes.byref(out_n), _ptr(ws), nb, _stream(stream)))
+                                n_lists, _ptr(sel), ctypes.byref(out_n), _ptr(ws), nb, _stream(stream)))
     assert out_n.value == n_sel
-    return sel[:, :n_sel] if sel.shape[1] != n_sel else sel
+    return sel if tuple(sel.shape) == shape else sel.view(-1)[:need].view(shape)
 
 
-def chunk_attn_fwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int) -> int:
-    return load().chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+def chunk_attn_fwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int,
+                            n_lists: int = 1) -> int:
+    return load().chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
 
 
-def chunk_attn_bwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int) -> int:
-    return load().chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+def chunk_attn_bwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int,
+                            n_lists: int = 1) -> int:
+    return load().chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
+
+
+def _sel_shape(sel: Optional[torch.Tensor]):
+    """(n_sel, n_lists) of a selection: None -> dense; [H_kv][n_sel]; [H_kv][C/page][n_sel]."""
+    if sel is None:
+        return -1, 1
+    _need(sel, torch.int32, "sel")
+    if sel.dim() == 2:
+        return sel.shape[1], 1
+    if sel.dim() == 3:
+        return sel.shape[2], sel.shape[1]
+    raise ValueError(f"sel must be [H_kv][n_sel] or [H_kv][C/page][n_sel], got shape {tuple(sel.shape)}")
 
 
 def chunk_attn_fwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, scale: float,
                    sel: Optional[torch.Tensor] = None, kvh0: int = 0, n_kvh: Optional[int] = None,
                    o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    ws: Optional[torch.Tensor] = None, stream=None):
-    """Forward of one chunk; returns (o [C][H_q][d] bf16, lse [H_q][C] fp32)."""
+    """Forward of one chunk; returns (o [C][H_q][d] bf16, lse [H_q][C] fp32). sel: None (dense),
+    [H_kv][n_sel] (one list per KV head) or [H_kv][C/page][n_sel] (one list per query page)."""
     lib = load()
     _need(bt, torch.int32, "bt")
     _need(q, torch.bfloat16, "q")
     C, H_q, d = q.shape
     n_kvh = pool.h_kv - kvh0 if n_kvh is None else n_kvh
-    n_sel = -1 if sel is None else sel.shape[1]
-    if sel is not None:
-        _need(sel, torch.int32, "sel")
+    n_sel, n_lists = _sel_shape(sel)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((H_q, C), dtype=torch.float32, device=q.device)
-    nb = lib.chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+    nb = lib.chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
     ws = _ws(nb, q.device, ws)
-    _check(lib.chunk_attn_fwd(pool.handle, _ptr(bt), bt.numel(), n_prior, _sel_ptr(sel, bt), max(n_sel, 0), kvh0, n_kvh,
+    _check(lib.chunk_attn_fwd(pool.handle, _ptr(bt), bt.numel(), n_prior, _sel_ptr(sel, bt), max(n_sel, 0), n_lists,
+                              kvh0, n_kvh,
                               _ptr(q), C, H_q, float(scale), _ptr(o), _ptr(lse), _ptr(ws), nb, _stream(stream)))
     return o, lse
 
@@ -242,17 +265,15 @@ def chunk_attn_bwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
     _need(lse, torch.float32, "lse")
     C, H_q, d = q.shape
     n_kvh = pool.h_kv - kvh0 if n_kvh is None else n_kvh
-    n_sel = -1 if sel is None else sel.shape[1]
-    if sel is not None:
-        _need(sel, torch.int32, "sel")
+    n_sel, n_lists = _sel_shape(sel)
     gpool = pool if gpool is None else gpool
     gbt = bt if gbt is None else gbt
     if dq is None:
         dq = torch.empty_like(q)
-    nb = lib.chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_kvh, C, H_q)
+    nb = lib.chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
     ws = _ws(nb, q.device, ws)
     _check(lib.chunk_attn_bwd(pool.handle, _ptr(bt), bt.numel(), gpool.handle, _ptr(gbt), gbt.numel(), n_prior,
-                              _sel_ptr(sel, bt), max(n_sel, 0), kvh0, n_kvh, _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), C,
+                              _sel_ptr(sel, bt), max(n_sel, 0), n_lists, kvh0, n_kvh, _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), C,
                               H_q, float(scale), _ptr(dq), _ptr(ws), nb, _stream(stream)))
     return dq
 

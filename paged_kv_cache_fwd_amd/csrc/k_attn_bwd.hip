@@ -86,8 +86,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int32_t gi = u / (n_rb * splits);
   const int32_t g = a.kvh0 + gi;
   const int32_t G = a.G, CG = a.C * G, P = a.page, H = a.h_kv;
-  const int32_t r0 = rb * 32 * T::NW;
-  const int32_t r_last = min(r0 + 32 * T::NW - 1, CG - 1);
+  // Row blocks never straddle two selection lists: list li owns rows [li*RL, (li+1)*RL).
+  const int32_t RL = CG / a.n_lists;
+  const int32_t bpl = (RL + 32 * T::NW - 1) / (32 * T::NW);
+  const int32_t li = rb / bpl;
+  const int32_t r0 = li * RL + (rb - li * bpl) * 32 * T::NW;
+  const int32_t r_end = min(r0 + 32 * T::NW, (li + 1) * RL);
+  const int32_t r_last = r_end - 1;
   const int32_t t_min = r0 / G, t_max = r_last / G;
   const int32_t q0 = a.n_prior * P;
   const int tsh = (P == 128) ? 1 : 0;  // log2(64-key tiles per page)
@@ -97,8 +102,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int32_t te = (int32_t)((int64_t)n_tiles * (sp + 1) / splits);
 
   const int32_t row = r0 + wave * 32 + l32;
-  const bool rvalid = row < CG;
-  const int32_t rr = rvalid ? row : CG - 1;
+  const bool rvalid = row < r_end;
+  const int32_t rr = rvalid ? row : r_last;
   const int32_t tq = rr / G;
   const int32_t h = g * G + (rr - tq * G);
   bf16x8 qreg[T::KS], doreg[T::KS];
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   auto tile_src = [&](int32_t i, int32_t& kpos0) -> const uint16_t* {
     const int32_t pi = i >> tsh, sub = i & ((1 << tsh) - 1);
-    const int32_t lp = list_page(a, g, pi);
+    const int32_t lp = list_page(a, g, li, pi);
     const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
     if (ph < 0) {
       kpos0 = -1;

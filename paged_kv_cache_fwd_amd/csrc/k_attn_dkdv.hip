@@ -5,6 +5,9 @@
 // it 2.B (custom kernels add the key/value gradients in place into gradient pages, outside
 // autograd, with atomic adds).
 //
+// With one page list per query page (pt 2.C) a workgroup takes one query page's rows and keys
+// from that page's list, so every row block it streams sees all of its keys.
+//
 // One workgroup = 4 waves, one per SIMD, each owning 64 keys (two 32-key tiles) of one KV head:
 // K of its keys in VGPRs, V in LDS, dK and dV (2 x 64 x d fp32) in accumulation registers for the
 // whole row range. The G query heads of the KV head are packed as rows r = t*G + hh and streamed
@@ -73,6 +76,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int32_t ku = (u / row_splits) % n_ku;
   const int32_t gi = u / (row_splits * n_ku);
   const int32_t g = a.kvh0 + gi;
+  // With one page list per query page the row splits are the query pages (the host plan sets
+  // row_splits = n_lists, whose row ranges then start and end on query-page boundaries).
+  const int32_t li = a.n_lists > 1 ? rs : 0;
   const int32_t G = a.G, CG = a.C * G, P = a.page, H = a.h_kv;
   const float invG = 1.0f / (float)G;
   const int32_t q0 = a.n_prior * P;
@@ -95,7 +101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (kval[j]) {
       const int32_t pi = kt_idx >> tsh;
       tsub[j] = kt_idx & ((1 << tsh) - 1);
-      const int32_t lp = list_page(a, g, pi);
+      const int32_t lp = list_page(a, g, li, pi);
       const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
       gph[j] = phys_page(e.gbt, e.n_gbt, e.n_gpool_pages, lp, a.err);
       kval[j] = (ph >= 0) && (gph[j] >= 0);

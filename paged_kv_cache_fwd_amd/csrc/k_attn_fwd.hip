@@ -8,6 +8,8 @@
 // Work decomposition. The G query heads sharing a KV head are packed into one row space:
 // row r = t*G + hh (t = chunk token, hh = head within the group), so every K/V tile staged in LDS
 // feeds 128 rows. A workgroup = (KV head, key-range split, 128-row block) with 4 waves of 32 rows;
+// with one page list per query page (pt 2.C) the row blocks are cut at query-page boundaries and
+// each walks its query page's list;
 // two independent workgroups share each CU (two waves per SIMD), so one wave's softmax overlaps
 // the other's matrix work without a shared barrier. K/V tiles go straight from global memory into
 // LDS. Splits > 1 write normalised partial outputs plus their log-sum-exp, merged by
@@ -54,8 +56,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int32_t gi = u / (n_rb * splits);
   const int32_t g = a.kvh0 + gi;
   const int32_t G = a.G, CG = a.C * G, P = a.page, H = a.h_kv;
-  const int32_t r0 = rb * 32 * T::NW;
-  const int32_t r_last = min(r0 + 32 * T::NW - 1, CG - 1);
+  // Row blocks never straddle two selection lists: list li owns rows [li*RL, (li+1)*RL).
+  const int32_t RL = CG / a.n_lists;
+  const int32_t bpl = (RL + 32 * T::NW - 1) / (32 * T::NW);
+  const int32_t li = rb / bpl;
+  const int32_t r0 = li * RL + (rb - li * bpl) * 32 * T::NW;
+  const int32_t r_end = min(r0 + 32 * T::NW, (li + 1) * RL);
+  const int32_t r_last = r_end - 1;
   const int32_t t_min = r0 / G, t_max = r_last / G;
   const int32_t q0 = a.n_prior * P;
   const int tsh = (P == 128) ? 1 : 0;  // log2(tiles per page)
@@ -66,8 +73,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // This lane's query row and its Q^T operand.
   const int32_t row = r0 + wave * 32 + l32;
-  const bool rvalid = row < CG;
-  const int32_t rr = rvalid ? row : CG - 1;
+  const bool rvalid = row < r_end;
+  const int32_t rr = rvalid ? row : r_last;
   const int32_t tq = rr / G;
   const int32_t h = g * G + (rr - tq * G);
   bf16x8 qreg[T::KS];
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Tile i of the key list -> first key position (-1 when the page is unreadable) and K base.
   auto tile_src = [&](int32_t i, int32_t& kpos0) -> const uint16_t* {
     const int32_t pi = i >> tsh, sub = i & ((1 << tsh) - 1);
-    const int32_t lp = list_page(a, g, pi);
+    const int32_t lp = list_page(a, g, li, pi);
     const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
     if (ph < 0) {
       kpos0 = -1;

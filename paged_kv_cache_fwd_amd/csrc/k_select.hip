@@ -9,6 +9,9 @@
 // is compiled with contraction off as well), so the selected ids are reproducible bit for bit:
 //   part[h][b][j] = sum_{t<64} Q[64b+t][h][j];  hsum[h][j] = sum_b part[h][b][j];
 //   qsum[g][j] = sum_{hh<G} hsum[gG+hh][j];      score[g][p] = sum_j qsum[g][j] * rep[p][g][j].
+// With one selection per query page (pt 2.C: the most relevant key pages for each page of
+// queries) the chunk's 64-token blocks are cut into n_lists groups of consecutive blocks; group i
+// is summarised, scored and selected on its own exactly as above (b running over its blocks).
 #include "pkv_device.h"
 
 #pragma clang fp contract(off)
@@ -30,50 +33,53 @@ __global__ __launch_bounds__(256) void k_qsum_part(const uint16_t* __restrict__ 
   part[idx] = acc;
 }
 
-// qsum[g][j], one workgroup per KV head g: hsum[hh][j] = sum_b part[gG+hh][b][j] by threads
-// (hh, j) with the part values fetched 16 at a time ahead of the in-order adds, then
-// qsum[g][j] = sum_hh hsum[hh][j] in order by threads j.
+// qsum[g][i][j], one workgroup per (KV head g, list i): hsum[hh][j] = sum over the list's blocks b
+// of part[gG+hh][b][j] by threads (hh, j) with the part values fetched 16 at a time ahead of the
+// in-order adds, then qsum[g][i][j] = sum_hh hsum[hh][j] in order by threads j.
 constexpr int kQsumThreads = 1024;
 __global__ __launch_bounds__(kQsumThreads) void k_qsum(const float* __restrict__ part, int32_t H_kv, int32_t G,
-                                                       int32_t D, int32_t nb, float* __restrict__ qsum) {
+                                                       int32_t D, int32_t nb, int32_t n_lists,
+                                                       float* __restrict__ qsum) {
   extern __shared__ float hsum[];  // [G][D]
-  const int32_t g = blockIdx.x;
+  const int32_t g = blockIdx.x / n_lists, li = blockIdx.x % n_lists;
+  const int32_t nbl = nb / n_lists, b0 = li * nbl;
   for (int32_t idx = threadIdx.x; idx < G * D; idx += kQsumThreads) {
     const int32_t hh = idx / D, j = idx % D;
-    const float* ph = part + ((int64_t)(g * G + hh) * nb) * D + j;
+    const float* ph = part + ((int64_t)(g * G + hh) * nb + b0) * D + j;
     float hs = 0.0f;
     int32_t b = 0;
-    for (; b + 16 <= nb; b += 16) {
+    for (; b + 16 <= nbl; b += 16) {
       float v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) v[u] = ph[(int64_t)(b + u) * D];
 #pragma unroll
       for (int u = 0; u < 16; ++u) hs = __fadd_rn(hs, v[u]);
     }
-    for (; b < nb; ++b) hs = __fadd_rn(hs, ph[(int64_t)b * D]);
+    for (; b < nbl; ++b) hs = __fadd_rn(hs, ph[(int64_t)b * D]);
     hsum[idx] = hs;
   }
   __syncthreads();
   for (int32_t j = threadIdx.x; j < D; j += kQsumThreads) {
     float qs = 0.0f;
     for (int32_t hh = 0; hh < G; ++hh) qs = __fadd_rn(qs, hsum[hh * D + j]);
-    qsum[(int64_t)g * D + j] = qs;
+    qsum[(int64_t)blockIdx.x * D + j] = qs;
   }
 }
 
-// score[g][p] for candidate logical pages p < n_cand; an unreadable page scores NaN (ranks last).
+// score[g][i][p] for candidate logical pages p < n_cand (blockIdx.y = g * n_lists + i); an
+// unreadable page scores NaN (ranks last).
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qsum, const float* __restrict__ rep,
-                                                int32_t n_pool, int32_t H_kv, int32_t D,
+                                                int32_t n_pool, int32_t H_kv, int32_t D, int32_t n_lists,
                                                 const int32_t* __restrict__ bt, int32_t n_bt, int32_t n_cand,
                                                 float* __restrict__ scores, int32_t* err) {
-  const int32_t g = blockIdx.y;
+  const int32_t gl = blockIdx.y, g = gl / n_lists;
   const int32_t p = blockIdx.x * 256 + threadIdx.x;
   if (p >= n_cand) return;
   const int32_t phys = phys_page(bt, n_bt, n_pool, p, err);
   float acc = __uint_as_float(0x7fc00000u);
   if (phys >= 0) {
     const f32x4* r = reinterpret_cast<const f32x4*>(rep + ((int64_t)phys * H_kv + g) * D);
-    const float* qs = qsum + (int64_t)g * D;
+    const float* qs = qsum + (int64_t)gl * D;
     acc = 0.0f;
 #pragma unroll 8
     for (int32_t j4 = 0; j4 < D / 4; ++j4) {
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qsum, 
       acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 3], rv[3]));
     }
   }
-  scores[(int64_t)g * n_cand + p] = acc;
+  scores[(int64_t)gl * n_cand + p] = acc;
 }
 
 // Order key: larger is better. High word: score mapped to an order-preserving unsigned integer
@@ -102,9 +108,9 @@ __device__ __forceinline__ uint64_t order_key(float s, int32_t id) {
 
 constexpr int kSelThreads = 1024;
 
-// One workgroup per KV head: radix select (8 passes of 8 bits, most significant first) finds the
-// K-th largest order key exactly; the winners are then compacted in ascending id order with a
-// block-wide ballot scan, and the local pages are appended.
+// One workgroup per (KV head, list): radix select (8 passes of 8 bits, most significant first)
+// finds the K-th largest order key exactly; the winners are then compacted in ascending id order
+// with a block-wide ballot scan, and the local pages are appended.
 __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ scores, int32_t n_cand,
                                                       int32_t K, int32_t n_prior, int32_t n_sel,
                                                       int32_t* __restrict__ sel) {
@@ -112,10 +118,10 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
   __shared__ uint64_t s_prefix, s_mask;
   __shared__ uint32_t s_remaining, s_done;
   __shared__ uint32_t wave_tot[kSelThreads / 64];
-  const int32_t g = blockIdx.x;
+  const int32_t gl = blockIdx.x;  // g * n_lists + list
   const int32_t tid = threadIdx.x;
-  const float* sc = scores + (int64_t)g * n_cand;
-  int32_t* out = sel + (int64_t)g * n_sel;
+  const float* sc = scores + (int64_t)gl * n_cand;
+  int32_t* out = sel + (int64_t)gl * n_sel;
 
   uint64_t threshold = 0;  // select keys >= threshold
   const bool take_all = (K >= n_cand);
@@ -199,16 +205,17 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
   for (int32_t u = tid; u < n_prior - n_cand; u += kSelThreads) out[kk + u] = n_cand + u;
 }
 
-size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d) {
-  const size_t nb = (size_t)C / 64;
+size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d, int32_t n_lists) {
+  const size_t nb = (size_t)C / 64, nl = (size_t)(n_lists > 0 ? n_lists : 1);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al((size_t)h_q * nb * d * 4) + al((size_t)h_kv * d * 4) + al((size_t)h_kv * (size_t)(n_cand > 0 ? n_cand : 1) * 4);
+  return al((size_t)h_q * nb * d * 4) + al((size_t)h_kv * nl * d * 4) +
+         al((size_t)h_kv * nl * (size_t)(n_cand > 0 ? n_cand : 1) * 4);
 }
 
 hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const uint16_t* q,
-                       int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t* sel, void* ws,
-                       hipStream_t s) {
-  const int32_t H = pool.h_kv, D = pool.d, G = h_q / H;
+                       int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t n_lists, int32_t* sel,
+                       void* ws, hipStream_t s) {
+  const int32_t H = pool.h_kv, D = pool.d, G = h_q / H, HL = H * n_lists;
   const int32_t nb = C / 64;
   const int32_t n_cand = n_prior > n_local ? n_prior - n_local : 0;
   const int32_t K = top_k < n_cand ? top_k : n_cand;
@@ -218,7 +225,7 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
   char* w = (char*)ws;
   float* part = (float*)w;
   float* qsum = (float*)(w + al((size_t)h_q * nb * D * 4));
-  float* scores = (float*)(w + al((size_t)h_q * nb * D * 4) + al((size_t)H * D * 4));
+  float* scores = (float*)(w + al((size_t)h_q * nb * D * 4) + al((size_t)HL * D * 4));
   if (n_cand > 0 && K > 0 && K < n_cand) {
     const int64_t n1 = (int64_t)h_q * nb * D;
     {
@@ -227,17 +234,18 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
     }
     {
       TimerScope ts_("k_qsum", s);
-      hipLaunchKernelGGL(k_qsum, dim3((unsigned)H), dim3(kQsumThreads), (size_t)G * D * 4, s, part, H, G, D, nb, qsum);
+      hipLaunchKernelGGL(k_qsum, dim3((unsigned)HL), dim3(kQsumThreads), (size_t)G * D * 4, s, part, H, G, D, nb,
+                         n_lists, qsum);
     }
     {
       TimerScope ts_("k_scores", s);
-      hipLaunchKernelGGL(k_scores, dim3((unsigned)((n_cand + 255) / 256), H), dim3(256), 0, s, qsum, pool.rep,
-                         pool.n_pages, H, D, bt, n_bt, n_cand, scores, pool.err);
+      hipLaunchKernelGGL(k_scores, dim3((unsigned)((n_cand + 255) / 256), HL), dim3(256), 0, s, qsum, pool.rep,
+                         pool.n_pages, H, D, n_lists, bt, n_bt, n_cand, scores, pool.err);
     }
   }
   {
     TimerScope ts_("k_topk", s);
-    hipLaunchKernelGGL(k_topk, dim3(H), dim3(kSelThreads), 0, s, scores, n_cand, K, n_prior, n_sel, sel);
+    hipLaunchKernelGGL(k_topk, dim3(HL), dim3(kSelThreads), 0, s, scores, n_cand, K, n_prior, n_sel, sel);
   }
   return hipGetLastError();
 }

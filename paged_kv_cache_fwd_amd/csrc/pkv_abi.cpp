@@ -49,8 +49,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Shared checks of chunk_attn_fwd / chunk_attn_bwd.
 int check_attn(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const int32_t* sel,
-               int32_t n_sel, int32_t kvh0, int32_t n_kvh, const uint16_t* q, int32_t C, int32_t H_q,
-               float scale) {
+               int32_t n_sel, int32_t n_lists, int32_t kvh0, int32_t n_kvh, const uint16_t* q, int32_t C,
+               int32_t H_q, float scale) {
   if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
   if (pool->flags & PKV_HOST_TIER)
     return fail(PKV_E_STATE, "attention reads device pages; gather host-tier pages into a device pool first");
@@ -69,14 +69,18 @@ int check_attn(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_
     return fail(PKV_E_INVALID, "KV head range [%d, %d) outside [0, %d)", kvh0, kvh0 + n_kvh, pool->h_kv);
   if (sel) {
     if (n_sel < 0 || n_sel > n_prior) return fail(PKV_E_INVALID, "n_sel=%d must be in [0, n_prior=%d]", n_sel, n_prior);
+    if (n_lists != 1 && n_lists != C / pool->page)
+      return fail(PKV_E_INVALID, "n_lists=%d must be 1 or C / page_size = %d", n_lists, C / pool->page);
+  } else if (n_lists != 1) {
+    return fail(PKV_E_INVALID, "dense attention takes n_lists = 1 (got %d)", n_lists);
   }
   if (!std::isfinite(scale)) return fail(PKV_E_INVALID, "scale is not finite");
   return PKV_OK;
 }
 
 pkv::AttnArgs make_args(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const int32_t* sel,
-                        int32_t n_sel, int32_t kvh0, int32_t n_kvh, const uint16_t* q, int32_t C, int32_t H_q,
-                        float scale) {
+                        int32_t n_sel, int32_t n_lists, int32_t kvh0, int32_t n_kvh, const uint16_t* q, int32_t C,
+                        int32_t H_q, float scale) {
   pkv::AttnArgs a;
   a.kv = pool->kv;
   a.n_pool_pages = pool->n_pages;
@@ -88,6 +92,7 @@ pkv::AttnArgs make_args(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, i
   a.n_prior = n_prior;
   a.sel = sel;
   a.n_sel = sel ? n_sel : 0;
+  a.n_lists = sel ? n_lists : 1;
   a.kvh0 = kvh0;
   a.n_kvh = n_kvh;
   a.q = q;
@@ -164,10 +169,17 @@ static int32_t best_split(int64_t base_units, double tiles, double overhead, int
   return best;
 }
 
-FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d) {
+// Row blocks of 128 rows, cut at selection-list boundaries (n_lists groups of C*G/n_lists rows).
+static int32_t row_blocks(int64_t rows, int32_t n_lists) {
+  const int64_t per_list = rows / n_lists;
+  return (int32_t)(n_lists * ((per_list + 127) / 128));
+}
+
+FwdPlan plan_fwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_kvh, int32_t C, int32_t G,
+                 int32_t d) {
   FwdPlan p;
   const int64_t rows = (int64_t)C * G;
-  p.n_rb = (int32_t)((rows + 127) / 128);  // 128 rows per workgroup, two workgroups per CU
+  p.n_rb = row_blocks(rows, n_lists);  // 128 rows per workgroup, two workgroups per CU
   const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
   p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 2);
@@ -175,10 +187,11 @@ FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, i
   return p;
 }
 
-BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d) {
+BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_kvh, int32_t C, int32_t G,
+                 int32_t d) {
   BwdPlan p;
   const int64_t rows = (int64_t)C * G;
-  p.n_rb = (int32_t)((rows + 127) / 128);  // 128 rows per workgroup, two workgroups per CU
+  p.n_rb = row_blocks(rows, n_lists);  // 128 rows per workgroup, two workgroups per CU
   const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
   p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 2);
@@ -186,7 +199,9 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, i
   p.n_ku = (int32_t)((n_kt + NKT_TILES_PER_WG - 1) / NKT_TILES_PER_WG);
   const int64_t n_blk = (rows + 31) / 32;
   const int32_t max_rs = (int32_t)std::min<int64_t>(64, n_blk);
-  p.row_splits = best_split((int64_t)n_kvh * p.n_ku, (double)n_blk, 2.0, max_rs, 1);
+  // One page list per query page: the dK/dV pass splits rows exactly at the lists (each query
+  // page's rows see only its list's pages).
+  p.row_splits = n_lists > 1 ? n_lists : best_split((int64_t)n_kvh * p.n_ku, (double)n_blk, 2.0, max_rs, 1);
   // [H_q][C] row dots (H_q = n_kvh*G is enough for the heads computed, but the buffer is indexed by
   // absolute head, so size it for every head the pool can address), then dQ partials.
   p.ws_bytes = 0;  // filled by the caller, which knows H_q
@@ -481,14 +496,15 @@ int paged_kv_check(pkv_pool* pool) {
   return PKV_OK;
 }
 
-size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int32_t H_q) {
-  if (!pool || C <= 0 || H_q <= 0 || n_prior < 0) return 0;
-  return pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d);
+size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int32_t H_q, int32_t n_lists) {
+  if (!pool || C <= 0 || H_q <= 0 || n_prior < 0 || n_lists <= 0) return 0;
+  return pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d, n_lists);
 }
 
 int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
                      const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
-                     int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes, void* stream) {
+                     int32_t n_lists, int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes,
+                     void* stream) {
   if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
   if (!bt_dev || !q_dev || !n_sel_out) return fail(PKV_E_INVALID, "NULL block table, q or n_sel_out");
   if (!aligned16(q_dev)) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
@@ -497,40 +513,52 @@ int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, 
   if (top_k < 0 || n_local < 0 || n_prior < 0) return fail(PKV_E_INVALID, "top_k, n_local, n_prior must be >= 0");
   if (H_q / pool->h_kv > 128) return fail(PKV_E_UNSUPPORTED, "H_q/H_kv=%d exceeds 128", H_q / pool->h_kv);
   if (n_prior > n_bt) return fail(PKV_E_RANGE, "n_prior=%d exceeds the block table (%d)", n_prior, n_bt);
+  if (n_lists != 1 && (C % pool->page != 0 || n_lists != C / pool->page))
+    return fail(PKV_E_INVALID, "n_lists=%d must be 1 or C / page_size", n_lists);
   const int32_t n_cand = n_prior > n_local ? n_prior - n_local : 0;
   const int32_t kk = std::min(top_k, n_cand);
   const int32_t n_sel = kk + (n_prior - n_cand);
   if (n_sel > 0 && !sel_dev) return fail(PKV_E_INVALID, "sel is NULL");
-  if (ws_bytes < pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d) || (!ws_dev && kk > 0 && kk < n_cand))
-    return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes,
-                pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d));
+  const size_t ws_need = pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d, n_lists);
+  if (ws_bytes < ws_need || (!ws_dev && kk > 0 && kk < n_cand))
+    return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes, ws_need);
   *n_sel_out = n_sel;
-  hipError_t e = pkv::launch_topk(*pool, bt_dev, n_bt, n_prior, q_dev, C, H_q, top_k, n_local, sel_dev, ws_dev,
-                                  (hipStream_t)stream);
+  hipError_t e = pkv::launch_topk(*pool, bt_dev, n_bt, n_prior, q_dev, C, H_q, top_k, n_local, n_lists, sel_dev,
+                                  ws_dev, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   ok();
   return PKV_OK;
 }
 
-size_t chunk_attn_fwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh, int32_t C,
-                               int32_t H_q) {
+// Selection lists per KV head as the plan sees them: 1 for dense calls and malformed counts (the
+// entry points reject those before planning).
+static int32_t plan_lists(int32_t n_sel, int32_t n_lists, int32_t C, int32_t page) {
+  return (n_sel >= 0 && n_lists > 1 && C % page == 0 && n_lists == C / page) ? n_lists : 1;
+}
+
+size_t chunk_attn_fwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_lists, int32_t n_kvh,
+                               int32_t C, int32_t H_q) {
   if (!pool || C <= 0 || H_q <= 0 || n_kvh <= 0 || H_q % pool->h_kv != 0) return 0;
   const int32_t n_list = n_sel >= 0 ? n_sel : n_prior;
-  return pkv::plan_fwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d).ws_bytes;
+  return pkv::plan_fwd(n_list, plan_lists(n_sel, n_lists, C, pool->page), pool->page, n_kvh, C, H_q / pool->h_kv,
+                       pool->d).ws_bytes;
 }
 
 int chunk_attn_fwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior, const int32_t* sel_dev,
-                   int32_t n_sel, int32_t kvh0, int32_t n_kvh, const uint16_t* q_dev, int32_t C, int32_t H_q,
-                   float scale, uint16_t* o_dev, float* lse_dev, void* ws_dev, size_t ws_bytes, void* stream) {
-  int rc = check_attn(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+                   int32_t n_sel, int32_t n_lists, int32_t kvh0, int32_t n_kvh, const uint16_t* q_dev, int32_t C,
+                   int32_t H_q, float scale, uint16_t* o_dev, float* lse_dev, void* ws_dev, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_attn(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, n_lists, kvh0, n_kvh, q_dev, C, H_q, scale);
   if (rc != PKV_OK) return rc;
   if (!o_dev || !lse_dev) return fail(PKV_E_INVALID, "NULL o or lse");
   if (!aligned16(o_dev)) return fail(PKV_E_INVALID, "o must be 16-byte aligned");
   const int32_t n_list = sel_dev ? n_sel : n_prior;
-  const pkv::FwdPlan plan = pkv::plan_fwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d);
+  const pkv::FwdPlan plan = pkv::plan_fwd(n_list, sel_dev ? n_lists : 1, pool->page, n_kvh, C, H_q / pool->h_kv,
+                                          pool->d);
   if (plan.ws_bytes > 0 && (!ws_dev || ws_bytes < plan.ws_bytes))
     return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
-  const pkv::AttnArgs a = make_args(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+  const pkv::AttnArgs a =
+      make_args(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, n_lists, kvh0, n_kvh, q_dev, C, H_q, scale);
   hipError_t e = pkv::launch_fwd(a, plan, o_dev, lse_dev, ws_dev, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   ok();
@@ -544,20 +572,21 @@ static size_t bwd_ws(const pkv_pool* pool, const pkv::BwdPlan& plan, int32_t n_k
   return align256(dbytes + dq);
 }
 
-size_t chunk_attn_bwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_kvh, int32_t C,
-                               int32_t H_q) {
+size_t chunk_attn_bwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_lists, int32_t n_kvh,
+                               int32_t C, int32_t H_q) {
   if (!pool || C <= 0 || H_q <= 0 || n_kvh <= 0 || H_q % pool->h_kv != 0) return 0;
   const int32_t n_list = n_sel >= 0 ? n_sel : n_prior;
-  const pkv::BwdPlan plan = pkv::plan_bwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d);
+  const pkv::BwdPlan plan = pkv::plan_bwd(n_list, plan_lists(n_sel, n_lists, C, pool->page), pool->page, n_kvh, C,
+                                          H_q / pool->h_kv, pool->d);
   return bwd_ws(pool, plan, n_kvh, C, H_q);
 }
 
 int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, pkv_pool* gpool, const int32_t* gbt_dev,
-                   int32_t n_gbt, int32_t n_prior, const int32_t* sel_dev, int32_t n_sel, int32_t kvh0, int32_t n_kvh,
-                   const uint16_t* q_dev, const uint16_t* o_dev, const uint16_t* dout_dev, const float* lse_dev,
+                   int32_t n_gbt, int32_t n_prior, const int32_t* sel_dev, int32_t n_sel, int32_t n_lists, int32_t kvh0,
+                   int32_t n_kvh, const uint16_t* q_dev, const uint16_t* o_dev, const uint16_t* dout_dev, const float* lse_dev,
                    int32_t C, int32_t H_q, float scale, uint16_t* dq_dev, void* ws_dev, size_t ws_bytes,
                    void* stream) {
-  int rc = check_attn(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+  int rc = check_attn(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, n_lists, kvh0, n_kvh, q_dev, C, H_q, scale);
   if (rc != PKV_OK) return rc;
   if (!gpool) return fail(PKV_E_INVALID, "gradient pool is NULL");
   if (!gpool->grad) return fail(PKV_E_STATE, "gradient pool has no gradient pages");
@@ -572,10 +601,12 @@ int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, pk
   if (!aligned16(o_dev) || !aligned16(dout_dev) || !aligned16(dq_dev))
     return fail(PKV_E_INVALID, "o, dout and dq must be 16-byte aligned");
   const int32_t n_list = sel_dev ? n_sel : n_prior;
-  const pkv::BwdPlan plan = pkv::plan_bwd(n_list, pool->page, n_kvh, C, H_q / pool->h_kv, pool->d);
+  const pkv::BwdPlan plan = pkv::plan_bwd(n_list, sel_dev ? n_lists : 1, pool->page, n_kvh, C, H_q / pool->h_kv,
+                                          pool->d);
   const size_t need = bwd_ws(pool, plan, n_kvh, C, H_q);
   if (!ws_dev || ws_bytes < need) return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes, need);
-  const pkv::AttnArgs a = make_args(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, kvh0, n_kvh, q_dev, C, H_q, scale);
+  const pkv::AttnArgs a =
+      make_args(pool, bt_dev, n_bt, n_prior, sel_dev, n_sel, n_lists, kvh0, n_kvh, q_dev, C, H_q, scale);
   pkv::BwdExtra x;
   x.o = o_dev;
   x.dout = dout_dev;

@@ -110,13 +110,14 @@ __device__ __forceinline__ void flag_error(int32_t* err, int32_t code) {
   if (err) atomicCAS(err, 0, code);
 }
 
-// Logical page of entry pi of a chunk's key-page list for KV head g: the prior part (all of
+// Logical page of entry pi of a chunk's key-page list for KV head g and selection list li (the
+// query page's list when there is one per query page, else 0): the prior part (all of
 // [0, n_prior) when dense, else the selected pages) followed by the chunk's own pages.
 // Returns -1 (and flags) for an out-of-range selection entry.
-__device__ __forceinline__ int32_t list_page(const AttnArgs& a, int32_t g, int32_t pi) {
+__device__ __forceinline__ int32_t list_page(const AttnArgs& a, int32_t g, int32_t li, int32_t pi) {
   if (a.sel == nullptr) return pi;
   if (pi < a.n_sel) {
-    int32_t lp = a.sel[(size_t)g * a.n_sel + pi];
+    int32_t lp = a.sel[((size_t)g * a.n_lists + li) * a.n_sel + pi];
     if (lp < 0 || lp >= a.n_prior) {
       flag_error(a.err, 2);
       return -1;

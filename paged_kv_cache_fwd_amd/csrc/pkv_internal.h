@@ -32,8 +32,9 @@ struct AttnArgs {
   const int32_t* bt;
   int32_t n_bt;
   int32_t n_prior;
-  const int32_t* sel;  // NULL = dense
+  const int32_t* sel;  // NULL = dense; else [h_kv][n_lists][n_sel] logical page ids
   int32_t n_sel;
+  int32_t n_lists;     // selection lists per KV head: 1, or one per query page (C / page)
   int32_t kvh0;
   int32_t n_kvh;
   const uint16_t* q;
@@ -68,23 +69,23 @@ class TimerScope {
 
 // Launch-shape decisions, computed on the host from the shapes alone.
 struct FwdPlan {
-  int32_t n_rb;       // row blocks of 256 rows per KV head
+  int32_t n_rb;       // row blocks of 128 rows per KV head (n_lists x blocks per list)
   int32_t splits;     // key-range splits (>1 needs the combine kernel and workspace)
   size_t ws_bytes;
 };
 struct BwdPlan {
-  int32_t n_rb;        // dQ pass: row blocks of 256 rows per KV head
+  int32_t n_rb;        // dQ pass: row blocks of 128 rows per KV head (n_lists x blocks per list)
   int32_t splits;      // dQ pass: key-range splits
   int32_t n_ku;        // dK/dV pass: key units of 256 keys per KV head
-  int32_t row_splits;  // dK/dV pass: row-range splits
+  int32_t row_splits;  // dK/dV pass: row-range splits (one per selection list when n_lists > 1)
   size_t ws_bytes;
 };
 
 int num_cus();
 // 32-key tiles per workgroup of the key-major dK/dV pass (4 waves x 2 tiles).
 constexpr int NKT_TILES_PER_WG = 8;
-FwdPlan plan_fwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
-BwdPlan plan_bwd(int32_t n_list_pages, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
+FwdPlan plan_fwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
+BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_kvh, int32_t C, int32_t G, int32_t d);
 
 hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t pos0, int32_t n,
                          const uint16_t* k, const uint16_t* v, hipStream_t s);
@@ -98,10 +99,10 @@ hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_
 hipError_t launch_grad_offload(const pkv_pool& host, const int32_t* host_bt, int32_t n_host_bt, const pkv_pool& dev,
                                const int32_t* dev_bt, int32_t n_dev_bt, const int32_t* lp, int32_t n, int32_t kvh0,
                                int32_t n_kvh, hipStream_t s);
-size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d);
+size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d, int32_t n_lists);
 hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const uint16_t* q,
-                       int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t* sel, void* ws,
-                       hipStream_t s);
+                       int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t n_lists, int32_t* sel,
+                       void* ws, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, const FwdPlan& plan, uint16_t* o, float* lse, void* ws, hipStream_t s);
 hipError_t launch_bwd(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, void* ws, hipStream_t s);
 template <int D>

@@ -50,7 +50,7 @@ class HostTierStep:
         self.sel = torch.empty((H, self.n_sel), dtype=torch.int32, device=device)
         self.own_lps = torch.arange(n_prior, n_prior + self.n_own, dtype=torch.int32, device=device)
         lib = load()
-        self.ws_t = torch.empty(max(lib.page_topk_ws_bytes(host.handle, n_prior, C, H_q), 1), dtype=torch.uint8,
+        self.ws_t = torch.empty(max(lib.page_topk_ws_bytes(host.handle, n_prior, C, H_q, 1), 1), dtype=torch.uint8,
                                 device=device)
         self.ws_f = torch.empty(max(chunk_attn_fwd_ws_bytes(self.dev, n_prior, self.n_sel, 1, C, H_q), 1),
                                 dtype=torch.uint8, device=device)

@@ -54,17 +54,18 @@ def test_argument_errors_without_device(lib):
     assert lib.paged_kv_alloc(ctypes.byref(h), 4, 64, 1, 64, 0x80) == -1
     assert lib.paged_kv_free(None) == 0
     assert lib.pkv_last_error() == b""
-    assert lib.chunk_attn_fwd(None, None, 0, 0, None, 0, 0, 1, None, 64, 4, 0.1, None, None, None, 0, None) == -1
-    assert lib.chunk_attn_bwd(None, None, 0, None, None, 0, 0, None, 0, 0, 1, None, None, None, None, 64, 4, 0.1,
+    assert lib.chunk_attn_fwd(None, None, 0, 0, None, 0, 1, 0, 1, None, 64, 4, 0.1, None, None, None, 0, None) == -1
+    assert lib.chunk_attn_bwd(None, None, 0, None, None, 0, 0, None, 0, 1, 0, 1, None, None, None, None, 64, 4, 0.1,
                               None, None, 0, None) == -1
-    assert lib.page_topk_select(None, None, 0, 0, None, 64, 4, 1, 0, None, None, None, 0, None) == -1
+    assert lib.page_topk_select(None, None, 0, 0, None, 64, 4, 1, 0, 1, None, None, None, 0, None) == -1
     assert lib.paged_kv_append(None, None, 0, 0, 0, None, None, None) == -1
     assert lib.paged_kv_gather(None, None, None, 0, None, 0, 0, None, None, 0, None) == -1
     assert lib.paged_kv_grad_offload(None, None, 0, None, None, 0, None, 0, 0, 1, None) == -1
     assert lib.paged_kv_copy(None, None, 1, 0, 0, None) == -1
     assert lib.paged_kv_check(None) == -1
     assert lib.paged_kv_data(None, 0) is None
-    assert lib.chunk_attn_fwd_ws_bytes(None, 0, -1, 1, 64, 4) == 0
+    assert lib.chunk_attn_fwd_ws_bytes(None, 0, -1, 1, 1, 64, 4) == 0
+    assert lib.page_topk_ws_bytes(None, 0, 64, 4, 1) == 0
 
 
 def test_binding_fails_loudly_without_library():

@@ -105,3 +105,38 @@ def test_topk256k_selection_and_full_sparse_step(pkv, big):
         compare(f"dV head {g}", dv[keys, g], ref["dv"][g], ATOL_GRAD)
         untouched = np.setdiff1d(np.arange(wl.context), keys)
         assert np.all(dk[untouched, g] == 0) and np.all(dv[untouched, g] == 0)
+
+
+def test_qpage256k_selection_and_full_sparse_step(pkv, big):
+    """Top-64 + 4 local pages chosen per query page (32 query pages x 4 KV heads), full size."""
+    wl, c, pool, bt, k, v, q, do = big
+    wk = synth.WORKLOADS["topk256k"]
+    n_prior = wl.n_prior(c)
+    pool.zero_grad()
+    qt, dot = t16(q), t16(do)
+    sel = pkv.page_topk_select(pool, bt, n_prior, qt, wk.top_k, wk.n_local, per_query_page=True)
+    o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, qt, wl.scale, sel=sel)
+    dq = pkv.chunk_attn_bwd(pool, bt, n_prior, qt, o, dot, lse, wl.scale, sel=sel)
+    dk = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy()
+    dv = pool.export(pkv.PKV_DV, bt, 0, wl.n_pages).cpu().numpy()
+    torch.cuda.synchronize()
+    pool.check()
+    sel_np = sel.cpu().numpy()
+    say("qpage256k: oracle selection per query page")
+    want, _, _ = oracle.topk_pages_per_query_page(q, k[: n_prior * wl.page], wl.page, wl.h_kv, n_prior, wk.top_k,
+                                                  wk.n_local)
+    assert sel_np.shape == (wl.h_kv, wl.chunk // wl.page, 68)
+    assert np.array_equal(sel_np, want)
+    union = [len(np.unique(want[g])) for g in range(wl.h_kv)]
+    say(f"  distinct prior pages selected per KV head: {union}")
+    say("qpage256k: full sparse oracle (float32)")
+    ref = oracle.chunk_backward(q, k, v, do, wl.q0(c), wl.scale, sel=want, page=wl.page, dtype=np.float32)
+    compare("O", host(o), ref["o"], ATOL_O)
+    compare("LSE", lse.cpu().numpy(), ref["lse"], ATOL_LSE, rel=1e-5)
+    compare("dQ", host(dq), ref["dq"], ATOL_GRAD)
+    for g in range(wl.h_kv):
+        keys = ref["keys"][g]
+        compare(f"dK head {g}", dk[keys, g], ref["dk"][g], ATOL_GRAD)
+        compare(f"dV head {g}", dv[keys, g], ref["dv"][g], ATOL_GRAD)
+        untouched = np.setdiff1d(np.arange(wl.context), keys)
+        assert np.all(dk[untouched, g] == 0) and np.all(dv[untouched, g] == 0)

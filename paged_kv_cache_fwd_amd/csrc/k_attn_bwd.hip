@@ -7,8 +7,8 @@
 //
 // Kernels here:
 //  k_bwd_rowdot  per (head, token): -D with D = rowsum(dO * O), lse * log2 e, -lse / scale.
-//  k_bwd_dq      query-major: each wave keeps dQ^T for 32 rows in registers while walking the key
-//                list (S^T = K Q^T, P^T = exp(S^T - LSE), dP^T = V dO^T, dS^T = P^T (dP^T - D),
+//  k_bwd_dq      query-major, workgroups of 8 (or 4) waves like the forward: each wave keeps dQ^T
+//                for 32 rows in registers while walking the key list (S^T = K Q^T, P^T = exp(S^T - LSE), dP^T = V dO^T, dS^T = P^T (dP^T - D),
 //                dQ^T += K^T dS^T). Split over key ranges like the forward; partials (fp32) are
 //                summed by k_bwd_dq_reduce.
 // The key-major dK/dV pass (k_attn_dkdv.hip) keeps dK/dV of its keys on chip for all rows and
@@ -58,9 +58,9 @@ __global__ __launch_bounds__(256) void k_bwd_rowdot(AttnArgs a, const uint16_t* 
 }
 
 // ---------------------------------------------------------------------------------------------
-template <int D>
+template <int D, int NWAVES>
 struct DqCfg {
-  static constexpr int NW = 4;                       // waves per workgroup (32 rows each)
+  static constexpr int NW = NWAVES;                  // waves per workgroup (32 rows each)
   static constexpr int BK = 64;                      // keys per tile
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
@@ -70,11 +70,11 @@ struct DqCfg {
   static constexpr int ROWS_PER_SEG = 1024 / (2 * D);
 };
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(AttnArgs a, BwdExtra e, int32_t n_rb, int32_t splits,
-                                                   const float* __restrict__ ndbuf, const float* __restrict__ lse2buf,
-                                                   float* __restrict__ ws_dq) {
-  using T = DqCfg<D>;
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(
+    AttnArgs a, BwdExtra e, int32_t n_rb, int32_t splits, const float* __restrict__ ndbuf,
+    const float* __restrict__ lse2buf, float* __restrict__ ws_dq) {
+  using T = DqCfg<D, NW>;
   constexpr int BK = T::BK;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
 
@@ -299,8 +299,12 @@ static hipError_t launch_bwd_d(const AttnArgs& a, const BwdExtra& e, const BwdPl
     const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
     {
       TimerScope ts_("k_bwd_dq", s);
-      hipLaunchKernelGGL(k_bwd_dq<D>, dim3(n_units), dim3(64 * DqCfg<D>::NW), 0, s, a, e, plan.n_rb, plan.splits,
-                         ndbuf, lse2buf, ws_dq);
+      if (plan.dq_nw == 8)
+        hipLaunchKernelGGL((k_bwd_dq<D, 8>), dim3(n_units), dim3(64 * 8), 0, s, a, e, plan.n_rb, plan.splits, ndbuf,
+                           lse2buf, ws_dq);
+      else
+        hipLaunchKernelGGL((k_bwd_dq<D, 4>), dim3(n_units), dim3(64 * 4), 0, s, a, e, plan.n_rb, plan.splits, ndbuf,
+                           lse2buf, ws_dq);
     }
     if (plan.splits > 1) {
       const int64_t work = rows_total * (D / 8);

@@ -69,7 +69,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::NS * T::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t vres[T::NW * T::VROWS * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
+  // Wave-uniform, so the LDS destinations of the direct loads stay in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t n_units = a.n_kvh * n_ku * row_splits;
   const int32_t u = xcd_remap(blockIdx.x, n_units);
   const int32_t rs = u % row_splits;

@@ -7,13 +7,13 @@
 //
 // Work decomposition. The G query heads sharing a KV head are packed into one row space:
 // row r = t*G + hh (t = chunk token, hh = head within the group), so every K/V tile staged in LDS
-// feeds 128 rows. A workgroup = (KV head, key-range split, 128-row block) with 4 waves of 32 rows;
-// with one page list per query page (pt 2.C) the row blocks are cut at query-page boundaries and
-// each walks its query page's list;
-// two independent workgroups share each CU (two waves per SIMD), so one wave's softmax overlaps
-// the other's matrix work without a shared barrier. K/V tiles go straight from global memory into
-// LDS. Splits > 1 write normalised partial outputs plus their log-sum-exp, merged by
-// k_fwd_combine.
+// feeds every row of the workgroup. A workgroup = (KV head, key-range split, row block) with 8
+// waves of 32 rows (256 rows, one workgroup per CU) or 4 (128 rows, two workgroups per CU; used
+// when a 256-row block would be half empty). Either way two waves share each SIMD, so one wave's
+// softmax overlaps the other's matrix work. With one page list per query page (pt 2.C) the row
+// blocks are cut at query-page boundaries and each walks its query page's list. K/V tiles go
+// straight from global memory into LDS. Splits > 1 write normalised partial outputs plus their
+// log-sum-exp, merged by k_fwd_combine.
 //
 // Per wave and 64-key tile: S^T (keys x queries) = K Q^T as two 32x32 tiles (A = K rows from
 // LDS, B = Q^T in registers), so each lane owns one query column and its softmax statistics
@@ -26,9 +26,9 @@
 
 namespace pkv {
 
-template <int D>
+template <int D, int NWAVES>
 struct FwdCfg {
-  static constexpr int NW = 4;                      // waves per workgroup (32 rows each)
+  static constexpr int NW = NWAVES;                 // waves per workgroup (32 rows each)
   static constexpr int BK = 64;                     // keys per tile
   static constexpr int KS = D / 16;                 // contraction steps over d
   static constexpr int DT = D / 32;                 // 32-row tiles of O^T
@@ -40,15 +40,17 @@ struct FwdCfg {
 
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(AttnArgs a, int32_t n_rb, int32_t splits,
-                                                     uint16_t* __restrict__ o, float* __restrict__ lse,
-                                                     float* __restrict__ ws_o, float* __restrict__ ws_lse) {
-  using T = FwdCfg<D>;
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_fwd(
+    AttnArgs a, int32_t n_rb, int32_t splits, uint16_t* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+  using T = FwdCfg<D, NW>;
   constexpr int BK = T::BK;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * 2 * T::TILE];  // [stage][K|V]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lg = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
+  // Wave-uniform, so the LDS destinations of the direct loads stay in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t n_units = a.n_kvh * splits * n_rb;
   const int32_t u = xcd_remap(blockIdx.x, n_units);
   const int32_t rb = u % n_rb;
@@ -104,21 +106,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Direct global->LDS staging: wave w fills 1 KiB segments w*SEG_PER_WAVE + j of the K and V
   // tiles; lane L lands at (row L / CHR of the segment, physical chunk L % CHR) and so fetches the
   // logical chunk the swizzle places there.
-  int32_t seg_off[T::SEG_PER_WAVE];
+  uint32_t seg_off[T::SEG_PER_WAVE];  // byte offsets: unsigned 32-bit, added to a scalar base
 #pragma unroll
   for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
     const int rl = (wave * T::SEG_PER_WAVE + j) * T::ROWS_PER_SEG + lane / T::CHR;
-    seg_off[j] = rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3);
+    seg_off[j] = 2u * (uint32_t)(rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3));
   }
   auto load_tile = [&](int32_t i, int stage, int32_t& kp) {
     const uint16_t* src = tile_src(i, kp);
     if (src == nullptr) src = a.kv;  // unreadable page: any in-bounds bytes, the tile is masked
     uint16_t* kt = lds + stage * 2 * T::TILE;
+    const char* ksrc = reinterpret_cast<const char*>(src);
+    const char* vsrc = reinterpret_cast<const char*>(src + (int64_t)P * D);
 #pragma unroll
     for (int j = 0; j < T::SEG_PER_WAVE; ++j) {
       const int seg = wave * T::SEG_PER_WAVE + j;
-      g2lds16(src + seg_off[j], kt + seg * 512);
-      g2lds16(src + (int64_t)P * D + seg_off[j], kt + T::TILE + seg * 512);
+      g2lds16(ksrc + seg_off[j], kt + seg * 512);
+      g2lds16(vsrc + seg_off[j], kt + T::TILE + seg * 512);
     }
   };
 
@@ -295,8 +299,12 @@ static hipError_t launch_fwd_d(const AttnArgs& a, const FwdPlan& plan, uint16_t*
   const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
   {
     TimerScope ts_("k_attn_fwd", s);
-    hipLaunchKernelGGL(k_attn_fwd<D>, dim3(n_units), dim3(64 * FwdCfg<D>::NW), 0, s, a, plan.n_rb, plan.splits, o,
-                       lse, ws_o, ws_lse);
+    if (plan.nw == 8)
+      hipLaunchKernelGGL((k_attn_fwd<D, 8>), dim3(n_units), dim3(64 * 8), 0, s, a, plan.n_rb, plan.splits, o, lse,
+                         ws_o, ws_lse);
+    else
+      hipLaunchKernelGGL((k_attn_fwd<D, 4>), dim3(n_units), dim3(64 * 4), 0, s, a, plan.n_rb, plan.splits, o, lse,
+                         ws_o, ws_lse);
   }
   if (plan.splits > 1) {
     const int64_t work = rows_total * (D / 8);

@@ -169,20 +169,28 @@ static int32_t best_split(int64_t base_units, double tiles, double overhead, int
   return best;
 }
 
-// Row blocks of 128 rows, cut at selection-list boundaries (n_lists groups of C*G/n_lists rows).
-static int32_t row_blocks(int64_t rows, int32_t n_lists) {
-  const int64_t per_list = rows / n_lists;
-  return (int32_t)(n_lists * ((per_list + 127) / 128));
+// Waves per workgroup of the forward and dQ passes. Eight waves (256 rows) share each staged K/V
+// tile between twice the rows of four (128 rows, two workgroups per CU), halving the tile traffic
+// into LDS; four are kept when a selection list's rows would leave a 256-row block half empty.
+static int32_t pick_nw(int64_t rows, int32_t n_lists) {
+  return (n_lists == 1 || (rows / n_lists) % 256 == 0) ? 8 : 4;
+}
+
+// Row blocks of 32*nw rows, cut at selection-list boundaries (n_lists groups of C*G/n_lists rows).
+static int32_t row_blocks(int64_t rows, int32_t n_lists, int32_t nw) {
+  const int64_t per_list = rows / n_lists, rb = 32 * nw;
+  return (int32_t)(n_lists * ((per_list + rb - 1) / rb));
 }
 
 FwdPlan plan_fwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_kvh, int32_t C, int32_t G,
                  int32_t d) {
   FwdPlan p;
   const int64_t rows = (int64_t)C * G;
-  p.n_rb = row_blocks(rows, n_lists);  // 128 rows per workgroup, two workgroups per CU
+  p.nw = pick_nw(rows, n_lists);
+  p.n_rb = row_blocks(rows, n_lists, p.nw);
   const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
-  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 2);
+  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 8 / p.nw);
   p.ws_bytes = p.splits > 1 ? align256((size_t)p.splits * n_kvh * rows * d * 4) + align256((size_t)p.splits * n_kvh * rows * 4) : 0;
   return p;
 }
@@ -191,10 +199,11 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_
                  int32_t d) {
   BwdPlan p;
   const int64_t rows = (int64_t)C * G;
-  p.n_rb = row_blocks(rows, n_lists);  // 128 rows per workgroup, two workgroups per CU
+  p.dq_nw = pick_nw(rows, n_lists);
+  p.n_rb = row_blocks(rows, n_lists, p.dq_nw);
   const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
-  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 2);
+  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 8 / p.dq_nw);
   const int64_t n_kt = (int64_t)(n_list_pages + C / page) * (page / 32);
   p.n_ku = (int32_t)((n_kt + NKT_TILES_PER_WG - 1) / NKT_TILES_PER_WG);
   const int64_t n_blk = (rows + 31) / 32;

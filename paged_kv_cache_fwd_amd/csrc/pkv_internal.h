@@ -69,12 +69,14 @@ class TimerScope {
 
 // Launch-shape decisions, computed on the host from the shapes alone.
 struct FwdPlan {
-  int32_t n_rb;       // row blocks of 128 rows per KV head (n_lists x blocks per list)
+  int32_t nw;         // waves per workgroup: 8 (256-row blocks) or 4 (128-row blocks)
+  int32_t n_rb;       // row blocks per KV head (n_lists x blocks per list)
   int32_t splits;     // key-range splits (>1 needs the combine kernel and workspace)
   size_t ws_bytes;
 };
 struct BwdPlan {
-  int32_t n_rb;        // dQ pass: row blocks of 128 rows per KV head (n_lists x blocks per list)
+  int32_t dq_nw;       // dQ pass: waves per workgroup, as the forward's nw
+  int32_t n_rb;        // dQ pass: row blocks per KV head (n_lists x blocks per list)
   int32_t splits;      // dQ pass: key-range splits
   int32_t n_ku;        // dK/dV pass: key units of 256 keys per KV head
   int32_t row_splits;  // dK/dV pass: row-range splits (one per selection list when n_lists > 1)

@@ -151,10 +151,12 @@ def test_qpage_identical_lists_match_shared_list(pkv):
         torch.cuda.synchronize()
         res.append((o, lse, dq, dk))
         pool.free()
-    # 896 rows per query page = 7 row blocks: the same blocks, keys and splits in both calls.
-    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
-    assert torch.equal(res[0][2], res[1][2])
-    compare("dK shared vs per query page", res[1][3], res[0][3], 1e-5, rel=1e-5)
+    # Same keys for every row; the two calls may cut rows and key ranges differently (896 rows per
+    # query page take 128-row blocks, the shared list 256-row blocks), so compare to rounding.
+    compare("O shared vs per query page", host(res[1][0]), host(res[0][0]), 4e-3, rel=2e-3)
+    compare("LSE shared vs per query page", res[1][1].cpu().numpy(), res[0][1].cpu().numpy(), 1e-5, rel=1e-6)
+    compare("dQ shared vs per query page", host(res[1][2]), host(res[0][2]), 4e-3, rel=2e-3)
+    compare("dK shared vs per query page", res[1][3], res[0][3], 4e-3, rel=2e-3)  # via O's rounding in D
 
 
 def test_qpage_rejects_bad_list_counts(pkv):

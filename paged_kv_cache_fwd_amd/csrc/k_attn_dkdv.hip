@@ -249,16 +249,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
     }
+    // Operands of k-step ks + 1 are read from LDS while the MFMAs of k-step ks run, so the LDS
+    // latency is not exposed before every k-step.
+    bf16x8 opq[2], opd[2], opv[2][NKT];
+    auto fetch = [&](int ks, int b) {
+      const int off = toff<D>(l32, ks * 16 + 8 * lg);
+      opq[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + off));
+      opd[b] = as_bf16x8(*reinterpret_cast<const u32x4*>(dos + off));
+#pragma unroll
+      for (int j = 0; j < NKT; ++j) opv[b][j] = as_bf16x8(*reinterpret_cast<const u32x4*>(vmine + j * 32 * D + off));
+    };
+    fetch(0, 0);
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) {
-      const int off = toff<D>(l32, ks * 16 + 8 * lg);
-      const bf16x8 qa = as_bf16x8(*reinterpret_cast<const u32x4*>(qs + off));
-      const bf16x8 da = as_bf16x8(*reinterpret_cast<const u32x4*>(dos + off));
+      if (ks + 1 < T::KS) fetch(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int j = 0; j < NKT; ++j) {
-        const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(vmine + j * 32 * D + off));
-        sacc[j] = mfma32(qa, kreg[j][ks], sacc[j]);
-        pacc[j] = mfma32(da, vb, pacc[j]);
+        sacc[j] = mfma32(opq[ks & 1], kreg[j][ks], sacc[j]);
+        pacc[j] = mfma32(opd[ks & 1], opv[ks & 1][j], pacc[j]);
       }
     }
   };
@@ -302,18 +310,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto dv_dk = [&](int stage) {
     const uint16_t* qs = reinterpret_cast<const uint16_t*>(smem + stage * T::STAGE_BYTES);
     const uint16_t* dos = qs + T::TILE;
+    // The transposed operands of step (hf, dt) + 1 are read while the MFMAs of (hf, dt) run.
+    bf16x8 opo[2], opq[2];
+    auto fetch = [&](int st, int b) {
+      const int k_lo = (st / T::DT) * 16 + 4 * lg, dt = st % T::DT;
+      opo[b] = tr_operand<D>(dos, k_lo, k_lo + 8, dt * 32, lane);
+      opq[b] = tr_operand<D>(qs, k_lo, k_lo + 8, dt * 32, lane);
+    };
+    fetch(0, 0);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int k_lo = hf * 16 + 4 * lg;
+    for (int st = 0; st < 2 * T::DT; ++st) {
+      if (st + 1 < 2 * T::DT) fetch(st + 1, (st + 1) & 1);
+      const int hf = st / T::DT, dt = st % T::DT;
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) {
-        const bf16x8 dob = tr_operand<D>(dos, k_lo, k_lo + 8, dt * 32, lane);
-        const bf16x8 qb = tr_operand<D>(qs, k_lo, k_lo + 8, dt * 32, lane);
-#pragma unroll
-        for (int j = 0; j < NKT; ++j) {
-          mfma32_agpr(dv[j][dt], pb[j][hf], dob);
-          mfma32_agpr(dk[j][dt], dsb[j][hf], qb);
-        }
+      for (int j = 0; j < NKT; ++j) {
+        mfma32_agpr(dv[j][dt], pb[j][hf], opo[st & 1]);
+        mfma32_agpr(dk[j][dt], dsb[j][hf], opq[st & 1]);
       }
     }
   };

@@ -241,3 +241,35 @@ def test_host_tier_1m_matches_resident(pkv):
                                 page=wl.page, rows=rows, dtype=np.float32)
     compare("O rows", host(res["o"])[rows], ref["o"], ATOL_O)
     compare("dQ rows", host(res["dq"])[rows], ref["dq"], ATOL_GRAD)
+
+
+def test_paged_kv_copy_rejects_bad_arguments(pkv):
+    """Copies between pools are refused before anything is enqueued when shapes, ranges or the
+    gradient pages do not fit, and a valid copy moves exactly the requested physical pages."""
+    a = pkv.Pool(6, 64, 2, 64, grads=True)
+    b = pkv.Pool(6, 64, 2, 64, grads=False)
+    c = pkv.Pool(6, 64, 1, 64, grads=True)
+    h = pkv.Pool(6, 64, 2, 64, grads=True, host_tier=True, host_grads=True)
+    bt = i32(np.arange(6))
+    k = torch.randn(6 * 64, 2, 64, device="cuda").to(torch.bfloat16)
+    a.append(bt, 0, k, k)
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_kv_copy(a, c, pkv.PKV_COPY_KV)           # head count differs
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_kv_copy(a, b, pkv.PKV_COPY_GRAD)         # destination has no gradient pages
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_kv_copy(a, h, pkv.PKV_COPY_KV, 4, 3)     # pages [4, 7) outside both pools
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_kv_copy(a, a, pkv.PKV_COPY_KV)           # same pool
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_kv_copy(a, h, 8)                         # unknown bit
+    pkv.paged_kv_copy(a, h, pkv.PKV_COPY_KV, 2, 3)         # physical pages 2..4 only
+    torch.cuda.synchronize()
+    got = h.export(pkv.PKV_K, bt, 0, 6).cpu()
+    want = a.export(pkv.PKV_K, bt, 0, 6).cpu()
+    assert torch.equal(got[2 * 64:5 * 64], want[2 * 64:5 * 64])
+    assert not torch.any(got[:2 * 64].float()) and not torch.any(got[5 * 64:].float())
+    with pytest.raises(ValueError):
+        pkv.chunk_attn_fwd(a, bt, 2, k[:128].contiguous(), 0.1, sel=i32(np.zeros((2, 1, 1, 1))))
+    for p in (a, b, c, h):
+        p.free()

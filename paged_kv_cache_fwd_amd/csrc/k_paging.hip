@@ -57,16 +57,31 @@ __global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ 
 }
 
 // Zero the gradient blocks of logical pages [lp0, lp0 + n_lp) (bt == NULL: physical = logical).
+// Grid (x: 32 KiB pieces of a page, y: pages, striding when there are more than gridDim.y): one
+// table lookup per workgroup, 8 16-byte stores per thread.
+constexpr int kZeroPerThread = 8;
 __global__ __launch_bounds__(256) void k_zero_grad(float* __restrict__ grad, int32_t n_pool, int32_t P, int32_t H,
                                                    int32_t D, const int32_t* __restrict__ bt, int32_t n_bt,
                                                    int32_t lp0, int32_t n_lp, int32_t* err) {
-  const int64_t per_page = (int64_t)H * 2 * P * D / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= per_page * n_lp) return;
-  const int32_t lp = lp0 + (int32_t)(idx / per_page);
-  const int32_t phys = bt ? phys_page(bt, n_bt, n_pool, lp, err) : lp;
-  if (phys < 0 || phys >= n_pool) return;
-  reinterpret_cast<f32x4*>(grad)[(int64_t)phys * per_page + idx % per_page] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int64_t per_page = (int64_t)H * 2 * P * D / 4;  // 16-byte chunks per page
+  const int64_t i0 = (int64_t)blockIdx.x * kZeroPerThread * 256 + threadIdx.x;
+  for (int32_t r = blockIdx.y; r < n_lp; r += gridDim.y) {
+    const int32_t lp = lp0 + r;
+    const int32_t phys = bt ? phys_page(bt, n_bt, n_pool, lp, err) : lp;
+    if (phys < 0 || phys >= n_pool) continue;
+    f32x4* base = reinterpret_cast<f32x4*>(grad) + (int64_t)phys * per_page;
+#pragma unroll
+    for (int u = 0; u < kZeroPerThread; ++u) {
+      const int64_t i = i0 + (int64_t)u * 256;
+      if (i < per_page) base[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+static dim3 zero_grid(const pkv_pool& pool, int32_t n_pages) {
+  const int64_t per_page = (int64_t)pool.h_kv * 2 * pool.page * pool.d / 4;
+  return dim3((unsigned)((per_page + kZeroPerThread * 256 - 1) / (kZeroPerThread * 256)),
+              (unsigned)(n_pages < 65535 ? n_pages : 65535));
 }
 
 // Export K/V (bf16) in logical order: dst[(lp*P + t)*H + g][d].
@@ -223,12 +238,9 @@ hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, 
   const int32_t first_new = (pos0 + P - 1) / P;           // first page starting at or after pos0
   const int32_t end_new = (pos0 + n + P - 1) / P;         // pages starting before pos0 + n
   if (pool.grad && end_new > first_new) {
-    const int64_t work = (int64_t)(end_new - first_new) * H * 2 * P * D / 4;
-    {
-      TimerScope ts_("k_zero_grad", s);
-      hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D, bt,
-                         n_bt, first_new, end_new - first_new, pool.err);
-    }
+    TimerScope ts_("k_zero_grad", s);
+    hipLaunchKernelGGL(k_zero_grad, zero_grid(pool, end_new - first_new), dim3(256), 0, s, pool.grad, pool.n_pages, P,
+                       H, D, bt, n_bt, first_new, end_new - first_new, pool.err);
   }
   const int64_t chunks = (int64_t)2 * n * H * (D / 8);
   {
@@ -252,11 +264,10 @@ hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, 
 
 hipError_t launch_zero_grad(const pkv_pool& pool, const int32_t* bt, int32_t first_page, int32_t n_pages,
                             hipStream_t s) {
-  const int64_t work = (int64_t)n_pages * pool.h_kv * 2 * pool.page * pool.d / 4;
-  if (work == 0) return hipSuccess;
+  if (n_pages <= 0) return hipSuccess;
   {
     TimerScope ts_("k_zero_grad", s);
-    hipLaunchKernelGGL(k_zero_grad, dim3(grid_for(work)), dim3(256), 0, s, pool.grad, pool.n_pages, pool.page,
+    hipLaunchKernelGGL(k_zero_grad, zero_grid(pool, n_pages), dim3(256), 0, s, pool.grad, pool.n_pages, pool.page,
                        pool.h_kv, pool.d, bt, first_page + n_pages, first_page, n_pages, pool.err);
   }
   return hipGetLastError();

@@ -505,6 +505,23 @@ def main():
         stats[name] = {"median_ms": round(per[len(per) // 2], 4), "min_ms": round(per[0], 4)}
         return dt / args.steps * 1e3, kt
 
+    def select_b2b(n=50, copy_gbps=None):
+        """page_topk_select alone, n calls back to back: steady-state per-call time and GB/s."""
+        for _ in range(3):
+            pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        b = C * H_q * d * 2 + (n_prior - n_local) * H_kv * d * 4
+        return {"ms_per_call": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b,
+                "pct_hbm_peak": round(100.0 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "pct_streaming_copy": None if copy_gbps is None else round(100.0 * b / (ms * 1e-3) / 1e9 / copy_gbps, 2)}
+
     pd = pairs_dense(C, q0)
     flop_dense = 14.0 * d * H_q * pd
     if args.only == "topk":
@@ -512,7 +529,8 @@ def main():
         ms_topk, kt_topk = run(step_topk, "topk256k")
         print(json.dumps({"workload": "topk256k", "ms_per_step": round(ms_topk, 4),
                           "TFLOP/s": round(14.0 * d * H_q * ps / (ms_topk * 1e-3) / 1e12, 2),
-                          "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}), flush=True)
+                          "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()},
+                          "select_back_to_back": select_b2b()}), flush=True)
         pool.free()
         return
     if args.only == "qpage":
@@ -585,23 +603,6 @@ def main():
         roofline = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": None, "traffic": None, "avg_launch_ms": round(avg_ms, 4)}
 
-    def select_b2b(n=50):
-        """page_topk_select alone, n calls back to back: steady-state per-call time and GB/s."""
-        for _ in range(3):
-            pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(n):
-            pkv.page_topk_select(pool, bt, n_prior, q, top_k, n_local, sel=sel, ws=ws_t)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / n
-        b = C * H_q * d * 2 + (n_prior - n_local) * H_kv * d * 4
-        return {"ms_per_call": round(ms, 4), "GBps": round(b / (ms * 1e-3) / 1e9, 1), "bytes": b,
-                "pct_hbm_peak": round(100.0 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                "pct_streaming_copy": round(100.0 * b / (ms * 1e-3) / 1e9 / copy_gbps, 2)}
-
     topk = None
     if not args.no_topk:
         ps = pairs_sparse(C, n_sel, P)
@@ -618,7 +619,7 @@ def main():
                 "step_speedup_vs_dense": round(ms_dense / ms_topk, 2),
                 "select_ms": round(sel_ms, 4),
                 "select_GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1) if sel_ms > 0 else None,
-                "select_back_to_back": select_b2b(),
+                "select_back_to_back": select_b2b(copy_gbps=copy_gbps),
                 "cold_cache": cold(step_topk, 10),
                 "fwd_ms": split_ms(kt_topk)[0], "bwd_ms": split_ms(kt_topk)[1],
                 "step_stats": stats.get("topk256k"),

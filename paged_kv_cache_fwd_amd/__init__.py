@@ -114,9 +114,21 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _need(t: torch.Tensor, dtype, name: str):
+def _need(t: torch.Tensor, dtype, name: str, shape=None):
+    """The library sees only pointers, so every tensor is checked here: dtype, device, layout and,
+    where the call fixes it, the exact shape (a wrong shape would make a kernel read past it)."""
     if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype:
         raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor, got {t.dtype} on {t.device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_q(pool: "Pool", q: torch.Tensor):
+    """q is [C][H_q][d] bf16 with d the pool's head dimension; returns (C, H_q)."""
+    _need(q, torch.bfloat16, "q")
+    if q.dim() != 3 or q.shape[2] != pool.d:
+        raise ValueError(f"q must be [C][H_q][{pool.d}], got {tuple(q.shape)}")
+    return q.shape[0], q.shape[1]
 
 
 class Pool:
@@ -145,9 +157,9 @@ class Pool:
 
     def append(self, bt: torch.Tensor, pos0: int, k: torch.Tensor, v: torch.Tensor, stream=None):
         _need(bt, torch.int32, "bt")
-        _need(k, torch.bfloat16, "k")
-        _need(v, torch.bfloat16, "v")
-        n = k.shape[0]
+        n = k.shape[0] if k.dim() == 3 else -1
+        _need(k, torch.bfloat16, "k", (n, self.h_kv, self.d))
+        _need(v, torch.bfloat16, "v", (n, self.h_kv, self.d))
         _check(load().paged_kv_append(self.handle, _ptr(bt), bt.numel(), pos0, n, _ptr(k), _ptr(v), _stream(stream)))
 
     def zero_grad(self, bt: Optional[torch.Tensor] = None, n_pages: int = 0, stream=None):
@@ -185,8 +197,7 @@ def page_topk_select(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor
     contiguous and large enough; the result is a view of its first elements."""
     lib = load()
     _need(bt, torch.int32, "bt")
-    _need(q, torch.bfloat16, "q")
-    C, H_q, _ = q.shape
+    C, H_q = _need_q(pool, q)
     n_cand = max(n_prior - n_local, 0)
     n_sel = min(top_k, n_cand) + (n_prior - n_cand)
     n_lists = C // pool.page if per_query_page else 1
@@ -216,16 +227,16 @@ def chunk_attn_bwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C:
     return load().chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
 
 
-def _sel_shape(sel: Optional[torch.Tensor]):
-    """(n_sel, n_lists) of a selection: None -> dense; [H_kv][n_sel]; [H_kv][C/page][n_sel]."""
+def _sel_shape(sel: Optional[torch.Tensor], pool: Pool):
+    """(n_sel, n_lists) of a selection: None -> dense; [H_kv][n_sel]; [H_kv][C/page][n_sel]. The
+    kernels index it by absolute KV head, so it holds a row per KV head of the pool."""
     if sel is None:
         return -1, 1
     _need(sel, torch.int32, "sel")
-    if sel.dim() == 2:
-        return sel.shape[1], 1
-    if sel.dim() == 3:
-        return sel.shape[2], sel.shape[1]
-    raise ValueError(f"sel must be [H_kv][n_sel] or [H_kv][C/page][n_sel], got shape {tuple(sel.shape)}")
+    if sel.dim() not in (2, 3) or sel.shape[0] != pool.h_kv:
+        raise ValueError(f"sel must be [{pool.h_kv}][n_sel] or [{pool.h_kv}][C/page][n_sel], "
+                         f"got shape {tuple(sel.shape)}")
+    return (sel.shape[1], 1) if sel.dim() == 2 else (sel.shape[2], sel.shape[1])
 
 
 def chunk_attn_fwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, scale: float,
@@ -236,14 +247,15 @@ def chunk_attn_fwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
     [H_kv][n_sel] (one list per KV head) or [H_kv][C/page][n_sel] (one list per query page)."""
     lib = load()
     _need(bt, torch.int32, "bt")
-    _need(q, torch.bfloat16, "q")
-    C, H_q, d = q.shape
+    C, H_q = _need_q(pool, q)
     n_kvh = pool.h_kv - kvh0 if n_kvh is None else n_kvh
-    n_sel, n_lists = _sel_shape(sel)
+    n_sel, n_lists = _sel_shape(sel, pool)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((H_q, C), dtype=torch.float32, device=q.device)
+    _need(o, torch.bfloat16, "o", q.shape)
+    _need(lse, torch.float32, "lse", (H_q, C))
     nb = lib.chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
     ws = _ws(nb, q.device, ws)
     _check(lib.chunk_attn_fwd(pool.handle, _ptr(bt), bt.numel(), n_prior, _sel_ptr(sel, bt), max(n_sel, 0), n_lists,
@@ -260,16 +272,18 @@ def chunk_attn_bwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
     """Backward of one chunk; returns dq. dK/dV are added into the gradient pages of gpool."""
     lib = load()
     _need(bt, torch.int32, "bt")
-    for t, nm in ((q, "q"), (o, "o"), (dout, "dout")):
-        _need(t, torch.bfloat16, nm)
-    _need(lse, torch.float32, "lse")
-    C, H_q, d = q.shape
+    C, H_q = _need_q(pool, q)
+    for t, nm in ((o, "o"), (dout, "dout")):
+        _need(t, torch.bfloat16, nm, q.shape)
+    _need(lse, torch.float32, "lse", (H_q, C))
     n_kvh = pool.h_kv - kvh0 if n_kvh is None else n_kvh
-    n_sel, n_lists = _sel_shape(sel)
+    n_sel, n_lists = _sel_shape(sel, pool)
     gpool = pool if gpool is None else gpool
     gbt = bt if gbt is None else gbt
+    _need(gbt, torch.int32, "gbt")
     if dq is None:
         dq = torch.empty_like(q)
+    _need(dq, torch.bfloat16, "dq", q.shape)
     nb = lib.chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
     ws = _ws(nb, q.device, ws)
     _check(lib.chunk_attn_bwd(pool.handle, _ptr(bt), bt.numel(), gpool.handle, _ptr(gbt), gbt.numel(), n_prior,
@@ -285,7 +299,7 @@ def paged_kv_gather(host: Pool, dev: Pool, host_bt: torch.Tensor, sel_row: torch
     dev_bt_out[sel_row[i]] = dst_pages[i]."""
     _need(host_bt, torch.int32, "host_bt")
     _need(sel_row, torch.int32, "sel_row")
-    _need(dst_pages, torch.int32, "dst_pages")
+    _need(dst_pages, torch.int32, "dst_pages", sel_row.shape)
     if dev_bt_out is not None:
         _need(dev_bt_out, torch.int32, "dev_bt_out")
     _check(load().paged_kv_gather(host.handle, dev.handle, _ptr(host_bt), host_bt.numel(), _ptr(sel_row),

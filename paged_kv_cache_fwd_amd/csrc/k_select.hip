@@ -27,9 +27,14 @@ __global__ __launch_bounds__(256) void k_qsum_part(const uint16_t* __restrict__ 
   const int32_t b = (int32_t)((idx / D) % nb);
   const int32_t h = (int32_t)(idx / ((int64_t)D * nb));
   const uint16_t* src = q + ((int64_t)(64 * b) * H_q + h) * D + j;
+  // All 64 loads are issued before the first add, so each thread waits on memory once (the kernel
+  // is latency-bound at this size).
+  uint16_t x[64];
+#pragma unroll
+  for (int32_t t = 0; t < 64; ++t) x[t] = src[(int64_t)t * H_q * D];
   float acc = 0.0f;
-#pragma unroll 16
-  for (int32_t t = 0; t < 64; ++t) acc = __fadd_rn(acc, bf16_to_f32(src[(int64_t)t * H_q * D]));
+#pragma unroll
+  for (int32_t t = 0; t < 64; ++t) acc = __fadd_rn(acc, bf16_to_f32(x[t]));
   part[idx] = acc;
 }
 

@@ -238,3 +238,72 @@ def test_topk_no_fma_and_ties(pkv):
         assert got.tolist() == [expect], (top_k, got)
     torch.cuda.synchronize()
     pool.free()
+
+
+def _tied_pool(pkv, n_pages, h_kv, seed):
+    """Pages whose keys are one constant per (page, head) on dimension 0, drawn from five
+    bf16-exact values, so scores take five values and ties fill whole id ranges."""
+    P, d = 64, 64
+    rng = np.random.default_rng(seed)
+    vals = np.array([-0.5, 0.25, 0.5, 0.75, 1.0], np.float32)
+    pick = vals[rng.integers(0, len(vals), (n_pages, h_kv))]
+    K = np.zeros((n_pages * P, h_kv, d), np.float32)
+    K[:, :, 0] = np.repeat(pick, P, axis=0)
+    K = synth.bf16_round(K)
+    Q = np.zeros((64, h_kv, d), np.float32)
+    Q[0, :, 0] = 1.0
+    Q = synth.bf16_round(Q)
+    perm = rng.permutation(n_pages).astype(np.int32)
+    pool = pkv.Pool(n_pages, P, h_kv, d, grads=False)
+    bt = i32(perm)
+    per = 4096
+    for p0 in range(0, n_pages, per):
+        n = min(per, n_pages - p0)
+        kk = K[p0 * P:(p0 + n) * P]
+        pool.append(bt, p0 * P, t16(kk), t16(np.zeros_like(kk)))
+    return pool, bt, K, Q, P
+
+
+@pytest.mark.parametrize("n_pages", [2600, 16400])
+def test_topk_ties_across_chunks(pkv, n_pages):
+    """Five distinct scores over thousands of candidates: the K-th page's score is tied with
+    hundreds of others spread over several 1024-id compaction chunks; the lowest ids must win.
+    16400 candidates exceed what the selection kernel stages on chip."""
+    pool, bt, K, Q, P = _tied_pool(pkv, n_pages, 2, seed=n_pages)
+    for top_k, n_local in ((1000, 4), (1500, 0), (7, 0), (n_pages - 5, 4), (n_pages // 2, 16)):
+        say(f"  n_pages={n_pages} top_k={top_k} n_local={n_local}")
+        want, sc, _ = oracle.topk_pages(Q, K, P, 2, n_pages, top_k, n_local)
+        assert len(np.unique(sc)) <= 5
+        got = pkv.page_topk_select(pool, bt, n_pages, t16(Q), top_k, n_local).cpu().numpy()
+        assert np.array_equal(got, want), (top_k, n_local)
+    pool.check()
+    torch.cuda.synchronize()
+    pool.free()
+
+
+def test_binding_rejects_mis_shaped_tensors(pkv):
+    """The library sees only pointers; the binding refuses tensors whose shape does not match the
+    pool or the call before anything is launched (a float32 array passed as bf16 bits doubles d)."""
+    pool = pkv.Pool(4, 64, 2, 64)
+    bt = i32(np.arange(4))
+    good_q = torch.zeros((64, 4, 64), dtype=torch.bfloat16, device="cuda")
+    bad_q = torch.zeros((64, 4, 128), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((128, 2, 64), dtype=torch.bfloat16, device="cuda")
+    pool.append(bt, 0, kv, kv)
+    with pytest.raises(ValueError):
+        pool.append(bt, 128, torch.zeros((64, 2, 128), dtype=torch.bfloat16, device="cuda"), kv[:64])
+    with pytest.raises(ValueError):
+        pkv.page_topk_select(pool, bt, 1, bad_q, 1, 0)
+    with pytest.raises(ValueError):
+        pkv.chunk_attn_fwd(pool, bt, 1, bad_q, 0.125)
+    with pytest.raises(ValueError):
+        pkv.chunk_attn_fwd(pool, bt, 1, good_q, 0.125, sel=torch.zeros((1, 1), dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        pkv.chunk_attn_fwd(pool, bt, 1, good_q, 0.125, lse=torch.zeros((4, 32), dtype=torch.float32, device="cuda"))
+    o, lse = pkv.chunk_attn_fwd(pool, bt, 1, good_q, 0.125)
+    with pytest.raises(ValueError):
+        pkv.chunk_attn_bwd(pool, bt, 1, good_q, o, good_q[:32].contiguous(), lse, 0.125)
+    with pytest.raises(ValueError):
+        pkv.chunk_attn_bwd(pool, bt, 1, good_q, o, good_q, lse.t().contiguous(), 0.125)
+    torch.cuda.synchronize()
+    pool.free()

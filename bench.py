@@ -350,7 +350,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-tokens", type=int, default=256, help="chunk tokens in the CPU-oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=1024, help="chunk tokens in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--no-host1m", action="store_true", help="skip the 1M-token host-tier workload")
@@ -409,7 +409,9 @@ def main():
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s; appending prior pages")
     pool = pkv.Pool(n_pages, P, H_kv, d, grads=True)
     bt = torch.from_numpy(bt_np).to(dev)
-    per = 256
+    # One append over all prior pages: the bulk datapoint of the append, representative and
+    # gradient-zeroing kernels (268 MB of keys in one launch, not launch-latency-sized pieces).
+    per = n_prior
     kv_pieces = [(p0, t16(k_np[p0 * P:(p0 + min(per, n_prior - p0)) * P]),
                   t16(v_np[p0 * P:(p0 + min(per, n_prior - p0)) * P])) for p0 in range(0, n_prior, per)]
     # The pool is filled twice with the same pages: the first pass is the first touch of freshly
@@ -424,7 +426,7 @@ def main():
     pkv.timing_enable(False)
     kt_fill = pkv.timing_collect()
     del kv_pieces
-    # Bulk append of the prior pages, 256 pages per call: K/V read and written, new gradient pages
+    # Bulk append of the prior pages in one call: K/V read and written, new gradient pages
     # zeroed, and one representative per (page, head) from the page's keys.
     pg = n_prior * H_kv * P * d
     fill = {"pages": n_prior, "calls": kt_fill.get("k_append", (0, 0))[0]}

@@ -34,26 +34,36 @@ __global__ __launch_bounds__(256) void k_append(uint16_t* __restrict__ kv, int32
 
 // Representative key of each page completed by an append: float32 sequential sum over the page's
 // tokens in token order starting from +0.0, times 1/P (exact: P is a power of two).
+// One wave per (logical page, KV head) block, four blocks per workgroup. Lane l owns key columns
+// 2l and 2l+1: it loads its 4-byte column pair from every token row (a wave's load covers one
+// whole 256-byte row), all P loads issued before the first add, then runs the two columns' sums
+// side by side. No LDS and no barrier; each block is read once, straight from the pool.
+template <int P>
 __global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ kv, float* __restrict__ rep,
-                                                   int32_t n_pool, int32_t P, int32_t H, int32_t D,
+                                                   int32_t n_pool, int32_t H, int32_t D,
                                                    const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
                                                    int32_t n_lp, int32_t* err) {
-  // One workgroup per (logical page, KV head): the P x D key block is staged in LDS with coalesced
-  // 16-byte loads, then thread j adds column j in token order.
-  __shared__ __attribute__((aligned(16))) uint16_t kb[128 * 128];
-  const int32_t g = blockIdx.x % H;
-  const int32_t lp = lp0 + blockIdx.x / H;
+  const int32_t lane = threadIdx.x & 63;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blk >= (int64_t)n_lp * H || 2 * lane >= D) return;
+  const int32_t g = (int32_t)(blk % H);
+  const int32_t lp = lp0 + (int32_t)(blk / H);
   const int32_t phys = phys_page(bt, n_bt, n_pool, lp, err);
   if (phys < 0) return;
-  const uint16_t* kp = kv + (((int64_t)phys * H + g) * 2) * P * D;
-  for (int32_t i = threadIdx.x; i < P * D / 8; i += 256)
-    reinterpret_cast<u32x4*>(kb)[i] = reinterpret_cast<const u32x4*>(kp)[i];
-  __syncthreads();
-  for (int32_t j = threadIdx.x; j < D; j += 256) {
-    float acc = 0.0f;
-    for (int32_t t = 0; t < P; ++t) acc = __fadd_rn(acc, bf16_to_f32(kb[t * D + j]));
-    rep[((int64_t)phys * H + g) * D + j] = __fmul_rn(acc, 1.0f / (float)P);
+  const uint32_t* kp = reinterpret_cast<const uint32_t*>(kv + (((int64_t)phys * H + g) * 2) * P * D) + lane;
+  const int32_t row = D / 2;  // 4-byte words per token row
+  uint32_t x[P];
+#pragma unroll
+  for (int32_t t = 0; t < P; ++t) x[t] = kp[t * row];
+  float a0 = 0.0f, a1 = 0.0f;  // columns 2*lane (low half-word) and 2*lane + 1 (high half-word)
+#pragma unroll
+  for (int32_t t = 0; t < P; ++t) {
+    a0 = __fadd_rn(a0, __uint_as_float(x[t] << 16));
+    a1 = __fadd_rn(a1, __uint_as_float(x[t] & 0xFFFF0000u));
   }
+  float* r = rep + ((int64_t)phys * H + g) * D + 2 * lane;
+  r[0] = __fmul_rn(a0, 1.0f / (float)P);
+  r[1] = __fmul_rn(a1, 1.0f / (float)P);
 }
 
 // Zero the gradient blocks of logical pages [lp0, lp0 + n_lp) (bt == NULL: physical = logical).
@@ -255,8 +265,13 @@ hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, 
   if (lp_b > lp_a) {
     {
       TimerScope ts_("k_page_reps", s);
-      hipLaunchKernelGGL(k_page_reps, dim3((unsigned)((lp_b - lp_a) * H)), dim3(256), 0, s, pool.kv, pool.rep,
-                         pool.n_pages, P, H, D, bt, n_bt, lp_a, lp_b - lp_a, pool.err);
+      const dim3 grid((unsigned)(((int64_t)(lp_b - lp_a) * H + 3) / 4));
+      if (P == 128)
+        hipLaunchKernelGGL(k_page_reps<128>, grid, dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, H, D, bt, n_bt,
+                           lp_a, lp_b - lp_a, pool.err);
+      else
+        hipLaunchKernelGGL(k_page_reps<64>, grid, dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, H, D, bt, n_bt,
+                           lp_a, lp_b - lp_a, pool.err);
     }
   }
   return hipGetLastError();

@@ -307,3 +307,26 @@ def test_binding_rejects_mis_shaped_tensors(pkv):
         pkv.chunk_attn_bwd(pool, bt, 1, good_q, o, good_q, lse.t().contiguous(), 0.125)
     torch.cuda.synchronize()
     pool.free()
+
+
+@pytest.mark.parametrize("page,d", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_page_reps_ragged_appends(pkv, page, d):
+    """Representatives written by appends that start and end inside pages, with 3 KV heads (so the
+    last workgroup of four (page, head) blocks is partly empty), equal the oracle's fixed-order
+    float32 key sums times 1/page, bit for bit; pages not yet full have no representative."""
+    wl = synth.Workload("reps", 6, 3, d, page, page * 11, page, (0,), offset_std=0.5, seed=4)
+    bt_np = synth.page_permutation(wl)
+    pool = pkv.Pool(wl.n_pages, page, wl.h_kv, d, grads=True)
+    bt = i32(bt_np)
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    cuts = [0, page // 2 + 3, 3 * page + 1, 3 * page + 5, 9 * page + page // 4]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        pool.append(bt, a, t16(k[a:b]), t16(v[a:b]))
+    full = cuts[-1] // page
+    got = pool.export(pkv.PKV_REP, bt, 0, full).cpu().numpy()
+    torch.cuda.synchronize()
+    pool.check()
+    want = oracle.page_reps(oracle.page_key_sums(k[:full * page], page), page)
+    assert got.shape == want.shape
+    assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
+    pool.free()

@@ -330,3 +330,27 @@ def test_page_reps_ragged_appends(pkv, page, d):
     assert got.shape == want.shape
     assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
     pool.free()
+
+
+@pytest.mark.parametrize("page,d", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_page_reps_bulk_append(pkv, page, d):
+    """An append that completes over a thousand (page, head) blocks at once, starting inside a
+    page and ending inside another, with 3 KV heads so the last workgroup is partly filled:
+    representatives equal the oracle's bit for bit."""
+    n_pages = 352
+    wl = synth.Workload("reps_bulk", 6, 3, d, page, page * n_pages, page, (0,), offset_std=0.5, seed=6)
+    bt_np = synth.page_permutation(wl)
+    pool = pkv.Pool(n_pages, page, wl.h_kv, d, grads=True)
+    bt = i32(bt_np)
+    k, v = synth.kv_tokens(wl, 0, n_pages)
+    a, b = page // 3, (n_pages - 1) * page + page // 2
+    pool.append(bt, 0, t16(k[:a]), t16(v[:a]))
+    pool.append(bt, a, t16(k[a:b]), t16(v[a:b]))
+    assert (b // page - 1) * wl.h_kv >= 1024
+    full = b // page
+    got = pool.export(pkv.PKV_REP, bt, 0, full).cpu().numpy()
+    torch.cuda.synchronize()
+    pool.check()
+    want = oracle.page_reps(oracle.page_key_sums(k[:full * page], page), page)
+    assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
+    pool.free()

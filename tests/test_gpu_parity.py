@@ -111,6 +111,21 @@ def test_mid_page64_d64(pkv):
     _check_against_oracle(wl, outs, dk, dv, wl.page)
 
 
+@pytest.mark.parametrize("name,G,h_kv,C,n_chunks,d,page", [
+    ("no GQA (G=1), 128-row chunks in 256-row blocks", 1, 2, 128, 3, 128, 128),
+    ("one-page chunks (C = page = 64), six chunks", 4, 1, 64, 6, 64, 64),
+    ("one-page chunks (C = page = 128)", 2, 2, 128, 4, 128, 128),
+    ("wide group (G=16, one KV head)", 16, 1, 128, 3, 128, 128),
+])
+def test_degenerate_shapes_dense(pkv, name, G, h_kv, C, n_chunks, d, page):
+    """Chunk sizes and group sizes at the edges of the tiling, every chunk checked against the
+    oracle and the gradient pages accumulated over all chunks."""
+    wl = _mid(seed=11, G=G, h_kv=h_kv, C=C, chunks=tuple(range(n_chunks)), d=d, page=page)
+    say(f"case {name}")
+    outs, dk, dv = _run_chunks(pkv, wl, synth.page_permutation(wl))
+    _check_against_oracle(wl, outs, dk, dv, wl.page)
+
+
 def test_head_subsets_match_full_call(pkv):
     """Running KV heads one at a time (kvh0/n_kvh) gives the same bits as one call over all heads."""
     wl = _mid(seed=5, chunks=(0, 1))

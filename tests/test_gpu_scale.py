@@ -1,7 +1,7 @@
-"""GPU parity at full size (256K context, 28/4 heads, d=128, page 128), in the launch configuration
-the benchmark times: sampled rows against the oracle computed row by row in float32, the complete
-sparse step against the oracle, gradient-sum invariants that hold at any size, and bit-exact page
-selection."""
+"""GPU parity at full size (256K context and the 32K chunk loop, 28/4 heads, d=128, page 128), in
+the launch configuration the benchmark times: sampled rows against the oracle computed row by row
+in float32, the complete sparse step against the oracle, gradient-sum invariants that hold at any
+size, and bit-exact page selection."""
 import numpy as np
 import pytest
 
@@ -140,3 +140,56 @@ def test_qpage256k_selection_and_full_sparse_step(pkv, big):
         compare(f"dV head {g}", dv[keys, g], ref["dv"][g], ATOL_GRAD)
         untouched = np.setdiff1d(np.arange(wl.context), keys)
         assert np.all(dk[untouched, g] == 0) and np.all(dv[untouched, g] == 0)
+
+
+def test_qwen32k_all_chunks_sampled_rows_last_page_and_invariants(pkv):
+    """The 32K dense workload at full size (28/4 heads, d=128, 8 chunks of 4096, page 128, shuffled
+    table), run as the chunk loop runs it: each chunk appended, then its forward and backward, dK/dV
+    accumulated in the gradient pages over all chunks. Sampled rows of every chunk against the
+    oracle; the last page's accumulated dK/dV element by element (only the last chunk's final
+    128 rows see its keys); gradient-sum invariants over all chunks."""
+    wl = synth.WORKLOADS["qwen32k"]
+    C, P, G = wl.chunk, wl.page, wl.group
+    bt_np = synth.page_permutation(wl)
+    pool = pkv.Pool(wl.n_pages, P, wl.h_kv, wl.d, grads=True)
+    bt = i32(bt_np)
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    rows = _sample_rows(C)
+    do_sum = np.zeros((wl.h_kv, wl.d))
+    for c in wl.chunks:
+        q0, n_prior = wl.q0(c), wl.n_prior(c)
+        pool.append(bt, q0, t16(k[q0:q0 + C]), t16(v[q0:q0 + C]))
+        q, do = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+        qt, dot = t16(q), t16(do)
+        o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, qt, wl.scale)
+        dq = pkv.chunk_attn_bwd(pool, bt, n_prior, qt, o, dot, lse, wl.scale)
+        say(f"qwen32k chunk {c} (q0 = {q0}): oracle on {len(rows)} sampled tokens x {wl.h_q} heads (float32)")
+        ref = oracle.chunk_backward(q, k, v, do, q0, wl.scale, page=P, rows=rows, dtype=np.float32)
+        compare("O rows", host(o)[rows], ref["o"], ATOL_O)
+        compare("LSE rows", lse.cpu().numpy()[:, rows], ref["lse"], ATOL_LSE, rel=1e-5)
+        compare("dQ rows", host(dq)[rows], ref["dq"], ATOL_GRAD)
+        dof = synth.bf16_widen(do).astype(np.float64)
+        for g in range(wl.h_kv):
+            do_sum[g] += dof[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+    dk = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    dv = pool.export(pkv.PKV_DV, bt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    pool.check()
+    c = wl.chunks[-1]
+    q, do = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+    say("qwen32k: last page's accumulated gradients from the oracle over the last 128 rows")
+    ref = oracle.chunk_backward(q, k, v, do, wl.q0(c), wl.scale, page=P, rows=np.arange(C - P, C),
+                                dtype=np.float32)
+    first_last = wl.context - P
+    for g in range(wl.h_kv):
+        keys = ref["keys"][g]
+        last = keys >= first_last
+        assert int(last.sum()) == P
+        compare(f"dK last page, head {g}", dk[keys[last], g], ref["dk"][g][last], ATOL_GRAD)
+        compare(f"dV last page, head {g}", dv[keys[last], g], ref["dv"][g][last], ATOL_GRAD)
+    for g in range(wl.h_kv):
+        err = np.linalg.norm(dv[:, g].sum(axis=0) - do_sum[g]) / np.linalg.norm(do_sum[g])
+        skew = np.linalg.norm(dk[:, g].sum(axis=0)) / np.abs(dk[:, g]).sum(axis=0).mean()
+        say(f"  head {g}: |sum dV - sum dO|/|sum dO| = {err:.2e}; |sum dK| / mean sum|dK| = {skew:.2e}")
+        assert err < 1e-2 and skew < 1e-2
+    pool.free()

@@ -507,6 +507,31 @@ def main():
         stats[name] = {"median_ms": round(per[len(per) // 2], 4), "min_ms": round(per[0], 4)}
         return dt / args.steps * 1e3, kt
 
+    def graph_ms(step):
+        """The step recorded once into a HIP graph (torch.cuda.CUDAGraph) and replayed back to back:
+        per-step time without host launch cost or gaps between the step's kernels."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        for _ in range(args.warmup):
+            gr.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        pool.check()
+        del gr
+        return round(e0.elapsed_time(e1) / args.steps, 4)
+
     def select_b2b(n=50, copy_gbps=None):
         """page_topk_select alone, n calls back to back: steady-state per-call time and GB/s."""
         for _ in range(3):
@@ -625,6 +650,7 @@ def main():
                 "cold_cache": cold(step_topk, 10),
                 "fwd_ms": split_ms(kt_topk)[0], "bwd_ms": split_ms(kt_topk)[1],
                 "step_stats": stats.get("topk256k"),
+                "graph_ms_per_step": graph_ms(step_topk),
                 "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_topk.items()}}
 
     qpage = None
@@ -657,7 +683,8 @@ def main():
                  "fwd_ms": split_ms(kt_local)[0], "bwd_ms": split_ms(kt_local)[1],
                  "mixed_pair_ms": round(ms_local + topk["ms_per_step"], 4),
                  "mixed_pair_note": "one local layer + one top-K layer (alternating policies), per pair",
-                 "step_stats": stats.get("local256k")}
+                 "step_stats": stats.get("local256k"),
+                 "graph_ms_per_step": graph_ms(step_local)}
 
     host1m = None if args.no_host1m else bench_host1m(args, pkv, synth, dev, t16)
     dense_host = None if args.no_densehost else bench_dense_host(args, pkv, synth, dev, t16)

@@ -48,7 +48,7 @@ static_assert(NKT_TILES_PER_WG == DkvCfg<128>::NW * DkvCfg<128>::NKT, "host plan
 // which the softmax needs for S and dP); the instruction is written out so that its accumulator is
 // pinned to the AGPR file.
 __device__ __forceinline__ void mfma32_agpr(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
 // x / G for 0 <= x < 2^24 from a float reciprocal, corrected to the exact quotient.

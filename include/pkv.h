@@ -30,6 +30,16 @@
  *    paged_kv_check.
  *  - Errors: the return value is a status code below; pkv_last_error() gives a message
  *    (thread-local, valid until the next call on the same thread).
+ *  - HIP graphs: paged_kv_zero_grad, paged_kv_append, page_topk_select and chunk_attn_fwd / _bwd
+ *    may be recorded into a HIP graph by stream capture (tested: a whole step, replayed) when the
+ *    caller passes every workspace (ws_dev with enough ws_bytes) and the timing hooks are off:
+ *    they then enqueue kernels only (memory is cleared by fill kernels, never by memset nodes),
+ *    allocate nothing and never synchronise. paged_kv_alloc, paged_kv_free and paged_kv_check
+ *    synchronise the device and must stay outside a capture.
+ *  - Streams: overlap between calls on different streams (host-tier gathers, gradient offload,
+ *    page copies beside attention) needs those streams on different hardware queues. HIP spreads
+ *    a process's streams over a small number of hardware queues, so keep the number of live
+ *    streams within it, or copies may run serialised behind the kernels of another stream.
  */
 #ifndef PKV_H
 #define PKV_H

@@ -154,6 +154,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
+  // Loop-invariant LDS byte offsets of this lane's MFMA operands within a stage. The swizzle of a
+  // tile row depends only on the row's low four bits, which the 32-key half (k2) and the 16-key
+  // step (hf) never change, so every operand address is one of these plus a constant.
+  uint32_t koff[T::KS];     // K and V rows l32, columns 16 ks + 8 lg
+  uint32_t toff_t[T::DT][2];  // K^T: rows 4 lg + rr (+8), columns 32 dt + 16 b4 + 4 (lane%4)
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) koff[ks] = 2u * (uint32_t)toff<D>(l32, ks * 16 + 8 * lg);
+  {
+    const int rr = (lane & 15) >> 2, cb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) toff_t[dt][kh] = 2u * (uint32_t)toff<D>(4 * lg + rr + 8 * kh, dt * 32 + cb);
+  }
+
   const float sl2 = a.scale * kLog2e;
   f32x16 dq[T::DT];
 #pragma unroll
@@ -168,8 +183,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int cur = (i - tb) & 1;
     const int32_t kpos_t = kpos_next;
     if (i + 1 < te) load_tile(i + 1, cur ^ 1, kpos_next);
-    const uint16_t* kt = lds + cur * 2 * T::TILE;
-    const uint16_t* vt = kt + T::TILE;
+    const char* kt = reinterpret_cast<const char*>(lds + cur * 2 * T::TILE);
+    const char* vt = kt + 2 * T::TILE;
     const bool bad = kpos_t < 0;
     const bool need_mask = bad || (kpos_t + BK - 1 > q0 + t_min);
     const int32_t lim = q0 + tq;
@@ -181,7 +196,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
-        const int off = toff<D>(k2 * 32 + l32, ks * 16 + 8 * lg);
+        const uint32_t off = koff[ks] + k2 * 32 * D * 2;
         const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + off));
         const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + off));
         sacc = mfma32(ka, qreg[ks], sacc);
@@ -213,10 +228,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int k_lo = k2 * 32 + hf * 16 + 4 * lg;
+        const int rowb = (k2 * 32 + hf * 16) * D * 2;  // bytes
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt) {
-          const bf16x8 kta = tr_operand<D>(kt, k_lo, k_lo + 8, dt * 32, lane);
+          const u32x2 lo = lds_tr16(reinterpret_cast<const uint16_t*>(kt + toff_t[dt][0] + rowb));
+          const u32x2 hi = lds_tr16(reinterpret_cast<const uint16_t*>(kt + toff_t[dt][1] + rowb));
+          const bf16x8 kta = as_bf16x8((u32x4){lo[0], lo[1], hi[0], hi[1]});
           dq[dt] = mfma32(kta, dsb[hf], dq[dt]);
         }
       }

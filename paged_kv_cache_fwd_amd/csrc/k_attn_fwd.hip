@@ -126,6 +126,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
+  // Loop-invariant LDS byte offsets of this lane's MFMA operands within a stage. The swizzle of a
+  // tile row depends only on the row's low four bits, which the 32-key half (k2) and the 16-key
+  // step (hf) never change, so every operand address is one of these plus a constant.
+  uint32_t koff[T::KS];             // K rows l32, columns 16 ks + 8 lg
+  uint32_t voff[T::DT][2];          // V^T: rows 4 lg + rr (+8), columns 32 dt + 16 b4 + 4 (lane%4)
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) koff[ks] = 2u * (uint32_t)toff<D>(l32, ks * 16 + 8 * lg);
+  {
+    const int rr = (lane & 15) >> 2, cb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) voff[dt][kh] = 2u * (uint32_t)toff<D>(4 * lg + rr + 8 * kh, dt * 32 + cb);
+  }
+
   const float sl2 = a.scale * kLog2e;
   float m = -INFINITY, l = 0.f;
   f32x16 oacc[T::DT];
@@ -141,8 +156,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int cur = (i - tb) & 1;
     const int32_t kpos0 = kpos_next;
     if (i + 1 < te) load_tile(i + 1, cur ^ 1, kpos_next);
-    const uint16_t* kt = lds + cur * 2 * T::TILE;
-    const uint16_t* vt = kt + T::TILE;
+    const char* kt = reinterpret_cast<const char*>(lds + cur * 2 * T::TILE);
+    const char* vt = kt + 2 * T::TILE;
 
     f32x16 sacc[2] = {(f32x16){}, (f32x16){}};
     __builtin_amdgcn_s_setprio(1);
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int ks = 0; ks < T::KS; ++ks) {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + toff<D>(k2 * 32 + l32, ks * 16 + 8 * lg)));
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + koff[ks] + k2 * 32 * D * 2));
         sacc[k2] = mfma32(ka, qreg[ks], sacc[k2]);
       }
     }
@@ -205,10 +220,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int k_lo = k2 * 32 + hf * 16 + 4 * lg;
+        const int rowb = (k2 * 32 + hf * 16) * D * 2;  // bytes
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt) {
-          const bf16x8 va = tr_operand<D>(vt, k_lo, k_lo + 8, dt * 32, lane);
+          const u32x2 lo = lds_tr16(reinterpret_cast<const uint16_t*>(vt + voff[dt][0] + rowb));
+          const u32x2 hi = lds_tr16(reinterpret_cast<const uint16_t*>(vt + voff[dt][1] + rowb));
+          const bf16x8 va = as_bf16x8((u32x4){lo[0], lo[1], hi[0], hi[1]});
           oacc[dt] = mfma32(va, pb[k2][hf], oacc[dt]);
         }
       }

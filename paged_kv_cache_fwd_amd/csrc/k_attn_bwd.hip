@@ -194,13 +194,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int k2 = 0; k2 < 2; ++k2) {
       f32x16 sacc = (f32x16){}, pacc = (f32x16){};
       __builtin_amdgcn_s_setprio(1);
+      // The K and V operands of k-step ks + 1 are read while the MFMAs of ks run.
+      bf16x8 ka[2], va[2];
+      ka[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + koff[0] + k2 * 32 * D * 2));
+      va[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + koff[0] + k2 * 32 * D * 2));
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
-        const uint32_t off = koff[ks] + k2 * 32 * D * 2;
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + off));
-        const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + off));
-        sacc = mfma32(ka, qreg[ks], sacc);
-        pacc = mfma32(va, doreg[ks], pacc);
+        if (ks + 1 < T::KS) {
+          const uint32_t off = koff[ks + 1] + k2 * 32 * D * 2;
+          ka[(ks + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + off));
+          va[(ks + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + off));
+        }
+        sacc = mfma32(ka[ks & 1], qreg[ks], sacc);
+        pacc = mfma32(va[ks & 1], doreg[ks], pacc);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        if (ks + 1 < T::KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       __builtin_amdgcn_s_setprio(0);
       float p[16];

@@ -54,6 +54,32 @@ def traffic_bytes(kernel):
     return TRAFFIC_BYTES[kernel]
 
 
+def mfma_loop_peak(pkv, dev, ms_target=30.0):
+    """Sustained bf16 MFMA rate of this GPU (the library's diagnostic loop, one 8-wave workgroup per
+    CU, about 30 ms per launch, best of three), in TFLOP/s."""
+    import torch
+    n_wg = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device=dev)
+    iters = 1000
+    flop = pkv.mfma_probe(n_wg, iters, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    pkv.mfma_probe(n_wg, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    iters = max(1000, int(iters * ms_target / max(e0.elapsed_time(e1), 1e-3)))
+    best = 0.0
+    for _ in range(3):
+        e0.record()
+        flop = pkv.mfma_probe(n_wg, iters, out)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    assert torch.isfinite(out).all()
+    return best
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -570,6 +596,8 @@ def main():
         return
     ms_dense, kt_dense = run(step_dense, "dense256k")
     tflops_dense = flop_dense / (ms_dense * 1e-3) / 1e12
+    mfma_peak = mfma_loop_peak(pkv, dev)
+    log(f"[bench] sustained MFMA loop: {mfma_peak:.1f} TFLOP/s")
     # Streaming-copy reference (1 GiB read + 1 GiB written) and cold-cache step times: a 1 GiB write
     # before each step evicts the L2 caches and the 256 MB Infinity Cache; events bracket the step only.
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -625,6 +653,8 @@ def main():
                     "traffic": None if tb is None else int(tb[0] + tb[1]),
                     "traffic_fetch_write": None if tb is None else [int(tb[0]), int(tb[1])],
                     "avg_launch_ms": round(avg_ms, 4),
+                    "measured_mfma_loop_TFLOPs": round(mfma_peak, 1),
+                    "frac_of_measured_mfma_loop": round(ach / mfma_peak, 4),
                     "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_dense.items()}}
     else:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -711,6 +741,7 @@ def main():
                                "+ causal own block, 28/4 heads, d=128, K = N(0,1) + per-page N(0,0.5) offset",
                    "context": wl.context, "chunk": C, "page": P, "h_q": H_q, "h_kv": H_kv, "head_dim": d,
                    "flop_per_step": flop_dense, "pct_bf16_peak": round(100.0 * tflops_dense / PEAK_BF16_TFLOPS, 2),
+                   "pct_measured_mfma_loop": round(100.0 * tflops_dense / mfma_peak, 2),
                    "step": "append own block + forward + backward (dK/dV accumulated into gradient pages)"},
         "roofline": roofline,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "step_stats": stats.get("dense256k"),

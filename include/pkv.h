@@ -258,6 +258,18 @@ int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_
                     int32_t* dev_bt_out_dev, int32_t n_dev_bt, void* stream);
 
 /*
+ * Diagnostic: the sustained bf16 MFMA rate of this GPU, the practical ceiling of the attention
+ * kernels (its clock under MFMA load is below the one the datasheet peak assumes). Enqueues
+ * n_workgroups workgroups of 512 threads (two waves per SIMD), each wave running iters steps of
+ * four independent v_mfma_f32_32x32x16_bf16 on register operands filled with pseudo-random bf16
+ * bits; no memory is touched in the loop. out_dev (float, n_workgroups * 512 entries, device)
+ * receives one sum per thread so the work is not optimised away; its values carry no meaning.
+ * *flop (host, may be NULL) receives the FLOP count of the launch; the caller times it.
+ * Errors: PKV_E_INVALID for non-positive sizes or a NULL out_dev.
+ */
+int pkv_mfma_probe(int32_t n_workgroups, int32_t iters, float* out_dev, double* flop, void* stream);
+
+/*
  * Per-kernel timing (tracing aid, off by default). While enabled, every kernel launch of the
  * library is bracketed by two HIP events recorded on the launch's own stream.
  * pkv_timing_enable(1) clears earlier records and starts recording; pkv_timing_enable(0) stops.

@@ -25,7 +25,8 @@ EXPORTED = (
     "pkv_version", "pkv_last_error", "paged_kv_alloc", "paged_kv_free", "paged_kv_info", "paged_kv_data",
     "paged_kv_append", "paged_kv_zero_grad", "paged_kv_export", "paged_kv_check", "page_topk_ws_bytes",
     "page_topk_select", "chunk_attn_fwd_ws_bytes", "chunk_attn_fwd", "chunk_attn_bwd_ws_bytes",
-    "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "paged_kv_copy", "pkv_timing_enable", "pkv_timing_collect",
+    "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "paged_kv_copy", "pkv_mfma_probe",
+    "pkv_timing_enable", "pkv_timing_collect",
     "pkv_timing_get",
 )
 
@@ -77,6 +78,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P]),
         "paged_kv_grad_offload": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _P]),
         "paged_kv_copy": (_I, [_P, _P, _U, _I, _I, _P]),
+        "pkv_mfma_probe": (_I, [_I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
         "pkv_timing_enable": (_I, [ctypes.c_int]),
         "pkv_timing_collect": (ctypes.c_int, []),
         "pkv_timing_get": (_I, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I),
@@ -324,6 +326,14 @@ def paged_kv_copy(src: Pool, dst: Pool, what: int, first_page: int = 0, n_pages:
     KV pages with PKV_COPY_KV, gradient pages with PKV_COPY_GRAD (host or device pools alike)."""
     n_pages = min(src.n_pages, dst.n_pages) - first_page if n_pages is None else n_pages
     _check(load().paged_kv_copy(src.handle, dst.handle, what, first_page, n_pages, _stream(stream)))
+
+
+def mfma_probe(n_workgroups: int, iters: int, out: torch.Tensor, stream=None) -> float:
+    """Enqueue the sustained-MFMA diagnostic; returns its FLOP count (the caller times it)."""
+    _need(out, torch.float32, "out", (n_workgroups * 512,))
+    flop = ctypes.c_double(0.0)
+    _check(load().pkv_mfma_probe(n_workgroups, iters, _ptr(out), ctypes.byref(flop), _stream(stream)))
+    return flop.value
 
 
 def timing_enable(on: bool = True):

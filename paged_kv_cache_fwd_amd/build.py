@@ -21,6 +21,7 @@ KERNELS = {
     "k_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_attn_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 HOST = ["pkv_abi.cpp"]
 

@@ -223,6 +223,16 @@ extern "C" {
 
 int pkv_version(void) { return 100; }
 
+int pkv_mfma_probe(int32_t n_workgroups, int32_t iters, float* out_dev, double* flop, void* stream) {
+  if (n_workgroups <= 0 || iters <= 0) return fail(PKV_E_INVALID, "n_workgroups and iters must be > 0");
+  if (!out_dev) return fail(PKV_E_INVALID, "out_dev is NULL");
+  if (flop) *flop = pkv::mfma_probe_flop(n_workgroups, iters);
+  hipError_t e = pkv::launch_mfma_probe(n_workgroups, iters, out_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mfma probe launch");
+  ok();
+  return PKV_OK;
+}
+
 int pkv_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(pkv::g_tmu);
   pkv::g_timing = on != 0;

@@ -106,6 +106,8 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
                        int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t n_lists, int32_t* sel,
                        void* ws, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, const FwdPlan& plan, uint16_t* o, float* lse, void* ws, hipStream_t s);
+hipError_t launch_mfma_probe(int32_t n_wg, int32_t iters, float* out, hipStream_t s);
+double mfma_probe_flop(int32_t n_wg, int32_t iters);
 hipError_t launch_bwd(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, void* ws, hipStream_t s);
 template <int D>
 hipError_t launch_dkdv(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, const float* ndbuf,

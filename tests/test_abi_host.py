@@ -63,6 +63,9 @@ def test_argument_errors_without_device(lib):
     assert lib.paged_kv_grad_offload(None, None, 0, None, None, 0, None, 0, 0, 1, None) == -1
     assert lib.paged_kv_copy(None, None, 1, 0, 0, None) == -1
     assert lib.paged_kv_check(None) == -1
+    assert lib.pkv_mfma_probe(0, 1, None, None, None) == -1
+    assert lib.pkv_mfma_probe(1, 0, None, None, None) == -1
+    assert lib.pkv_mfma_probe(1, 1, None, None, None) == -1
     assert lib.paged_kv_data(None, 0) is None
     assert lib.chunk_attn_fwd_ws_bytes(None, 0, -1, 1, 1, 64, 4) == 0
     assert lib.page_topk_ws_bytes(None, 0, 64, 4, 1) == 0

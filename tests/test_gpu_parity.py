@@ -369,3 +369,20 @@ def test_page_reps_bulk_append(pkv, page, d):
     want = oracle.page_reps(oracle.page_key_sums(k[:full * page], page), page)
     assert np.array_equal(got.view(np.uint32), want.astype(np.float32).view(np.uint32))
     pool.free()
+
+
+def test_mfma_probe_runs_and_counts(pkv):
+    """The sustained-MFMA diagnostic: finite outputs, the FLOP count it reports, a rate below the
+    datasheet peak."""
+    n_wg, iters = 8, 2000
+    out = torch.empty(n_wg * 512, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flop = pkv.mfma_probe(n_wg, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    assert flop == n_wg * 8 * iters * 4 * 32 * 32 * 16 * 2
+    assert bool(torch.isfinite(out).all())
+    tflops = flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    say(f"  mfma probe on {n_wg} CUs: {tflops:.1f} TFLOP/s")
+    assert 0 < tflops < 2600.0 * n_wg / 256

@@ -386,3 +386,48 @@ def test_mfma_probe_runs_and_counts(pkv):
     tflops = flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
     say(f"  mfma probe on {n_wg} CUs: {tflops:.1f} TFLOP/s")
     assert 0 < tflops < 2600.0 * n_wg / 256
+
+
+def test_bad_table_and_selection_entries_are_skipped_and_reported(pkv):
+    """Device-side validation: a block-table entry outside the pool and a selection id outside
+    [0, n_prior) are skipped by every kernel (the page acts as absent) and reported once through
+    paged_kv_check (PKV_E_DEVICE). Results equal the oracle's with that page left out."""
+    wl = synth.Workload("bad", 4, 1, 64, 64, 64 * 12, 256, (2,), offset_std=0.5, seed=41)
+    c = wl.chunks[0]
+    q0, C, P, n_prior = wl.q0(c), wl.chunk, wl.page, wl.n_prior(c)  # 8 prior pages
+    bt_np = synth.page_permutation(wl).copy()
+    bad_lp = 5
+    bt_np[bad_lp] = wl.n_pages + 3  # outside the pool
+    pool = pkv.Pool(wl.n_pages, P, wl.h_kv, wl.d, grads=True)
+    bt = i32(bt_np)
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    pool.append(bt, 0, t16(k), t16(v))
+    torch.cuda.synchronize()
+    with pytest.raises(pkv.PkvError) as ei:
+        pool.check()
+    assert ei.value.code == pkv.PKV_E_DEVICE
+    pool.check()  # the error word was cleared by the read
+    q, do = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+    keep = np.array([[p for p in range(n_prior) if p != bad_lp]], np.int32)
+    cases = (("dense pass over a bad table entry", None, keep),
+             ("selection with an id past n_prior", np.array([[0, 2, 7, n_prior + 91]], np.int32),
+              np.array([[0, 2, 7]], np.int32)))
+    for name, sel_gpu, sel_ref in cases:
+        say(f"case {name}")
+        pool.zero_grad()
+        sel_t = None if sel_gpu is None else i32(sel_gpu)
+        o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, t16(q), wl.scale, sel=sel_t)
+        dq = pkv.chunk_attn_bwd(pool, bt, n_prior, t16(q), o, t16(do), lse, wl.scale, sel=sel_t)
+        dk = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy()
+        torch.cuda.synchronize()
+        with pytest.raises(pkv.PkvError) as ei:
+            pool.check()
+        assert ei.value.code == pkv.PKV_E_DEVICE
+        ref = oracle.chunk_backward(q, k, v, do, q0, wl.scale, sel=sel_ref, page=P)
+        compare("O", host(o), ref["o"], ATOL_O)
+        compare("LSE", lse.cpu().numpy(), ref["lse"], ATOL_LSE, rel=1e-5)
+        compare("dQ", host(dq), ref["dq"], ATOL_GRAD)
+        keys = ref["keys"][0]
+        compare("dK", dk[keys, 0], ref["dk"][0], ATOL_GRAD)
+        assert np.all(dk[bad_lp * P:(bad_lp + 1) * P] == 0)
+    pool.free()

@@ -10,13 +10,12 @@
 
 namespace pkv {
 
-// One thread per 16-byte chunk (8 bf16) of K or V.
-__global__ __launch_bounds__(256) void k_append(uint16_t* __restrict__ kv, int32_t n_pool, int32_t P, int32_t H,
-                                                int32_t D, const int32_t* __restrict__ bt, int32_t n_bt,
-                                                int32_t pos0, int32_t n, const uint16_t* __restrict__ k,
-                                                const uint16_t* __restrict__ v, int32_t* err) {
+// One thread per 16-byte chunk (8 bf16) of K or V; idx is the chunk index.
+__device__ __forceinline__ void append_chunk(uint16_t* __restrict__ kv, int32_t n_pool, int32_t P, int32_t H,
+                                             int32_t D, const int32_t* __restrict__ bt, int32_t n_bt, int32_t pos0,
+                                             int32_t n, const uint16_t* __restrict__ k,
+                                             const uint16_t* __restrict__ v, int32_t* err, int64_t idx) {
   const int64_t per = (int64_t)n * H * (D / 8);
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= 2 * per) return;
   const int which = idx >= per;
   const int64_t c = which ? idx - per : idx;
@@ -32,19 +31,27 @@ __global__ __launch_bounds__(256) void k_append(uint16_t* __restrict__ kv, int32
   *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
+__global__ __launch_bounds__(256) void k_append(uint16_t* __restrict__ kv, int32_t n_pool, int32_t P, int32_t H,
+                                                int32_t D, const int32_t* __restrict__ bt, int32_t n_bt,
+                                                int32_t pos0, int32_t n, const uint16_t* __restrict__ k,
+                                                const uint16_t* __restrict__ v, int32_t* err) {
+  append_chunk(kv, n_pool, P, H, D, bt, n_bt, pos0, n, k, v, err, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
 // Representative key of each page completed by an append: float32 sequential sum over the page's
 // tokens in token order starting from +0.0, times 1/P (exact: P is a power of two).
-// One wave per (logical page, KV head) block, four blocks per workgroup. Lane l owns key columns
-// 2l and 2l+1: it loads its 4-byte column pair from every token row (a wave's load covers one
-// whole 256-byte row), all P loads issued before the first add, then runs the two columns' sums
-// side by side. No LDS and no barrier; each block is read once, straight from the pool.
+// One wave per (logical page, KV head) block, four blocks per workgroup (blk = 4 * wg + wave).
+// Lane l owns key columns 2l and 2l+1: it loads its 4-byte column pair from every token row (a
+// wave's load covers one whole 256-byte row), all P loads issued before the first add, then runs
+// the two columns' sums side by side. No LDS and no barrier. Rows come from the pool, or, when
+// ksrc is given, rows at positions >= pos0 come from the appended keys ksrc ([n][H][D], first row
+// at pos0) instead, so the sums need nothing written by the same launch.
 template <int P>
-__global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ kv, float* __restrict__ rep,
-                                                   int32_t n_pool, int32_t H, int32_t D,
-                                                   const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
-                                                   int32_t n_lp, int32_t* err) {
-  const int32_t lane = threadIdx.x & 63;
-  const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+__device__ __forceinline__ void page_rep_block(const uint16_t* __restrict__ kv, float* __restrict__ rep,
+                                               int32_t n_pool, int32_t H, int32_t D,
+                                               const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
+                                               int32_t n_lp, int32_t* err, const uint16_t* __restrict__ ksrc,
+                                               int32_t pos0, int64_t blk, int32_t lane) {
   if (blk >= (int64_t)n_lp * H || 2 * lane >= D) return;
   const int32_t g = (int32_t)(blk % H);
   const int32_t lp = lp0 + (int32_t)(blk / H);
@@ -53,8 +60,16 @@ __global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ 
   const uint32_t* kp = reinterpret_cast<const uint32_t*>(kv + (((int64_t)phys * H + g) * 2) * P * D) + lane;
   const int32_t row = D / 2;  // 4-byte words per token row
   uint32_t x[P];
+  if (ksrc == nullptr) {
 #pragma unroll
-  for (int32_t t = 0; t < P; ++t) x[t] = kp[t * row];
+    for (int32_t t = 0; t < P; ++t) x[t] = kp[t * row];
+  } else {
+    // Row t of the page sits at position lp * P + t; rows from pos0 on are the appended keys.
+    const int32_t t_src = pos0 - lp * P;  // first row taken from ksrc (may be <= 0)
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(ksrc) + ((int64_t)(-t_src) * H + g) * row + lane;
+#pragma unroll
+    for (int32_t t = 0; t < P; ++t) x[t] = t >= t_src ? sp[(int64_t)t * H * row] : kp[t * row];
+  }
   float a0 = 0.0f, a1 = 0.0f;  // columns 2*lane (low half-word) and 2*lane + 1 (high half-word)
 #pragma unroll
   for (int32_t t = 0; t < P; ++t) {
@@ -66,25 +81,66 @@ __global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ 
   r[1] = __fmul_rn(a1, 1.0f / (float)P);
 }
 
+template <int P>
+__global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ kv, float* __restrict__ rep,
+                                                   int32_t n_pool, int32_t H, int32_t D,
+                                                   const int32_t* __restrict__ bt, int32_t n_bt, int32_t lp0,
+                                                   int32_t n_lp, int32_t* err) {
+  page_rep_block<P>(kv, rep, n_pool, H, D, bt, n_bt, lp0, n_lp, err, nullptr, 0,
+                    (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
 // Zero the gradient blocks of logical pages [lp0, lp0 + n_lp) (bt == NULL: physical = logical).
 // Grid (x: 32 KiB pieces of a page, y: pages, striding when there are more than gridDim.y): one
 // table lookup per workgroup, 8 16-byte stores per thread.
 constexpr int kZeroPerThread = 8;
+// Piece `piece` (8 x 256 16-byte chunks) of the gradient block of logical page lp.
+__device__ __forceinline__ void zero_grad_piece(float* __restrict__ grad, int32_t n_pool, int32_t P, int32_t H,
+                                                int32_t D, const int32_t* __restrict__ bt, int32_t n_bt,
+                                                int32_t lp, int32_t piece, int32_t* err) {
+  const int64_t per_page = (int64_t)H * 2 * P * D / 4;  // 16-byte chunks per page
+  const int64_t i0 = (int64_t)piece * kZeroPerThread * 256 + threadIdx.x;
+  const int32_t phys = bt ? phys_page(bt, n_bt, n_pool, lp, err) : lp;
+  if (phys < 0 || phys >= n_pool) return;
+  f32x4* base = reinterpret_cast<f32x4*>(grad) + (int64_t)phys * per_page;
+#pragma unroll
+  for (int u = 0; u < kZeroPerThread; ++u) {
+    const int64_t i = i0 + (int64_t)u * 256;
+    if (i < per_page) base[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Zero the gradient blocks of logical pages [lp0, lp0 + n_lp) (bt == NULL: physical = logical).
+// Grid (x: 32 KiB pieces of a page, y: pages, striding when there are more than gridDim.y): one
+// table lookup per workgroup, 8 16-byte stores per thread.
 __global__ __launch_bounds__(256) void k_zero_grad(float* __restrict__ grad, int32_t n_pool, int32_t P, int32_t H,
                                                    int32_t D, const int32_t* __restrict__ bt, int32_t n_bt,
                                                    int32_t lp0, int32_t n_lp, int32_t* err) {
-  const int64_t per_page = (int64_t)H * 2 * P * D / 4;  // 16-byte chunks per page
-  const int64_t i0 = (int64_t)blockIdx.x * kZeroPerThread * 256 + threadIdx.x;
-  for (int32_t r = blockIdx.y; r < n_lp; r += gridDim.y) {
-    const int32_t lp = lp0 + r;
-    const int32_t phys = bt ? phys_page(bt, n_bt, n_pool, lp, err) : lp;
-    if (phys < 0 || phys >= n_pool) continue;
-    f32x4* base = reinterpret_cast<f32x4*>(grad) + (int64_t)phys * per_page;
-#pragma unroll
-    for (int u = 0; u < kZeroPerThread; ++u) {
-      const int64_t i = i0 + (int64_t)u * 256;
-      if (i < per_page) base[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
+  for (int32_t r = blockIdx.y; r < n_lp; r += gridDim.y)
+    zero_grad_piece(grad, n_pool, P, H, D, bt, n_bt, lp0 + r, blockIdx.x, err);
+}
+
+// A chunk-sized append in one launch: workgroups [0, nr) build the representatives of the pages
+// it completes, reading the appended rows from k itself (dispatched first: each is a chain of
+// dependent row loads), [nr, nr + nz) zero the gradient blocks of the pages the append starts
+// (zp pieces per page), the rest copy K and V into the pages. None of the three reads what
+// another writes.
+template <int P>
+__global__ __launch_bounds__(256) void k_append_fused(uint16_t* __restrict__ kv, float* __restrict__ grad,
+                                                      float* __restrict__ rep, int32_t n_pool, int32_t H, int32_t D,
+                                                      const int32_t* __restrict__ bt, int32_t n_bt, int32_t pos0,
+                                                      int32_t n, const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v, int32_t first_new, int32_t zp,
+                                                      int32_t nz, int32_t nr, int32_t lp_a, int32_t n_lp,
+                                                      int32_t* err) {
+  const int32_t b = blockIdx.x;
+  if (b < nr) {
+    page_rep_block<P>(kv, rep, n_pool, H, D, bt, n_bt, lp_a, n_lp, err, k, pos0,
+                      (int64_t)b * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+  } else if (b < nr + nz) {
+    zero_grad_piece(grad, n_pool, P, H, D, bt, n_bt, first_new + (b - nr) / zp, (b - nr) % zp, err);
+  } else {
+    append_chunk(kv, n_pool, P, H, D, bt, n_bt, pos0, n, k, v, err, (int64_t)(b - nr - nz) * 256 + threadIdx.x);
   }
 }
 
@@ -241,38 +297,58 @@ __global__ __launch_bounds__(256) void k_grad_offload(float* __restrict__ host_g
 
 static inline unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+// Appends of at most this many tokens (a chunk's own block) run as one fused launch; larger ones
+// (pool fills) as three kernels, each with the whole grid to itself.
+constexpr int32_t kFusedAppendMaxTokens = 16384;
+
 hipError_t launch_append(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t pos0, int32_t n,
                          const uint16_t* k, const uint16_t* v, hipStream_t s) {
   const int32_t P = pool.page, H = pool.h_kv, D = pool.d;
   // Pages whose first token is written here get zeroed gradients.
   const int32_t first_new = (pos0 + P - 1) / P;           // first page starting at or after pos0
   const int32_t end_new = (pos0 + n + P - 1) / P;         // pages starting before pos0 + n
-  if (pool.grad && end_new > first_new) {
-    TimerScope ts_("k_zero_grad", s);
-    hipLaunchKernelGGL(k_zero_grad, zero_grid(pool, end_new - first_new), dim3(256), 0, s, pool.grad, pool.n_pages, P,
-                       H, D, bt, n_bt, first_new, end_new - first_new, pool.err);
-  }
+  const int32_t n_new = (pool.grad && end_new > first_new) ? end_new - first_new : 0;
   const int64_t chunks = (int64_t)2 * n * H * (D / 8);
+  // Pages whose last token is written here get their representative key.
+  const int32_t first_full = pos0 / P;                    // candidate: page containing pos0
+  const int32_t lp_a = ((first_full + 1) * P - 1 >= pos0) ? first_full : first_full + 1;
+  const int32_t lp_b = (pos0 + n) / P;                    // pages fully ending before pos0 + n
+  const int32_t n_lp = lp_b > lp_a ? lp_b - lp_a : 0;
+  if (n <= kFusedAppendMaxTokens) {
+    const int32_t zp = (int32_t)zero_grid(pool, 1).x;     // pieces per page
+    const int32_t nz = n_new * zp;
+    const int32_t na = (int32_t)grid_for(chunks);
+    const int32_t nr = (int32_t)(((int64_t)n_lp * H + 3) / 4);
+    TimerScope ts_("k_append_fused", s);
+    if (P == 128)
+      hipLaunchKernelGGL(k_append_fused<128>, dim3((unsigned)(nz + na + nr)), dim3(256), 0, s, pool.kv, pool.grad,
+                         pool.rep, pool.n_pages, H, D, bt, n_bt, pos0, n, k, v, first_new, zp, nz, nr, lp_a, n_lp,
+                         pool.err);
+    else
+      hipLaunchKernelGGL(k_append_fused<64>, dim3((unsigned)(nz + na + nr)), dim3(256), 0, s, pool.kv, pool.grad,
+                         pool.rep, pool.n_pages, H, D, bt, n_bt, pos0, n, k, v, first_new, zp, nz, nr, lp_a, n_lp,
+                         pool.err);
+    return hipGetLastError();
+  }
+  if (n_new > 0) {
+    TimerScope ts_("k_zero_grad", s);
+    hipLaunchKernelGGL(k_zero_grad, zero_grid(pool, n_new), dim3(256), 0, s, pool.grad, pool.n_pages, P, H, D, bt,
+                       n_bt, first_new, n_new, pool.err);
+  }
   {
     TimerScope ts_("k_append", s);
     hipLaunchKernelGGL(k_append, dim3(grid_for(chunks)), dim3(256), 0, s, pool.kv, pool.n_pages, P, H, D, bt, n_bt,
                        pos0, n, k, v, pool.err);
   }
-  // Pages whose last token is written here get their representative key.
-  const int32_t first_full = pos0 / P;                    // candidate: page containing pos0
-  const int32_t lp_a = ((first_full + 1) * P - 1 >= pos0) ? first_full : first_full + 1;
-  const int32_t lp_b = (pos0 + n) / P;                    // pages fully ending before pos0 + n
-  if (lp_b > lp_a) {
-    {
-      TimerScope ts_("k_page_reps", s);
-      const dim3 grid((unsigned)(((int64_t)(lp_b - lp_a) * H + 3) / 4));
-      if (P == 128)
-        hipLaunchKernelGGL(k_page_reps<128>, grid, dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, H, D, bt, n_bt,
-                           lp_a, lp_b - lp_a, pool.err);
-      else
-        hipLaunchKernelGGL(k_page_reps<64>, grid, dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, H, D, bt, n_bt,
-                           lp_a, lp_b - lp_a, pool.err);
-    }
+  if (n_lp > 0) {
+    TimerScope ts_("k_page_reps", s);
+    const dim3 grid((unsigned)(((int64_t)n_lp * H + 3) / 4));
+    if (P == 128)
+      hipLaunchKernelGGL(k_page_reps<128>, grid, dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, H, D, bt, n_bt,
+                         lp_a, n_lp, pool.err);
+    else
+      hipLaunchKernelGGL(k_page_reps<64>, grid, dim3(256), 0, s, pool.kv, pool.rep, pool.n_pages, H, D, bt, n_bt,
+                         lp_a, n_lp, pool.err);
   }
   return hipGetLastError();
 }

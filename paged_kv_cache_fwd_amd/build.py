@@ -19,7 +19,9 @@ KERNELS = {
     "k_select.hip": ["-ffp-contract=off"],
     # MFMA results stay in architectural VGPRs (the softmax and gradient math reads them there).
     "k_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "k_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # dQ pass: the ILP-maximising machine scheduler measured about 1.7% faster here (and slower on
+    # the forward, which keeps the default).
+    "k_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "k_attn_dkdv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }

@@ -73,10 +73,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Wave-uniform, so the LDS destinations of the direct loads stay in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t n_units = a.n_kvh * n_ku * row_splits;
+  // Row splits vary slowest: the workgroups that run together on one XCD take neighbouring key
+  // units of one (KV head, row split) and stream the same query rows through its L2.
   const int32_t u = xcd_remap(blockIdx.x, n_units);
-  const int32_t rs = u % row_splits;
-  const int32_t ku = (u / row_splits) % n_ku;
-  const int32_t gi = u / (row_splits * n_ku);
+  const int32_t ku = u % n_ku;
+  const int32_t gi = (u / n_ku) % a.n_kvh;
+  const int32_t rs = u / (n_ku * a.n_kvh);
   const int32_t g = a.kvh0 + gi;
   // With one page list per query page the row splits are the query pages (the host plan sets
   // row_splits = n_lists, whose row ranges then start and end on query-page boundaries).

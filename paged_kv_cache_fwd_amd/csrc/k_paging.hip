@@ -66,9 +66,9 @@ __device__ __forceinline__ void page_rep_block(const uint16_t* __restrict__ kv, 
   } else {
     // Row t of the page sits at position lp * P + t; rows from pos0 on are the appended keys.
     const int32_t t_src = pos0 - lp * P;  // first row taken from ksrc (may be <= 0)
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(ksrc) + ((int64_t)(-t_src) * H + g) * row + lane;
+    const uint32_t* ks = reinterpret_cast<const uint32_t*>(ksrc) + (int64_t)g * row + lane;
 #pragma unroll
-    for (int32_t t = 0; t < P; ++t) x[t] = t >= t_src ? sp[(int64_t)t * H * row] : kp[t * row];
+    for (int32_t t = 0; t < P; ++t) x[t] = t >= t_src ? ks[(int64_t)(t - t_src) * H * row] : kp[t * row];
   }
   float a0 = 0.0f, a1 = 0.0f;  // columns 2*lane (low half-word) and 2*lane + 1 (high half-word)
 #pragma unroll
@@ -90,9 +90,6 @@ __global__ __launch_bounds__(256) void k_page_reps(const uint16_t* __restrict__ 
                     (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
-// Zero the gradient blocks of logical pages [lp0, lp0 + n_lp) (bt == NULL: physical = logical).
-// Grid (x: 32 KiB pieces of a page, y: pages, striding when there are more than gridDim.y): one
-// table lookup per workgroup, 8 16-byte stores per thread.
 constexpr int kZeroPerThread = 8;
 // Piece `piece` (8 x 256 16-byte chunks) of the gradient block of logical page lp.
 __device__ __forceinline__ void zero_grad_piece(float* __restrict__ grad, int32_t n_pool, int32_t P, int32_t H,

@@ -122,9 +122,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     wg_kpos_min = (lp0 < 0) ? 0 : lp0 * P + ((kt_first - (pi0 << tsh)) * 32);
   }
   const int32_t n_blk = (CG + BQ - 1) / BQ;
-  int32_t blk_b = (int32_t)((int64_t)n_blk * rs / row_splits);
-  const int32_t blk_e = (int32_t)((int64_t)n_blk * (rs + 1) / row_splits);
+  int32_t blk_b, blk_e;
+  if (a.n_lists > 1 || row_splits == 1) {
+    blk_b = (int32_t)((int64_t)n_blk * rs / row_splits);
+    blk_e = (int32_t)((int64_t)n_blk * (rs + 1) / row_splits);
+  } else {
+    // Row splits of equal work rather than equal rows. A unit with a prior key streams every row
+    // block; a unit of own keys only starts at its causal diagonal, so later blocks carry more
+    // units. work(b) counts the (unit, block) pairs of one KV head before block b, and split r
+    // starts at the first block where work reaches r/R of the total. Every workgroup evaluates
+    // the same integer function, so the splits partition [0, n_blk) exactly.
+    // Own unit j >= n_full starts at block G * (j * per_unit - prior_tiles) (32 keys per tile, 32
+    // rows per block): an arithmetic progression, so the sum over units has a closed form.
+    static_assert(BQ == 32, "unit start blocks assume 32-row blocks");
+    const int32_t prior_tiles = list_prior(a) << tsh, per_unit = T::NW * NKT;
+    const int32_t n_full = min(n_ku, (prior_tiles + per_unit - 1) / per_unit);
+    const int32_t s0 = G * (n_full * per_unit - prior_tiles), dlt = G * per_unit;
+    auto work = [&](int32_t b) {
+      int64_t w = (int64_t)n_full * b;
+      if (b > s0) {
+        const int64_t k = min<int64_t>(n_ku - n_full, (b - s0 + dlt - 1) / dlt);  // units begun before b
+        w += k * (b - s0) - (int64_t)dlt * k * (k - 1) / 2;
+      }
+      return w;
+    };
+    const int64_t total = work(n_blk);
+    auto split_start = [&](int32_t r) {
+      const int64_t target = total * r / row_splits;
+      int32_t lo = 0, hi = n_blk;  // first b with work(b) >= target
+      while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (work(mid) >= target) hi = mid;
+        else lo = mid + 1;
+      }
+      return lo;
+    };
+    blk_b = split_start(rs);
+    blk_e = rs + 1 == row_splits ? n_blk : split_start(rs + 1);
+  }
   if (wg_kpos_min > q0) blk_b = max(blk_b, (G * (wg_kpos_min - q0)) / BQ);
+  if (blk_b >= blk_e) return;  // no row of this split sees a key of the unit (uniform per workgroup)
   // Row r sees key k iff r >= G * (k - q0). Blocks before blk_m hold rows that some key of the
   // workgroup does not see (own pages only) and run the masked, unpipelined path.
   int32_t my_rmin[NKT];
@@ -382,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // grad[gphys][g][0/1][sub*32 + key][d]. Lanes of one instruction cover 32 consecutive d.
 #pragma unroll
   for (int j = 0; j < NKT; ++j) {
-    if (kval[j] && blk_b < blk_e) {
+    if (kval[j]) {
       float* gk = e.grad + (((int64_t)gph[j] * H + g) * 2) * P * D + (int64_t)tsub[j] * 32 * D;
       float* gv = gk + (int64_t)P * D;
 #pragma unroll

@@ -53,7 +53,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int32_t n_units = a.n_kvh * splits * n_rb;
   const int32_t u = xcd_remap(blockIdx.x, n_units);
-  const int32_t rb = u % n_rb;
+  // Row blocks run last to first within each (split, KV head): later rows see more of the chunk's
+  // own keys, so the longest workgroups are dispatched first and the short ones fill the tail.
+  const int32_t rb = n_rb - 1 - u % n_rb;
   const int32_t sp = (u / n_rb) % splits;
   const int32_t gi = u / (n_rb * splits);
   const int32_t g = a.kvh0 + gi;

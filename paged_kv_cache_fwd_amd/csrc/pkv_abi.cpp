@@ -12,6 +12,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/pkv.h"
@@ -182,6 +183,69 @@ static int32_t row_blocks(int64_t rows, int32_t n_lists, int32_t nw) {
   return (int32_t)(n_lists * ((per_list + rb - 1) / rb));
 }
 
+// Key-range split count of the forward and dQ passes. Their row blocks see different numbers of
+// key tiles (the chunk's own keys up to each block's last row), so the count comes from a model of
+// the dispatch: units u = (row block, split, KV head) in the kernels' order, row blocks last to
+// first, cut into eight contiguous XCD shares, each run in rounds of (CUs per XCD x workgroups
+// per CU) whose length is that round's longest workgroup (its tiles + a fixed 3), plus the
+// combine or reduce pass for more than one split (4 + 4.3 per split, in tile times). The model
+// runs once per shape.
+static int32_t key_splits(int32_t n_kvh, int32_t n_lists, int64_t rows, int32_t nw, int32_t G, int32_t prior_tiles,
+                          int32_t max_split) {
+  struct Key {
+    int32_t n_kvh, n_lists, nw, G, prior_tiles, max_split;
+    int64_t rows;
+    bool operator<(const Key& o) const {
+      return std::tie(n_kvh, n_lists, nw, G, prior_tiles, max_split, rows) <
+             std::tie(o.n_kvh, o.n_lists, o.nw, o.G, o.prior_tiles, o.max_split, o.rows);
+    }
+  };
+  static std::mutex mu;
+  static std::map<Key, int32_t> cache;
+  const Key key{n_kvh, n_lists, nw, G, prior_tiles, max_split, rows};
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const int64_t RL = rows / n_lists, rbw = 32 * (int64_t)nw, bpl = (RL + rbw - 1) / rbw, n_rb = n_lists * bpl;
+  const int64_t slots = std::max<int64_t>(1, (int64_t)num_cus() / 8 * (8 / nw));
+  std::vector<int32_t> tiles((size_t)n_rb);
+  for (int64_t rb = 0; rb < n_rb; ++rb) {
+    const int64_t li = rb / bpl, r0 = li * RL + (rb - li * bpl) * rbw;
+    const int64_t r_last = std::min(r0 + rbw, (li + 1) * RL) - 1;
+    tiles[(size_t)rb] = prior_tiles + (int32_t)((r_last / G) / 64) + 1;
+  }
+  int32_t best = 1;
+  double best_cost = 1e300;
+  for (int32_t s = 1; s <= std::min(max_split, 16); ++s) {
+    const int64_t n = (int64_t)n_kvh * s * n_rb, q = n / 8, r = n % 8;
+    double worst = 0;
+    for (int64_t x = 0; x < 8; ++x) {
+      const int64_t a = x * q + std::min(x, r), b = a + q + (x < r ? 1 : 0);
+      double cost = 0;
+      for (int64_t k0 = a; k0 < b; k0 += slots) {
+        int64_t m = 0;
+        for (int64_t u = k0; u < std::min(b, k0 + slots); ++u) {
+          const int64_t rb = n_rb - 1 - u % n_rb, sp = (u / n_rb) % s, nt = tiles[(size_t)rb];
+          m = std::max(m, nt * (sp + 1) / s - nt * sp / s);
+        }
+        cost += (double)m + 3.0;
+      }
+      worst = std::max(worst, cost);
+    }
+    const double total = worst + (s > 1 ? 4.0 + 4.3 * s : 0.0);
+    if (total < best_cost - 1e-9) {
+      best_cost = total;
+      best = s;
+    }
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache.size() > 256) cache.clear();
+  cache[key] = best;
+  return best;
+}
+
 FwdPlan plan_fwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_kvh, int32_t C, int32_t G,
                  int32_t d) {
   FwdPlan p;
@@ -190,7 +254,7 @@ FwdPlan plan_fwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_
   p.n_rb = row_blocks(rows, n_lists, p.nw);
   const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
-  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 8 / p.nw);
+  p.splits = key_splits(n_kvh, n_lists, rows, p.nw, G, n_list_pages * (page / 64), max_split);
   p.ws_bytes = p.splits > 1 ? align256((size_t)p.splits * n_kvh * rows * d * 4) + align256((size_t)p.splits * n_kvh * rows * 4) : 0;
   return p;
 }
@@ -203,7 +267,7 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_
   p.n_rb = row_blocks(rows, n_lists, p.dq_nw);
   const double tiles = (double)n_list_pages * (page / 64) + (C / 64 + 1) / 2.0;
   const int32_t max_split = (int32_t)std::max(1.0, std::min(32.0, tiles));
-  p.splits = best_split((int64_t)n_kvh * p.n_rb, tiles, 3.0, max_split, 8 / p.dq_nw);
+  p.splits = key_splits(n_kvh, n_lists, rows, p.dq_nw, G, n_list_pages * (page / 64), max_split);
   const int64_t n_kt = (int64_t)(n_list_pages + C / page) * (page / 32);
   p.n_ku = (int32_t)((n_kt + NKT_TILES_PER_WG - 1) / NKT_TILES_PER_WG);
   const int64_t n_blk = (rows + 31) / 32;

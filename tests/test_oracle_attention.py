@@ -5,6 +5,10 @@
 * closed forms (first row, identical keys, constant values);
 * invariants (chunked == full sequence, sparse == dense over the compacted sequence, selecting
   every page == dense, gradient sums, convex hull).
+
+The sparse key sets (selected pages plus the own block, and one page list per query page) are
+written out here as boolean masks from the reading of the pages, never taken from the oracle's own
+key-set functions; planted mistakes in those functions must make these pins fail.
 """
 import numpy as np
 import pytest
@@ -26,11 +30,35 @@ def _full_grads(res, L, H_kv, d):
     return dk, dv
 
 
-def _torch_reference(q, k, v, do, q0, scale, kidx_per_g, H_q, H_kv, row_sets=None):
+def _hand_mask(C, L, q0, P, pages=None):
+    """Keys each chunk row may see, written out from the reading of the pages, independently of the
+    oracle's own key-set code: with no page list every earlier token; with one, the P tokens of each
+    listed page (logical page p holds tokens [p*P, (p+1)*P)) plus the chunk's own block
+    [q0, q0 + C); causality (key j <= q0 + t) is applied on top in _torch_reference."""
+    allowed = torch.zeros(C, L, dtype=torch.bool)
+    if pages is None:
+        allowed[:, :] = True
+        return allowed
+    for p in pages:
+        allowed[:, p * P:(p + 1) * P] = True
+    allowed[:, q0:q0 + C] = True
+    return allowed
+
+
+def _hand_mask_per_query_page(C, L, q0, P, lists):
+    """One page list per query page: the rows of chunk tokens [i*P, (i+1)*P) see lists[i] plus the
+    own block."""
+    allowed = torch.zeros(C, L, dtype=torch.bool)
+    for i, pages in enumerate(lists):
+        allowed[i * P:(i + 1) * P] = _hand_mask(C, L, q0, P, pages)[i * P:(i + 1) * P]
+    return allowed
+
+
+def _torch_reference(q, k, v, do, q0, scale, masks, H_q, H_kv):
     """Independent reference with torch SDPA (math path) + autograd, float64.
 
-    kidx_per_g[g]: key tokens every row may see; or, with row_sets, row_sets[g] is a list of
-    (rows, key tokens) pairs giving each row its own key set."""
+    masks[g]: [C][L] boolean, the keys each row of KV head g's query heads may see before the
+    causal cut."""
     C, _, d = q.shape
     L = k.shape[0]
     G = H_q // H_kv
@@ -40,14 +68,8 @@ def _torch_reference(q, k, v, do, q0, scale, kidx_per_g, H_q, H_kv, row_sets=Non
     outs = []
     for h in range(H_q):
         g = h // G
-        allowed = torch.zeros(C, L, dtype=torch.bool)
         qpos = torch.arange(C) + q0
-        if row_sets is None:
-            allowed[:, torch.tensor(kidx_per_g[g])] = True
-        else:
-            for rws, ks in row_sets[g]:
-                allowed[torch.tensor(rws)[:, None], torch.tensor(ks)[None, :]] = True
-        allowed &= torch.arange(L)[None, :] <= qpos[:, None]
+        allowed = masks[g].clone() & (torch.arange(L)[None, :] <= qpos[:, None])
         o = torch.nn.functional.scaled_dot_product_attention(
             tq[:, h, :][None, None], tk[:, g, :][None, None], tv[:, g, :][None, None],
             attn_mask=allowed[None, None], scale=scale)
@@ -70,8 +92,8 @@ def test_matches_torch_sdpa_and_autograd(sparse):
     sel = [[1, 4, 7], [0, 8, 9]] if sparse else None
     o, lse = oracle.chunk_forward(q, k, v, q0, scale, sel=sel, page=P)
     res = oracle.chunk_backward(q, k, v, do, q0, scale, sel=sel, page=P)
-    kidx = [oracle.visible_keys(q0, C, P, None if sel is None else sel[g]) for g in range(H_kv)]
-    to, tdq, tdk, tdv = _torch_reference(q, k, v, do, q0, scale, kidx, H_q, H_kv)
+    masks = [_hand_mask(C, L, q0, P, None if sel is None else sel[g]) for g in range(H_kv)]
+    to, tdq, tdk, tdv = _torch_reference(q, k, v, do, q0, scale, masks, H_q, H_kv)
     dk, dv = _full_grads(res, L, H_kv, d)
     assert np.max(np.abs(o - to)) < 1e-12
     assert np.max(np.abs(res["dq"] - tdq)) < 1e-12
@@ -81,7 +103,7 @@ def test_matches_torch_sdpa_and_autograd(sparse):
     for h in range(H_q):
         g = h // (H_q // H_kv)
         for t in range(C):
-            ks = [j for j in kidx[g] if j <= q0 + t]
+            ks = [j for j in range(L) if masks[g][t, j] and j <= q0 + t]
             s = scale * np.array([q[t, h] @ k[j, g] for j in ks])
             assert abs(lse[h, t] - (s.max() + np.log(np.exp(s - s.max()).sum()))) < 1e-12
 
@@ -187,7 +209,9 @@ def test_sparse_equals_dense_over_compacted_sequence():
     s = 0.4
     o, lse = oracle.chunk_forward(q, k, v, q0, s, sel=sel, page=P)
     res = oracle.chunk_backward(q, k, v, do, q0, s, sel=sel, page=P)
-    toks = oracle.visible_keys(q0, C, P, sel[0])
+    # The compacted key sequence written out by hand: the selected pages' tokens, then the own block.
+    toks = np.concatenate([np.arange(p * P, (p + 1) * P) for p in sel[0]] + [np.arange(q0, q0 + C)])
+    assert np.array_equal(toks, oracle.visible_keys(q0, C, P, sel[0]))
     kc, vc = k[toks], v[toks]
     q0c = len(sel[0]) * P
     oc, lsec = oracle.chunk_forward(q, kc, vc, q0c, s, page=P)
@@ -261,9 +285,8 @@ def test_per_query_page_lists_match_torch_sdpa_and_autograd():
                     [[0, 8, 9], [2, 3, 7], [4, 5, 9], [0, 1, 6]]])
     o, lse = oracle.chunk_forward(q, k, v, q0, scale, sel=sel, page=P)
     res = oracle.chunk_backward(q, k, v, do, q0, scale, sel=sel, page=P)
-    row_sets = [[(list(range(i * P, (i + 1) * P)), oracle.visible_keys(q0, C, P, sel[g][i])) for i in range(C // P)]
-                for g in range(H_kv)]
-    to, tdq, tdk, tdv = _torch_reference(q, k, v, do, q0, scale, None, H_q, H_kv, row_sets=row_sets)
+    masks = [_hand_mask_per_query_page(C, L, q0, P, sel[g]) for g in range(H_kv)]
+    to, tdq, tdk, tdv = _torch_reference(q, k, v, do, q0, scale, masks, H_q, H_kv)
     dk, dv = _full_grads(res, L, H_kv, d)
     assert np.max(np.abs(o - to)) < 1e-12
     assert np.max(np.abs(res["o"] - to)) < 1e-12
@@ -272,7 +295,7 @@ def test_per_query_page_lists_match_torch_sdpa_and_autograd():
     assert np.max(np.abs(dv - tdv)) < 1e-12
     # Keys no list selects get no gradient; the reported keys are the union, ascending.
     for g in range(H_kv):
-        want = np.union1d(np.concatenate([oracle.visible_keys(q0, C, P, sel[g][i]) for i in range(C // P)]), [])
+        want = np.nonzero(masks[g].any(dim=0).numpy())[0]
         assert np.array_equal(res["keys"][g], want)
     # A row subset returns the same rows.
     rows = np.array([1, 6, 13])
@@ -299,3 +322,99 @@ def test_per_query_page_identical_lists_equal_one_list():
         assert np.array_equal(r2["keys"][g], r3["keys"][g])
         assert np.max(np.abs(r2["dk"][g] - r3["dk"][g])) < 1e-12
         assert np.max(np.abs(r2["dv"][g] - r3["dv"][g])) < 1e-12
+
+
+# Planted mistakes in the oracle's key-set code (on the CPU, in this process only): each must make
+# the hand-masked SDPA pin above fail, so the pin really constrains which keys the oracle uses.
+def _broken_visible_keys_no_page_scale(q0, chunk, page, sel_pages=None):
+    if sel_pages is None:
+        return np.arange(q0 + chunk, dtype=np.int64)
+    sel = np.asarray(sel_pages, dtype=np.int64).reshape(-1)
+    toks = (sel[:, None] + np.arange(page, dtype=np.int64)[None, :]).reshape(-1)  # page id not scaled
+    return np.concatenate([toks, np.arange(q0, q0 + chunk, dtype=np.int64)])
+
+
+def _broken_visible_keys_own_block_shift(q0, chunk, page, sel_pages=None):
+    if sel_pages is None:
+        return np.arange(q0 + chunk, dtype=np.int64)
+    sel = np.asarray(sel_pages, dtype=np.int64).reshape(-1)
+    toks = (sel[:, None] * page + np.arange(page, dtype=np.int64)[None, :]).reshape(-1)
+    return np.concatenate([toks, np.arange(q0 + 1, q0 + chunk, dtype=np.int64)])  # own block off by one
+
+
+def _broken_visible_keys_no_own_block(q0, chunk, page, sel_pages=None):
+    if sel_pages is None:
+        return np.arange(q0 + chunk, dtype=np.int64)
+    sel = np.asarray(sel_pages, dtype=np.int64).reshape(-1)
+    return (sel[:, None] * page + np.arange(page, dtype=np.int64)[None, :]).reshape(-1)
+
+
+def _broken_visible_keys_page_shift(q0, chunk, page, sel_pages=None):
+    if sel_pages is None:
+        return np.arange(q0 + chunk, dtype=np.int64)
+    sel = np.asarray(sel_pages, dtype=np.int64).reshape(-1) + 1  # every selected page one later
+    toks = (sel[:, None] * page + np.arange(page, dtype=np.int64)[None, :]).reshape(-1)
+    return np.concatenate([toks, np.arange(q0, q0 + chunk, dtype=np.int64)])
+
+
+def _sparse_pin_errors(sel):
+    """Max-abs differences between the oracle and the hand-masked SDPA reference on one sparse case
+    (O, dQ, dK, dV), with the oracle as it currently stands in this process."""
+    rng = np.random.default_rng(21)
+    H_q, H_kv, d, P, C = 4, 2, 8, 4, 16
+    n_prior = 10
+    q0 = n_prior * P
+    L = q0 + C
+    q, k, v, do = _rand((C, H_q, d), rng), _rand((L, H_kv, d), rng), _rand((L, H_kv, d), rng), _rand((C, H_q, d), rng)
+    scale = 0.37
+    res = oracle.chunk_backward(q, k, v, do, q0, scale, sel=sel, page=P)
+    if np.ndim(sel[0]) == 1:
+        masks = [_hand_mask(C, L, q0, P, sel[g]) for g in range(H_kv)]
+    else:
+        masks = [_hand_mask_per_query_page(C, L, q0, P, sel[g]) for g in range(H_kv)]
+    to, tdq, tdk, tdv = _torch_reference(q, k, v, do, q0, scale, masks, H_q, H_kv)
+    dk, dv = _full_grads(res, L, H_kv, d)
+    return max(np.max(np.abs(res["o"] - to)), np.max(np.abs(res["dq"] - tdq)), np.max(np.abs(dk - tdk)),
+               np.max(np.abs(dv - tdv)))
+
+
+_SEL_SHARED = [[1, 4, 7], [0, 8, 9]]
+_SEL_PER_QPAGE = np.array([[[1, 4, 7], [0, 2, 9], [5, 6, 8], [1, 3, 4]],
+                           [[0, 8, 9], [2, 3, 7], [4, 5, 9], [0, 1, 6]]])
+
+
+@pytest.mark.parametrize("broken", [_broken_visible_keys_no_page_scale, _broken_visible_keys_own_block_shift,
+                                    _broken_visible_keys_no_own_block, _broken_visible_keys_page_shift])
+@pytest.mark.parametrize("sel", [_SEL_SHARED, _SEL_PER_QPAGE], ids=["shared", "per_query_page"])
+def test_planted_key_set_mistakes_fail_the_pin(monkeypatch, broken, sel):
+    assert _sparse_pin_errors(sel) < 1e-12
+    monkeypatch.setattr(oracle.attention, "visible_keys", broken)
+    err = _sparse_pin_errors(sel)
+    assert err > 1e-3, f"planted mistake {broken.__name__} went unnoticed (error {err})"
+
+
+def _broken_key_sets_list_per_row_block(q0, C, page, sel, g, rows):
+    """Per-query-page routing with the query page of a row computed from the wrong page size."""
+    lists = np.asarray(sel[g])
+    if lists.ndim == 1:
+        yield oracle.attention.visible_keys(q0, C, page, lists), np.arange(len(rows))
+        return
+    qpage = np.minimum(rows // (2 * page), lists.shape[0] - 1)
+    for i in range(lists.shape[0]):
+        pos = np.nonzero(qpage == i)[0]
+        if len(pos):
+            yield oracle.attention.visible_keys(q0, C, page, lists[i]), pos
+
+
+def _broken_key_sets_first_list_only(q0, C, page, sel, g, rows):
+    """Every row routed to the first query page's list."""
+    lists = np.asarray(sel[g])
+    first = lists if lists.ndim == 1 else lists[0]
+    yield oracle.attention.visible_keys(q0, C, page, first), np.arange(len(rows))
+
+
+@pytest.mark.parametrize("broken", [_broken_key_sets_list_per_row_block, _broken_key_sets_first_list_only])
+def test_planted_per_query_page_routing_mistakes_fail_the_pin(monkeypatch, broken):
+    assert _sparse_pin_errors(_SEL_PER_QPAGE) < 1e-12
+    monkeypatch.setattr(oracle.attention, "_key_sets", broken)
+    assert _sparse_pin_errors(_SEL_PER_QPAGE) > 1e-3

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int32_t sp = (u / n_rb) % splits;
   const int32_t gi = u / (n_rb * splits);
   const int32_t g = a.kvh0 + gi;
-  const int32_t G = a.G, CG = a.C * G, P = a.page, H = a.h_kv;
+  const int32_t G = a.G, CG = a.C * G, P = a.page;
   // Row blocks never straddle two selection lists: list li owns rows [li*RL, (li+1)*RL).
   const int32_t RL = CG / a.n_lists;
   const int32_t bpl = (RL + 32 * T::NW - 1) / (32 * T::NW);
@@ -92,18 +92,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   }
 
-  // Tile i of the key list -> first key position (-1 when the page is unreadable) and K base.
-  auto tile_src = [&](int32_t i, int32_t& kpos0) -> const uint16_t* {
-    const int32_t pi = i >> tsh, sub = i & ((1 << tsh) - 1);
-    const int32_t lp = list_page(a, g, li, pi);
-    const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
-    if (ph < 0) {
-      kpos0 = -1;
-      return nullptr;
-    }
-    kpos0 = lp * P + sub * BK;
-    return a.kv + (((int64_t)ph * H + g) * 2) * P * D + (int64_t)sub * BK * D;
-  };
+  // Tiles of the key list in order, with their table reads issued a tile ahead.
+  KeyWalk walk = walk_begin(a, g, li, tsh, tb, te);
 
   // Direct global->LDS staging: wave w fills 1 KiB segments w*SEG_PER_WAVE + j of the K and V
   // tiles; lane L lands at (row L / CHR of the segment, physical chunk L % CHR) and so fetches the
@@ -114,8 +104,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int rl = (wave * T::SEG_PER_WAVE + j) * T::ROWS_PER_SEG + lane / T::CHR;
     seg_off[j] = 2u * (uint32_t)(rl * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3));
   }
-  auto load_tile = [&](int32_t i, int stage, int32_t& kp) {
-    const uint16_t* src = tile_src(i, kp);
+  // Stage the walk's next tile (kp: its first key position, -1 when unreadable).
+  auto load_tile = [&](int stage, int32_t& kp) {
+    const uint16_t* src = walk_take<D>(a, walk, kp);
     if (src == nullptr) src = a.kv;  // unreadable page: any in-bounds bytes, the tile is masked
     uint16_t* kt = lds + stage * 2 * T::TILE;
     const char* ksrc = reinterpret_cast<const char*>(src);
@@ -150,14 +141,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int dt = 0; dt < T::DT; ++dt) oacc[dt] = (f32x16){};
 
   int32_t kpos_next = -1;
-  if (tb < te) load_tile(tb, 0, kpos_next);
+  if (tb < te) load_tile(0, kpos_next);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int32_t i = tb; i < te; ++i) {
     const int cur = (i - tb) & 1;
     const int32_t kpos0 = kpos_next;
-    if (i + 1 < te) load_tile(i + 1, cur ^ 1, kpos_next);
+    if (i + 1 < te) load_tile(cur ^ 1, kpos_next);
     const char* kt = reinterpret_cast<const char*>(lds + cur * 2 * T::TILE);
     const char* vt = kt + 2 * T::TILE;
 

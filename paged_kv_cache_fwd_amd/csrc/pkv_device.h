@@ -146,6 +146,98 @@ __device__ __forceinline__ int32_t phys_page(const int32_t* bt, int32_t n_bt, in
 // Number of prior pages in the key list (selected count when sparse).
 __device__ __forceinline__ int32_t list_prior(const AttnArgs& a) { return a.sel ? a.n_sel : a.n_prior; }
 
+// Walk over the 64-key tiles of a chunk's key list with the table reads issued ahead of use.
+// Tile i lies in list entry i >> tsh (tsh = log2 of tiles per page). Resolving it takes a
+// selection read (prior entries of a sparse list) and then a block-table read, each a round trip
+// to the L2; issued when the tile's K/V loads are due, they would stall every wave of the
+// workgroup at the start of each tile. walk_take(i) instead uses the block-table entry of tile i
+// read during the previous call and the selection entry of tile i + 1 read then too, and issues
+// the reads for tiles i + 1 (block table) and i + 2 (selection). The kernels wait for all their
+// memory operations at the end of each tile, so those values have landed by the next call.
+// Every value is wave-uniform; validation and error flags are those of list_page / phys_page.
+struct KeyWalk {
+  int32_t g, li, tsh, te;
+  int32_t t;     // tile the next walk_take resolves
+  int32_t lp;    // its logical page (-1: unreadable or past the list)
+  int32_t btv;   // block-table entry of lp (read ahead)
+  int32_t selv;  // selection entry of tile t + 1 (read ahead; prior entries of sparse lists only)
+};
+
+// Logical page of tile t from the selection entry `selv` read for it (sparse prior entries) or
+// directly (dense lists, the own block); -1 (flagged) when out of range or past the list.
+__device__ __forceinline__ int32_t walk_page(const AttnArgs& a, const KeyWalk& w, int32_t t, int32_t selv) {
+  if (t >= w.te) return -1;
+  const int32_t pi = t >> w.tsh;
+  int32_t lp;
+  if (a.sel == nullptr) {
+    lp = pi;
+  } else if (pi >= a.n_sel) {
+    lp = a.n_prior + (pi - a.n_sel);
+  } else {
+    lp = __builtin_amdgcn_readfirstlane(selv);
+    if (lp < 0 || lp >= a.n_prior) {
+      flag_error(a.err, 2);
+      return -1;
+    }
+  }
+  if (lp >= a.n_bt) {
+    flag_error(a.err, 3);
+    return -1;
+  }
+  return lp;
+}
+
+__device__ __forceinline__ bool walk_needs_sel(const AttnArgs& a, const KeyWalk& w, int32_t t) {
+  return a.sel != nullptr && t < w.te && (t >> w.tsh) < a.n_sel;
+}
+
+__device__ __forceinline__ int32_t walk_sel_read(const AttnArgs& a, const KeyWalk& w, int32_t t) {
+  return a.sel[((size_t)w.g * a.n_lists + w.li) * a.n_sel + (t >> w.tsh)];
+}
+
+// Start the walk at tile t0 (its reads complete before its walk_take returns).
+__device__ __forceinline__ KeyWalk walk_begin(const AttnArgs& a, int32_t g, int32_t li, int32_t tsh, int32_t t0,
+                                              int32_t te) {
+  KeyWalk w;
+  w.g = g;
+  w.li = li;
+  w.tsh = tsh;
+  w.te = te;
+  w.t = t0;
+  w.btv = 0;
+  w.selv = 0;
+  const int32_t s0 = walk_needs_sel(a, w, t0) ? walk_sel_read(a, w, t0) : 0;
+  w.lp = walk_page(a, w, t0, s0);
+  if (w.lp >= 0) w.btv = a.bt[w.lp];
+  if (walk_needs_sel(a, w, t0 + 1)) w.selv = walk_sel_read(a, w, t0 + 1);
+  return w;
+}
+
+// K base of tile w.t (nullptr when unreadable; kpos0 = -1 then, else the tile's first key
+// position) and the reads for the following tiles. D is the head dimension.
+template <int D>
+__device__ __forceinline__ const uint16_t* walk_take(const AttnArgs& a, KeyWalk& w, int32_t& kpos0) {
+  const uint16_t* src = nullptr;
+  kpos0 = -1;
+  if (w.lp >= 0) {
+    const int32_t ph = __builtin_amdgcn_readfirstlane(w.btv);
+    if (ph < 0 || ph >= a.n_pool_pages) {
+      flag_error(a.err, 1);
+    } else {
+      const int32_t sub = w.t & ((1 << w.tsh) - 1);
+      kpos0 = w.lp * a.page + sub * 64;
+      src = a.kv + (((int64_t)ph * a.h_kv + w.g) * 2) * a.page * D + (int64_t)sub * 64 * D;
+    }
+  }
+  const int32_t t1 = w.t + 1;
+  const int32_t lp1 = walk_page(a, w, t1, w.selv);
+  if (lp1 >= 0) w.btv = a.bt[lp1];
+  if (walk_needs_sel(a, w, t1 + 1)) w.selv = walk_sel_read(a, w, t1 + 1);
+  w.lp = lp1;
+  w.t = t1;
+  return src;
+}
+
 // XCD-aware block ordering: workgroups are dispatched round-robin over 8 XCDs, so consecutive
 // logical units are gathered onto one XCD (sharing its L2). Bijective on [0, n).
 __device__ __forceinline__ int32_t xcd_remap(int32_t bid, int32_t n) {

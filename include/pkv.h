@@ -130,8 +130,29 @@ int paged_kv_grad_offload(pkv_pool* host, const int32_t* host_bt_dev, int32_t n_
 int paged_kv_copy(const pkv_pool* src, pkv_pool* dst, uint32_t what, int32_t first_page, int32_t n_pages,
                   void* stream);
 
-/* Synchronise the device and release the pool. NULL is a no-op returning PKV_OK. */
+/* Release a pool and all its memory (the paged memory manager owns its pages: pt 2.B, it 2.B).
+ * Synchronises the device first, so no enqueued kernel still reads the pages. NULL is a no-op
+ * returning PKV_OK. */
 int paged_kv_free(pkv_pool* pool);
+
+/*
+ * Page allocation from the pool's free list (pt 2.B, it 2.B: the paged memory manager hands out
+ * fixed-size pages, so appending never reallocates or copies, and released pages are reused with no
+ * fragmentation). A new pool has every physical page free; they are handed out from page 0 up, and
+ * afterwards the most recently released page first. paged_kv_page_alloc takes n pages and writes
+ * their physical ids to pages_host (host memory, n entries), which the caller places in its block
+ * table; with fewer than n pages free it fails with PKV_E_NOMEM and takes none.
+ * paged_kv_page_release returns n pages; an id outside the pool, a page that is not allocated or an
+ * id listed twice fails the call with PKV_E_INVALID and releases none. paged_kv_pages_available
+ * returns the number of free pages (a negative status for a NULL pool). These calls only keep host
+ * bookkeeping: nothing is enqueued or synchronised, so the caller orders the reuse of a released
+ * page after the kernels that still read or write it. The three calls are thread-safe per pool.
+ * Block tables need not come from the allocator: kernels accept any table whose entries lie in
+ * the pool.
+ */
+int paged_kv_page_alloc(pkv_pool* pool, int32_t n, int32_t* pages_host);
+int paged_kv_page_release(pkv_pool* pool, int32_t n, const int32_t* pages_host);
+int32_t paged_kv_pages_available(const pkv_pool* pool);
 
 /* Shape of a pool (any output pointer may be NULL). */
 int paged_kv_info(const pkv_pool* pool, int32_t* n_pages, int32_t* page_size, int32_t* n_kv_heads,
@@ -157,7 +178,9 @@ int paged_kv_append(pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t
                     const uint16_t* k_dev, const uint16_t* v_dev, void* stream);
 
 /* Zero the gradient blocks of logical pages [0, n_pages) through bt_dev, or of the whole pool when
- * bt_dev is NULL. Uses a fill kernel (no memset node), so it may be captured in a graph. */
+ * bt_dev is NULL: the gradient pages accumulate in place across backward calls (pt 2.B, it 2.B), so
+ * a new accumulation starts from cleared pages. Uses a fill kernel (no memset node), so it may be
+ * captured in a graph. Errors: PKV_E_STATE (no gradient pages), PKV_E_INVALID (n_pages < 0). */
 int paged_kv_zero_grad(pkv_pool* pool, const int32_t* bt_dev, int32_t n_pages, void* stream);
 
 /*
@@ -210,13 +233,14 @@ int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, 
  *           page_size (the row's query page, pt 2.C) when n_lists == C / page_size. A selection
  *           of no page (n_sel == 0: the own block only) still passes a non-NULL sel_dev, which
  *           is then not read. Dense calls take n_lists = 1.
- * with softmax(scale * q.k). The own block (logical pages [n_prior, n_prior + C/page_size)) must
+ * with softmax(scale * q.k), scale > 0 and finite. The own block (logical pages [n_prior, n_prior + C/page_size)) must
  * already be appended. Only KV heads [kvh0, kvh0 + n_kvh) and their query heads are computed.
  * Outputs: o_dev [C][H_q][head_dim] bf16 and lse_dev [H_q][C] fp32 for those heads.
  * ws_dev: at least chunk_attn_fwd_ws_bytes(...) bytes of device scratch (may be NULL if 0). The
  * *_ws_bytes queries take n_sel < 0 for dense calls, and the call's n_lists.
- * Errors: PKV_E_INVALID (shapes, alignment, n_sel or n_lists out of range), PKV_E_RANGE (block
- * table too short), PKV_E_STATE (host-tier pool), PKV_E_NOMEM (workspace too small).
+ * Errors: PKV_E_INVALID (shapes, alignment, n_sel or n_lists out of range, scale not a positive
+ * finite number), PKV_E_RANGE (block table too short), PKV_E_STATE (host-tier pool), PKV_E_NOMEM
+ * (workspace too small).
  */
 size_t chunk_attn_fwd_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t n_sel, int32_t n_lists,
                                int32_t n_kvh, int32_t C, int32_t H_q);
@@ -268,6 +292,21 @@ int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_
  * Errors: PKV_E_INVALID for non-positive sizes or a NULL out_dev.
  */
 int pkv_mfma_probe(int32_t n_workgroups, int32_t iters, float* out_dev, double* flop, void* stream);
+
+/*
+ * Diagnostic: the device's fp32 atomic-add rate in the pattern of a gradient flush into pages
+ * (pt 2.B, it 2.B: key/value gradients are added in place with atomic adds). Enqueues n_workgroups
+ * workgroups of 256 threads; workgroup w adds 1.0 to each of the region_elems floats of region
+ * w % n_regions of buf_dev (n_regions * region_elems floats, device), consecutive threads on
+ * consecutive floats. With n_regions == n_workgroups every float gets one add; with fewer regions,
+ * n_workgroups / n_regions workgroups add into the same floats concurrently. After the launch each
+ * float of region r has grown by the number of workgroups w < n_workgroups with w % n_regions == r.
+ * *bytes (host, may be NULL) receives the bytes added (n_workgroups * region_elems * 4); the caller
+ * times the launch. Errors: PKV_E_INVALID for non-positive sizes, n_regions > n_workgroups, a
+ * buffer over 2^31 floats or a NULL buf_dev.
+ */
+int pkv_atomic_probe(int32_t n_workgroups, int32_t n_regions, int32_t region_elems, float* buf_dev, double* bytes,
+                     void* stream);
 
 /*
  * Per-kernel timing (tracing aid, off by default). While enabled, every kernel launch of the

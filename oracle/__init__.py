@@ -27,6 +27,7 @@ from .attention import (
     group_backward,
     chunk_forward,
     chunk_backward,
+    key_gradients,
 )
 from .selection import (
     page_key_sums,
@@ -40,6 +41,6 @@ from .selection import (
 )
 
 __all__ = [
-    "widen_bf16", "visible_keys", "group_forward", "group_backward", "chunk_forward", "chunk_backward",
+    "widen_bf16", "visible_keys", "group_forward", "group_backward", "chunk_forward", "chunk_backward", "key_gradients",
     "page_key_sums", "page_reps", "query_sum", "page_scores", "select_pages", "n_selected", "topk_pages",
 ]

@@ -199,3 +199,42 @@ def chunk_backward(q, kseq, vseq, do, q0, scale, sel=None, page=None, rows=None,
         dks.append(dkg)
         dvs.append(dvg)
     return {"dq": dq, "keys": keys, "dk": dks, "dv": dvs, "o": o_all, "lse": lse_all}
+
+
+def key_gradients(q, kseq, vseq, do, q0, scale, keys, lse, dd, dtype=np.float64, block=512):
+    """dK and dV of chosen keys from the row statistics of a finished forward (pt 2.B / it 2.B: the
+    backward adds these into the keys' gradient pages).
+
+    For each KV head g in ``keys`` (a dict g -> logical key tokens, each a subset of the keys every
+    chunk row of that head may see; causality is applied here) and each of its query heads h, every
+    chunk row t contributes, with P_tj = exp(scale q_t.k_j - LSE_t) for key j <= q0 + t (else 0) and
+    dS_tj = P_tj (dO_t.v_j - D_t):
+        dK_j += scale dS_tj q_t,    dV_j += P_tj dO_t.
+    lse [H_q][C] and dd [H_q][C] (D_t = dO_t.O_t) come from the forward; q, do [C][H_q][d];
+    kseq, vseq [L][H_kv][d]. Returns {g: (dK [n_g][d], dV [n_g][d])}. This is the backward of
+    ``group_backward`` written per key from the stored statistics, so that a few keys' gradients can
+    be evaluated without recomputing every key's."""
+    q, k, v = _prep(q, kseq, vseq, dtype)
+    do = widen_bf16(do).astype(dtype, copy=False)
+    lse = np.asarray(lse, dtype=dtype)
+    dd = np.asarray(dd, dtype=dtype)
+    C, H_q, d = q.shape
+    H_kv = k.shape[1]
+    G = H_q // H_kv
+    out = {}
+    for g, kidx in keys.items():
+        kidx = np.asarray(kidx, dtype=np.int64)
+        kg, vg = k[kidx, g, :], v[kidx, g, :]
+        dk = np.zeros((len(kidx), d), dtype=dtype)
+        dv = np.zeros((len(kidx), d), dtype=dtype)
+        for hh in range(G):
+            h = g * G + hh
+            for t0 in range(0, C, block):
+                t = np.arange(t0, min(t0 + block, C))
+                visible = kidx[None, :] <= (q0 + t)[:, None]
+                p = np.where(visible, np.exp(scale * (q[t, h, :] @ kg.T) - lse[h, t][:, None]), 0.0)
+                ds = p * (do[t, h, :] @ vg.T - dd[h, t][:, None])
+                dk += scale * (ds.T @ q[t, h, :])
+                dv += p.T @ do[t, h, :]
+        out[g] = (dk, dv)
+    return out

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import warnings
 from typing import Optional
 
 import torch
@@ -27,7 +28,8 @@ EXPORTED = (
     "page_topk_select", "chunk_attn_fwd_ws_bytes", "chunk_attn_fwd", "chunk_attn_bwd_ws_bytes",
     "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "paged_kv_copy", "pkv_mfma_probe",
     "pkv_timing_enable", "pkv_timing_collect",
-    "pkv_timing_get",
+    "pkv_timing_get", "paged_kv_page_alloc", "paged_kv_page_release", "paged_kv_pages_available",
+    "pkv_atomic_probe",
 )
 
 
@@ -83,6 +85,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "pkv_timing_collect": (ctypes.c_int, []),
         "pkv_timing_get": (_I, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_I),
                                 ctypes.POINTER(ctypes.c_double)]),
+        "paged_kv_page_alloc": (_I, [_P, _I, ctypes.POINTER(_I)]),
+        "paged_kv_page_release": (_I, [_P, _I, ctypes.POINTER(_I)]),
+        "paged_kv_pages_available": (_I, [_P]),
+        "pkv_atomic_probe": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -182,12 +188,44 @@ class Pool:
     def check(self):
         _check(load().paged_kv_check(self.handle))
 
+    def alloc_pages(self, n: int) -> list:
+        """Take n physical pages from the pool's free list (raises PkvError PKV_E_NOMEM, taking none,
+        when fewer are free); returns their ids for the caller's block table."""
+        buf = (_I * max(n, 1))()
+        _check(load().paged_kv_page_alloc(self.handle, n, buf))
+        return [int(buf[i]) for i in range(n)]
 
-def _ws(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    def release_pages(self, pages) -> None:
+        """Return pages to the free list (all or none: an id outside the pool, not allocated, or
+        repeated raises PKV_E_INVALID)."""
+        pages = [int(p) for p in pages]
+        buf = (_I * max(len(pages), 1))(*pages)
+        _check(load().paged_kv_page_release(self.handle, len(pages), buf))
+
+    def pages_available(self) -> int:
+        n = load().paged_kv_pages_available(self.handle)
+        if n < 0:
+            _check(n)
+        return n
+
+
+class WorkspaceAllocationWarning(UserWarning):
+    """A hot-path call had to allocate its own device workspace (the caller passed none, or one too
+    small): pass ws= (sized by the *_ws_bytes queries) to keep the step free of allocations."""
+
+
+_warned_ws = set()
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor], call: str) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return ws
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
+    if call not in _warned_ws:  # once per entry point
+        _warned_ws.add(call)
+        warnings.warn(f"{call}: no workspace of {nbytes} bytes was passed, so one is allocated on every such call; "
+                      "pass ws= to avoid allocating on the hot path", WorkspaceAllocationWarning, stacklevel=3)
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
@@ -211,12 +249,16 @@ def page_topk_select(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor
     if sel.numel() < need:
         raise ValueError(f"sel holds {sel.numel()} entries, {need} needed")
     nb = lib.page_topk_ws_bytes(pool.handle, n_prior, C, H_q, n_lists)
-    ws = _ws(nb, q.device, ws)
+    ws = _ws(nb, q.device, ws, "page_topk_select")
     out_n = _I(0)
     _check(lib.page_topk_select(pool.handle, _ptr(bt), bt.numel(), n_prior, _ptr(q), C, H_q, top_k, n_local,
                                 n_lists, _ptr(sel), ctypes.byref(out_n), _ptr(ws), nb, _stream(stream)))
     assert out_n.value == n_sel
     return sel if tuple(sel.shape) == shape else sel.view(-1)[:need].view(shape)
+
+
+def page_topk_ws_bytes(pool: Pool, n_prior: int, C: int, H_q: int, n_lists: int = 1) -> int:
+    return load().page_topk_ws_bytes(pool.handle, n_prior, C, H_q, n_lists)
 
 
 def chunk_attn_fwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int,
@@ -259,7 +301,7 @@ def chunk_attn_fwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
     _need(o, torch.bfloat16, "o", q.shape)
     _need(lse, torch.float32, "lse", (H_q, C))
     nb = lib.chunk_attn_fwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
-    ws = _ws(nb, q.device, ws)
+    ws = _ws(nb, q.device, ws, "chunk_attn_fwd")
     _check(lib.chunk_attn_fwd(pool.handle, _ptr(bt), bt.numel(), n_prior, _sel_ptr(sel, bt), max(n_sel, 0), n_lists,
                               kvh0, n_kvh,
                               _ptr(q), C, H_q, float(scale), _ptr(o), _ptr(lse), _ptr(ws), nb, _stream(stream)))
@@ -287,7 +329,7 @@ def chunk_attn_bwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
         dq = torch.empty_like(q)
     _need(dq, torch.bfloat16, "dq", q.shape)
     nb = lib.chunk_attn_bwd_ws_bytes(pool.handle, n_prior, n_sel, n_lists, n_kvh, C, H_q)
-    ws = _ws(nb, q.device, ws)
+    ws = _ws(nb, q.device, ws, "chunk_attn_bwd")
     _check(lib.chunk_attn_bwd(pool.handle, _ptr(bt), bt.numel(), gpool.handle, _ptr(gbt), gbt.numel(), n_prior,
                               _sel_ptr(sel, bt), max(n_sel, 0), n_lists, kvh0, n_kvh, _ptr(q), _ptr(o), _ptr(dout), _ptr(lse), C,
                               H_q, float(scale), _ptr(dq), _ptr(ws), nb, _stream(stream)))
@@ -334,6 +376,16 @@ def mfma_probe(n_workgroups: int, iters: int, out: torch.Tensor, stream=None) ->
     flop = ctypes.c_double(0.0)
     _check(load().pkv_mfma_probe(n_workgroups, iters, _ptr(out), ctypes.byref(flop), _stream(stream)))
     return flop.value
+
+
+def atomic_probe(n_workgroups: int, n_regions: int, region_elems: int, buf: torch.Tensor, stream=None) -> float:
+    """Enqueue the fp32 atomic-add diagnostic on buf ([n_regions * region_elems] float32); returns the
+    bytes it adds (the caller times it)."""
+    _need(buf, torch.float32, "buf", (n_regions * region_elems,))
+    nbytes = ctypes.c_double(0.0)
+    _check(load().pkv_atomic_probe(n_workgroups, n_regions, region_elems, _ptr(buf), ctypes.byref(nbytes),
+                                   _stream(stream)))
+    return nbytes.value
 
 
 def timing_enable(on: bool = True):

@@ -55,4 +55,24 @@ double mfma_probe_flop(int32_t n_wg, int32_t iters) {
   return (double)n_wg * (kProbeThreads / 64) * (double)iters * kProbeChains * (32.0 * 32.0 * 16.0 * 2.0);
 }
 
+// Diagnostic: the rate of fp32 atomic adds into global memory, in the pattern a gradient flush
+// makes: workgroup w adds 1.0 to every element of region w % n_regions, 256 threads striding over
+// it, so consecutive lanes hit consecutive addresses. With n_regions equal to the workgroup count
+// every element receives one add (the key-major dK/dV pass's single flush per gradient element);
+// with fewer regions n_workgroups / n_regions workgroups add into each element (a query-major
+// backward's per-row-block partials of one key tile).
+constexpr int kAtomicProbeThreads = 256;
+
+__global__ __launch_bounds__(kAtomicProbeThreads) void k_atomic_probe(float* __restrict__ buf, int32_t n_regions,
+                                                                    int32_t region_elems) {
+  float* r = buf + (int64_t)(blockIdx.x % (uint32_t)n_regions) * region_elems;
+  for (int32_t i = threadIdx.x; i < region_elems; i += kAtomicProbeThreads) unsafeAtomicAdd(r + i, 1.0f);
+}
+
+hipError_t launch_atomic_probe(int32_t n_wg, int32_t n_regions, int32_t region_elems, float* buf, hipStream_t s) {
+  hipLaunchKernelGGL(k_atomic_probe, dim3((unsigned)n_wg), dim3(kAtomicProbeThreads), 0, s, buf, n_regions,
+                     region_elems);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

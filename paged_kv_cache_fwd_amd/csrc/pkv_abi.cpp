@@ -18,6 +18,14 @@
 #include "../../include/pkv.h"
 #include "pkv_internal.h"
 
+// Free list of a pool's physical pages. Pages are all the same size, so a page freed anywhere can
+// serve any later request: the pool never fragments and nothing is ever moved.
+struct pkv_page_alloc {
+  std::mutex mu;
+  std::vector<int32_t> free_pages;  // stack: the most recently released page is handed out first
+  std::vector<uint8_t> is_free;     // per physical page
+};
+
 namespace {
 
 thread_local std::string g_err;
@@ -52,6 +60,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int check_attn(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const int32_t* sel,
                int32_t n_sel, int32_t n_lists, int32_t kvh0, int32_t n_kvh, const uint16_t* q, int32_t C,
                int32_t H_q, float scale) {
+  // A non-positive scale has no softmax reading (scale 0 turns the running maximum into inf * 0,
+  // a negative one inverts it), so it is rejected before anything else.
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PKV_E_INVALID, "scale=%g must be a positive finite number", (double)scale);
   if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
   if (pool->flags & PKV_HOST_TIER)
     return fail(PKV_E_STATE, "attention reads device pages; gather host-tier pages into a device pool first");
@@ -75,7 +87,6 @@ int check_attn(const pkv_pool* pool, const int32_t* bt, int32_t n_bt, int32_t n_
   } else if (n_lists != 1) {
     return fail(PKV_E_INVALID, "dense attention takes n_lists = 1 (got %d)", n_lists);
   }
-  if (!std::isfinite(scale)) return fail(PKV_E_INVALID, "scale is not finite");
   return PKV_OK;
 }
 
@@ -297,6 +308,21 @@ int pkv_mfma_probe(int32_t n_workgroups, int32_t iters, float* out_dev, double* 
   return PKV_OK;
 }
 
+int pkv_atomic_probe(int32_t n_workgroups, int32_t n_regions, int32_t region_elems, float* buf_dev, double* bytes,
+                     void* stream) {
+  if (n_workgroups <= 0 || n_regions <= 0 || region_elems <= 0)
+    return fail(PKV_E_INVALID, "n_workgroups, n_regions and region_elems must be > 0");
+  if (n_regions > n_workgroups) return fail(PKV_E_INVALID, "n_regions=%d exceeds n_workgroups=%d", n_regions, n_workgroups);
+  if ((int64_t)n_regions * region_elems > ((int64_t)1 << 31))
+    return fail(PKV_E_INVALID, "buffer of %lld floats too large", (long long)n_regions * region_elems);
+  if (!buf_dev) return fail(PKV_E_INVALID, "buf_dev is NULL");
+  if (bytes) *bytes = (double)n_workgroups * region_elems * sizeof(float);
+  hipError_t e = pkv::launch_atomic_probe(n_workgroups, n_regions, region_elems, buf_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "atomic probe launch");
+  ok();
+  return PKV_OK;
+}
+
 int pkv_timing_enable(int on) {
   std::lock_guard<std::mutex> lk(pkv::g_tmu);
   pkv::g_timing = on != 0;
@@ -361,11 +387,29 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
   p->grad_host = nullptr;
   p->rep = nullptr;
   p->err = nullptr;
+  p->alloc = new (std::nothrow) pkv_page_alloc();
+  if (!p->alloc) {
+    delete p;
+    return fail(PKV_E_NOMEM, "out of host memory");
+  }
+  try {
+    p->alloc->free_pages.resize((size_t)n_pages);
+    p->alloc->is_free.assign((size_t)n_pages, 1);
+  } catch (const std::bad_alloc&) {
+    delete p->alloc;
+    delete p;
+    return fail(PKV_E_NOMEM, "out of host memory for the page free list");
+  }
+  for (int32_t i = 0; i < n_pages; ++i) p->alloc->free_pages[(size_t)i] = n_pages - 1 - i;  // page 0 first
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) {
+    delete p->alloc;
     delete p;
     return hip_fail(e, "hipGetDevice");
   }
+  // Sizes are taken before anything can fail: cleanup() deletes p, and the error messages below
+  // still report them.
+  const size_t kvb = kv_bytes(*p), gb = grad_bytes(*p);
   auto cleanup = [&]() {
     if (p->kv_host) (void)hipHostFree(p->kv_host);
     else if (p->kv) (void)hipFree(p->kv);
@@ -373,6 +417,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
     else if (p->grad) (void)hipFree(p->grad);
     if (p->rep) (void)hipFree(p->rep);
     if (p->err) (void)hipFree(p->err);
+    delete p->alloc;
     delete p;
   };
   if (getenv("PKV_FAIL_HOST_ALLOC") && (flags & PKV_HOST_TIER)) {
@@ -385,7 +430,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
       p->kv_host = nullptr;
       (void)hipGetLastError();
       cleanup();
-      return fail(PKV_E_NOMEM, "hipHostMalloc(%zu bytes): %s", kv_bytes(*p), hipGetErrorString(e));
+      return fail(PKV_E_NOMEM, "hipHostMalloc(%zu bytes): %s", kvb, hipGetErrorString(e));
     }
     void* dptr = nullptr;
     e = hipHostGetDevicePointer(&dptr, p->kv_host, 0);
@@ -401,7 +446,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
       p->kv = nullptr;
       (void)hipGetLastError();
       cleanup();
-      return fail(PKV_E_NOMEM, "hipMalloc(%zu bytes) for KV pages: %s", kv_bytes(*p), hipGetErrorString(e));
+      return fail(PKV_E_NOMEM, "hipMalloc(%zu bytes) for KV pages: %s", kvb, hipGetErrorString(e));
     }
     e = hipMemset(p->kv, 0, kv_bytes(*p));
     if (e != hipSuccess) {
@@ -415,7 +460,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
       p->grad_host = nullptr;
       (void)hipGetLastError();
       cleanup();
-      return fail(PKV_E_NOMEM, "hipHostMalloc(%zu bytes) for gradient pages: %s", grad_bytes(*p),
+      return fail(PKV_E_NOMEM, "hipHostMalloc(%zu bytes) for gradient pages: %s", gb,
                   hipGetErrorString(e));
     }
     void* gptr = nullptr;
@@ -432,7 +477,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
       p->grad = nullptr;
       (void)hipGetLastError();
       cleanup();
-      return fail(PKV_E_NOMEM, "hipMalloc(%zu bytes) for gradient pages: %s", grad_bytes(*p), hipGetErrorString(e));
+      return fail(PKV_E_NOMEM, "hipMalloc(%zu bytes) for gradient pages: %s", gb, hipGetErrorString(e));
     }
     e = hipMemset(p->grad, 0, grad_bytes(*p));
     if (e != hipSuccess) {
@@ -467,10 +512,64 @@ int paged_kv_free(pkv_pool* pool) {
   else if (pool->grad) (void)hipFree(pool->grad);
   if (pool->rep) (void)hipFree(pool->rep);
   if (pool->err) (void)hipFree(pool->err);
+  delete pool->alloc;
   delete pool;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize in paged_kv_free");
   ok();
   return PKV_OK;
+}
+
+int paged_kv_page_alloc(pkv_pool* pool, int32_t n, int32_t* pages_host) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (n < 0) return fail(PKV_E_INVALID, "n=%d < 0", n);
+  if (n > 0 && !pages_host) return fail(PKV_E_INVALID, "pages_host is NULL");
+  std::lock_guard<std::mutex> lk(pool->alloc->mu);
+  auto& fl = pool->alloc->free_pages;
+  if ((size_t)n > fl.size())
+    return fail(PKV_E_NOMEM, "%d pages requested, %zu of %d free", n, fl.size(), pool->n_pages);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t pg = fl.back();
+    fl.pop_back();
+    pool->alloc->is_free[(size_t)pg] = 0;
+    pages_host[i] = pg;
+  }
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_page_release(pkv_pool* pool, int32_t n, const int32_t* pages_host) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  if (n < 0) return fail(PKV_E_INVALID, "n=%d < 0", n);
+  if (n > 0 && !pages_host) return fail(PKV_E_INVALID, "pages_host is NULL");
+  std::lock_guard<std::mutex> lk(pool->alloc->mu);
+  auto& fr = pool->alloc->is_free;
+  // Validate everything first (ids in range, allocated, no repeats), then release: a failed call
+  // changes nothing.
+  int32_t i = 0;
+  for (; i < n; ++i) {
+    const int32_t pg = pages_host[i];
+    if (pg < 0 || pg >= pool->n_pages || fr[(size_t)pg] != 0) break;
+    fr[(size_t)pg] = 2;  // marked for this call
+  }
+  if (i < n) {
+    const int32_t bad = pages_host[i];
+    for (int32_t j = 0; j < i; ++j) fr[(size_t)pages_host[j]] = 0;
+    if (bad < 0 || bad >= pool->n_pages) return fail(PKV_E_INVALID, "page %d outside the pool (%d pages)", bad, pool->n_pages);
+    return fail(PKV_E_INVALID, "page %d is not allocated (already free, or listed twice)", bad);
+  }
+  for (int32_t j = 0; j < n; ++j) {
+    fr[(size_t)pages_host[j]] = 1;
+    pool->alloc->free_pages.push_back(pages_host[j]);
+  }
+  ok();
+  return PKV_OK;
+}
+
+int32_t paged_kv_pages_available(const pkv_pool* pool) {
+  if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
+  std::lock_guard<std::mutex> lk(pool->alloc->mu);
+  ok();
+  return (int32_t)pool->alloc->free_pages.size();
 }
 
 int paged_kv_info(const pkv_pool* pool, int32_t* n_pages, int32_t* page_size, int32_t* n_kv_heads,
@@ -584,10 +683,11 @@ size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int3
   return pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d, n_lists);
 }
 
-int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
-                     const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
-                     int32_t n_lists, int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes,
-                     void* stream) {
+// Checks of page_topk_select; on success *ws_need is the workspace the call needs and *n_sel the
+// selection length.
+static int check_topk(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior, const uint16_t* q_dev,
+                      int32_t C, int32_t H_q, int32_t top_k, int32_t n_local, int32_t n_lists, const int32_t* sel_dev,
+                      const int32_t* n_sel_out, size_t* ws_need, int32_t* n_sel, bool* needs_ws) {
   if (!pool) return fail(PKV_E_INVALID, "pool is NULL");
   if (!bt_dev || !q_dev || !n_sel_out) return fail(PKV_E_INVALID, "NULL block table, q or n_sel_out");
   if (!aligned16(q_dev)) return fail(PKV_E_INVALID, "q must be 16-byte aligned");
@@ -600,10 +700,24 @@ int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, 
     return fail(PKV_E_INVALID, "n_lists=%d must be 1 or C / page_size", n_lists);
   const int32_t n_cand = n_prior > n_local ? n_prior - n_local : 0;
   const int32_t kk = std::min(top_k, n_cand);
-  const int32_t n_sel = kk + (n_prior - n_cand);
-  if (n_sel > 0 && !sel_dev) return fail(PKV_E_INVALID, "sel is NULL");
-  const size_t ws_need = pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d, n_lists);
-  if (ws_bytes < ws_need || (!ws_dev && kk > 0 && kk < n_cand))
+  *n_sel = kk + (n_prior - n_cand);
+  if (*n_sel > 0 && !sel_dev) return fail(PKV_E_INVALID, "sel is NULL");
+  *ws_need = pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d, n_lists);
+  *needs_ws = kk > 0 && kk < n_cand;
+  return PKV_OK;
+}
+
+int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
+                     const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
+                     int32_t n_lists, int32_t* sel_dev, int32_t* n_sel_out, void* ws_dev, size_t ws_bytes,
+                     void* stream) {
+  size_t ws_need = 0;
+  int32_t n_sel = 0;
+  bool needs_ws = false;
+  int rc = check_topk(pool, bt_dev, n_bt, n_prior, q_dev, C, H_q, top_k, n_local, n_lists, sel_dev, n_sel_out,
+                      &ws_need, &n_sel, &needs_ws);
+  if (rc != PKV_OK) return rc;
+  if (ws_bytes < ws_need || (!ws_dev && needs_ws))
     return fail(PKV_E_NOMEM, "workspace too small: %zu < %zu bytes", ws_bytes, ws_need);
   *n_sel_out = n_sel;
   hipError_t e = pkv::launch_topk(*pool, bt_dev, n_bt, n_prior, q_dev, C, H_q, top_k, n_local, n_lists, sel_dev,

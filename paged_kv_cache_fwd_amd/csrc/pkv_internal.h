@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct pkv_page_alloc;  // host-side free list of physical pages (pkv_abi.cpp)
+
 struct pkv_pool {
   int32_t n_pages;
   int32_t page;
@@ -18,6 +20,7 @@ struct pkv_pool {
   void* grad_host;    // host allocation of PKV_HOST_GRADS gradient pages (NULL otherwise)
   float* rep;         // fp32 representative key per (page, head)
   int32_t* err;       // device word: nonzero once a kernel met an out-of-range table entry
+  pkv_page_alloc* alloc;  // free list of physical pages handed out by paged_kv_page_alloc
 };
 
 namespace pkv {
@@ -108,6 +111,7 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
 hipError_t launch_fwd(const AttnArgs& a, const FwdPlan& plan, uint16_t* o, float* lse, void* ws, hipStream_t s);
 hipError_t launch_mfma_probe(int32_t n_wg, int32_t iters, float* out, hipStream_t s);
 double mfma_probe_flop(int32_t n_wg, int32_t iters);
+hipError_t launch_atomic_probe(int32_t n_wg, int32_t n_regions, int32_t region_elems, float* buf, hipStream_t s);
 hipError_t launch_bwd(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, void* ws, hipStream_t s);
 template <int D>
 hipError_t launch_dkdv(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, const float* ndbuf,

@@ -44,10 +44,13 @@ class HostTierStep:
         base = torch.zeros(n_bt, dtype=torch.int32, device=device)
         base[n_prior:n_prior + self.n_own] = torch.arange(self.n_own, dtype=torch.int32, device=device)
         self.own_bt = base.clone()
-        self.bt: List[torch.Tensor] = [base.clone() for _ in range(H)]
+        # The selection and the per-head device block tables are double-buffered by step parity: the
+        # gradient offload of step s still reads them while step s + 1 selects and gathers.
+        self.bt: List[List[torch.Tensor]] = [[base.clone() for _ in range(H)] for _ in range(2)]
         self.slots = [torch.arange(self.n_own + g * self.n_sel, self.n_own + (g + 1) * self.n_sel, dtype=torch.int32,
                                    device=device) for g in range(H)]
-        self.sel = torch.empty((H, self.n_sel), dtype=torch.int32, device=device)
+        self.sel = [torch.empty((H, self.n_sel), dtype=torch.int32, device=device) for _ in range(2)]
+        self.parity = 0
         self.own_lps = torch.arange(n_prior, n_prior + self.n_own, dtype=torch.int32, device=device)
         lib = load()
         self.ws_t = torch.empty(max(lib.page_topk_ws_bytes(host.handle, n_prior, C, H_q, 1), 1), dtype=torch.uint8,
@@ -62,9 +65,11 @@ class HostTierStep:
         # Gradient offloads run on a stream of their own, so the next step's gathers need not queue
         # behind them; the next backward of head g waits for head g's offload.
         self.off = torch.cuda.Stream(device=device) if self.host_grads else None
-        self.off_done = [torch.cuda.Event() for _ in range(H)]
+        # off_done[b][g]: the offload of head g by the last step that used buffer b (it reads
+        # sel[b][g] and bt[b][g] and clears head g's device gradient slots).
+        self.off_done = [[torch.cuda.Event() for _ in range(H)] for _ in range(2)]
         self.own_done = torch.cuda.Event()  # the last head's own-page offload
-        for ev in self.done + self.off_done + [self.own_done]:
+        for ev in self.done + self.off_done[0] + self.off_done[1] + [self.own_done]:
             ev.record(torch.cuda.current_stream(device))
 
     def append_own(self, k: torch.Tensor, v: torch.Tensor):
@@ -88,18 +93,31 @@ class HostTierStep:
         offload, so a slot is cleared before it is reused."""
         assert gather or not self.host_grads
         compute = torch.cuda.current_stream(q.device)
-        sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local, sel=self.sel,
-                               ws=self.ws_t)
         H = self.host.h_kv
+        if gather:
+            b = self.parity
+            self.parity ^= 1
+        else:
+            b = self.parity ^ 1  # the buffers the last gathering step filled
+        prev = b ^ 1
+        bts = self.bt[b]
+        if self.host_grads:
+            # sel[b] was last read by the offloads of the step before the previous one; the offload
+            # stream runs in order, so its last head's event covers them all.
+            compute.wait_event(self.off_done[b][H - 1])
+        sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local, sel=self.sel[b],
+                               ws=self.ws_t)
 
         def enqueue_gather(g, after=None):
             # Events are waited on at their latest record: `after` is this step's selection, done[g]
             # the previous step's backward of head g (recorded again only later in this step).
             with torch.cuda.stream(self.side):
                 self.side.wait_event(self.done[g])  # slots of g are free once its last backward ended
+                if self.host_grads:
+                    self.side.wait_event(self.off_done[b][g])  # bt[b][g] is no longer read by an offload
                 if after is not None:
                     self.side.wait_event(after)
-                paged_kv_gather(self.host, self.dev, self.host_bt, sel[g], g, self.slots[g], dev_bt_out=self.bt[g],
+                paged_kv_gather(self.host, self.dev, self.host_bt, sel[g], g, self.slots[g], dev_bt_out=bts[g],
                                 stream=self.side)
                 self.ready[g].record(self.side)
 
@@ -112,14 +130,15 @@ class HostTierStep:
         for g in range(H):
             if gather:
                 compute.wait_event(self.ready[g])
-            chunk_attn_fwd(self.dev, self.bt[g], self.n_prior, q, scale, sel=sel, kvh0=g, n_kvh=1, o=o, lse=lse,
+            chunk_attn_fwd(self.dev, bts[g], self.n_prior, q, scale, sel=sel, kvh0=g, n_kvh=1, o=o, lse=lse,
                            ws=self.ws_f)
             if self.host_grads:
-                compute.wait_event(self.off_done[g])  # the previous step's offload of head g's blocks
-                chunk_attn_bwd(self.dev, self.bt[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
-                               gpool=self.dev, gbt=self.bt[g], dq=dq, ws=self.ws_b)
+                # Head g's gradient slots are cleared by the previous step's offload of head g.
+                compute.wait_event(self.off_done[prev][g])
+                chunk_attn_bwd(self.dev, bts[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
+                               gpool=self.dev, gbt=bts[g], dq=dq, ws=self.ws_b)
             else:
-                chunk_attn_bwd(self.dev, self.bt[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
+                chunk_attn_bwd(self.dev, bts[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
                                gpool=self.host, gbt=self.host_bt, dq=dq, ws=self.ws_b)
             self.done[g].record(compute)
             if self.host_grads:
@@ -130,9 +149,9 @@ class HostTierStep:
                     paged_kv_grad_offload(self.host, self.host_bt, self.dev, self.own_bt, self.own_lps, kvh0=g,
                                           n_kvh=1, stream=self.off)
                     self.own_done.record(self.off)
-                    paged_kv_grad_offload(self.host, self.host_bt, self.dev, self.bt[g], sel[g], kvh0=g, n_kvh=1,
+                    paged_kv_grad_offload(self.host, self.host_bt, self.dev, bts[g], sel[g], kvh0=g, n_kvh=1,
                                           stream=self.off)
-                    self.off_done[g].record(self.off)
+                    self.off_done[b][g].record(self.off)
         return sel
 
     def free(self):

@@ -26,7 +26,8 @@ from typing import Callable, List, Optional, Sequence
 
 import torch
 
-from . import PKV_DK, PKV_DV, Pool, chunk_attn_bwd, chunk_attn_fwd, page_topk_select
+from . import (PKV_DK, PKV_DV, Pool, chunk_attn_bwd, chunk_attn_bwd_ws_bytes, chunk_attn_fwd, chunk_attn_fwd_ws_bytes,
+               page_topk_select, page_topk_ws_bytes)
 
 
 class PagedChunkAttention(torch.autograd.Function):
@@ -37,7 +38,7 @@ class PagedChunkAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, layer, n_prior, sel):
-        o, lse = chunk_attn_fwd(layer.pool, layer.bt, n_prior, q, layer.scale, sel=sel)
+        o, lse = chunk_attn_fwd(layer.pool, layer.bt, n_prior, q, layer.scale, sel=sel, ws=layer.ws_f)
         ctx.save_for_backward(q, o, lse)
         ctx.layer, ctx.n_prior, ctx.sel = layer, n_prior, sel
         return o
@@ -47,7 +48,7 @@ class PagedChunkAttention(torch.autograd.Function):
         q, o, lse = ctx.saved_tensors
         layer, n_prior, sel = ctx.layer, ctx.n_prior, ctx.sel
         dq = chunk_attn_bwd(layer.pool, layer.bt, n_prior, q, o, do.to(torch.bfloat16).contiguous(), lse,
-                            layer.scale, sel=sel)
+                            layer.scale, sel=sel, ws=layer.ws_b)
         C = q.shape[0]
         n_own = C // layer.page
         shape = (C, layer.h_kv, layer.d)
@@ -82,6 +83,21 @@ class ChunkRecurrentAttention(torch.nn.Module):
         self.n_pages = context // page
         self.pool = Pool(self.n_pages, page, h_kv, d, grads=True)
         self.bt = torch.arange(self.n_pages, dtype=torch.int32, device=device)
+        # Workspaces sized once for the largest call of any chunk position, so the steps allocate
+        # nothing in the library calls.
+        per_chunk = chunk // page
+        fb = bb = tb = 1
+        for n_prior in range(0, self.n_pages - per_chunk + 1, per_chunk):
+            n_sel = -1
+            if top_k is not None:
+                n_cand = max(n_prior - n_local, 0)
+                n_sel = min(top_k, n_cand) + (n_prior - n_cand)
+                tb = max(tb, page_topk_ws_bytes(self.pool, n_prior, chunk, h_q))
+            fb = max(fb, chunk_attn_fwd_ws_bytes(self.pool, n_prior, n_sel, h_kv, chunk, h_q))
+            bb = max(bb, chunk_attn_bwd_ws_bytes(self.pool, n_prior, n_sel, h_kv, chunk, h_q))
+        self.ws_f = torch.empty(fb, dtype=torch.uint8, device=device)
+        self.ws_b = torch.empty(bb, dtype=torch.uint8, device=device)
+        self.ws_t = torch.empty(tb, dtype=torch.uint8, device=device)
 
     def qkv(self, x: torch.Tensor):
         C = x.shape[0]
@@ -96,7 +112,7 @@ class ChunkRecurrentAttention(torch.nn.Module):
     def _select(self, q: torch.Tensor, n_prior: int):
         if self.top_k is None:
             return None
-        return page_topk_select(self.pool, self.bt, n_prior, q, self.top_k, self.n_local)
+        return page_topk_select(self.pool, self.bt, n_prior, q, self.top_k, self.n_local, ws=self.ws_t)
 
     def train_step(self, xs: Sequence[torch.Tensor],
                    loss_fn: Callable[[torch.Tensor, int], torch.Tensor]) -> tuple:
@@ -115,7 +131,7 @@ class ChunkRecurrentAttention(torch.nn.Module):
                 self.pool.append(self.bt, n_prior * self.page, k.contiguous(), v.contiguous())
                 sel = self._select(q, n_prior)
                 sels.append(sel)
-                o, _ = chunk_attn_fwd(self.pool, self.bt, n_prior, q, self.scale, sel=sel)
+                o, _ = chunk_attn_fwd(self.pool, self.bt, n_prior, q, self.scale, sel=sel, ws=self.ws_f)
                 total += loss_fn(self.out(o), i)
         self.last_selection = sels
         self.pool.zero_grad()

@@ -67,6 +67,17 @@ def test_argument_errors_without_device(lib):
     assert lib.pkv_mfma_probe(1, 0, None, None, None) == -1
     assert lib.pkv_mfma_probe(1, 1, None, None, None) == -1
     assert lib.paged_kv_data(None, 0) is None
+    # A scale that is not a positive finite number is rejected before anything else.
+    for bad in (0.0, -0.1, float("nan"), float("inf")):
+        assert lib.chunk_attn_fwd(None, None, 0, 0, None, 0, 1, 0, 1, None, 64, 4, bad, None, None, None, 0,
+                                  None) == -1
+        assert b"scale" in lib.pkv_last_error()
+        assert lib.chunk_attn_bwd(None, None, 0, None, None, 0, 0, None, 0, 1, 0, 1, None, None, None, None, 64, 4,
+                                  bad, None, None, 0, None) == -1
+        assert b"scale" in lib.pkv_last_error()
+    assert lib.paged_kv_page_alloc(None, 1, None) == -1
+    assert lib.paged_kv_page_release(None, 1, None) == -1
+    assert lib.paged_kv_pages_available(None) == -1
     assert lib.chunk_attn_fwd_ws_bytes(None, 0, -1, 1, 1, 64, 4) == 0
     assert lib.page_topk_ws_bytes(None, 0, 64, 4, 1) == 0
 

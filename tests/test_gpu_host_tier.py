@@ -131,6 +131,64 @@ def test_host_grads_small_parity_and_accumulation(pkv):
     hpool.free()
 
 
+def test_host_grads_back_to_back_steps_with_different_selections(pkv):
+    """Gradient pages in host memory over two steps enqueued back to back whose queries, and so page
+    selections, differ. The second step selects and gathers while the first step's gradient offload
+    may still be running, so the offload must keep reading its own step's selection and device block
+    tables: the host pages must hold the sum of the oracle's two results, pages selected by neither
+    step none, and every device gradient slot must end cleared."""
+    from paged_kv_cache_fwd_amd.host_tier import HostTierStep
+    wl = synth.Workload("host-small", 14, 2, 128, 128, 128 * 24, 384, (7,), offset_std=0.5, seed=23)
+    wl2 = wl.with_seed(24)  # the second step's queries and output gradients
+    c, top_k, n_local = 7, 6, 2
+    n_prior, C, P = wl.n_prior(c), wl.chunk, wl.page
+    say("host gradient pages: two back-to-back steps with different selections")
+    bt_np = synth.page_permutation(wl)
+    hpool, hbt = fill_pool(pkv, wl, wl.n_pages, bt_np, host_tier=True, host_grads=True)
+    step = HostTierStep(hpool, hbt, n_prior, C, wl.h_q, top_k, n_local, torch.device("cuda:0"))
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    step.append_own(t16(k[n_prior * P:]), t16(v[n_prior * P:]))
+    hpool.zero_grad()
+    qs = [synth.q_chunk(wl, c), synth.q_chunk(wl2, c)]
+    dos = [synth.do_chunk(wl, c), synth.do_chunk(wl2, c)]
+    outs = []
+    for qn, don in zip(qs, dos):
+        q, do = t16(qn), t16(don)
+        o, dq = torch.empty_like(q), torch.empty_like(q)
+        lse = torch.empty((wl.h_q, C), dtype=torch.float32, device=q.device)
+        sel = step.run(q, do, wl.scale, o, lse, dq)
+        outs.append((sel, q, do, o, dq, lse))  # keep every buffer alive until the end
+    torch.cuda.synchronize()
+    sels = [o[0].cpu().numpy() for o in outs]
+    dk = hpool.export(pkv.PKV_DK, hbt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    dv = hpool.export(pkv.PKV_DV, hbt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    slots = step.dev.export(pkv.PKV_DK, torch.arange(step.dev.n_pages, dtype=torch.int32, device="cuda"), 0,
+                            step.dev.n_pages).cpu().numpy()
+    slots_v = step.dev.export(pkv.PKV_DV, torch.arange(step.dev.n_pages, dtype=torch.int32, device="cuda"), 0,
+                              step.dev.n_pages).cpu().numpy()
+    hpool.check()
+    step.dev.check()
+    want_dk = np.zeros_like(dk)
+    want_dv = np.zeros_like(dv)
+    wants = []
+    for qn, don, got in zip(qs, dos, sels):
+        want, _, _ = oracle.topk_pages(qn, k[: n_prior * P], P, wl.h_kv, n_prior, top_k, n_local)
+        assert np.array_equal(got, want)
+        wants.append(want)
+        ref = oracle.chunk_backward(qn, k, v, don, wl.q0(c), wl.scale, sel=want, page=P)
+        for g in range(wl.h_kv):
+            np.add.at(want_dk[:, g], ref["keys"][g], ref["dk"][g])
+            np.add.at(want_dv[:, g], ref["keys"][g], ref["dv"][g])
+    assert not np.array_equal(wants[0], wants[1]), "the two steps must select different pages"
+    for g in range(wl.h_kv):
+        compare(f"host dK (two steps) head {g}", dk[:, g], want_dk[:, g], ATOL_GRAD)
+        compare(f"host dV (two steps) head {g}", dv[:, g], want_dv[:, g], ATOL_GRAD)
+    assert not np.any(dk[want_dk == 0]) and not np.any(dv[want_dv == 0])
+    assert not np.any(slots) and not np.any(slots_v)
+    step.free()
+    hpool.free()
+
+
 def test_dense_layer_prefetch_matches_resident(pkv):
     """Two layers whose KV and gradient pages live in pinned host memory, run dense with the next
     layer's pages copied in (and the last one's gradients copied home) beside each step. O, LSE and
@@ -241,6 +299,23 @@ def test_host_tier_1m_matches_resident(pkv):
                                 page=wl.page, rows=rows, dtype=np.float32)
     compare("O rows", host(res["o"])[rows], ref["o"], ATOL_O)
     compare("dQ rows", host(res["dq"])[rows], ref["dq"], ATOL_GRAD)
+    # LSE of every row and dK/dV of sampled selected pages and the last own page over all rows, for
+    # two KV heads, against the oracle (its float32 statistics of every row of the head).
+    do = synth.do_chunk(wl, c)
+    G, P, q0 = wl.group, wl.page, wl.q0(c)
+    for g in (0, 3):
+        say(f"host tier 1M: oracle statistics of all rows of KV head {g} over its {len(sel_pages[g])} pages")
+        qg, dog = q[:, g * G:(g + 1) * G], do[:, g * G:(g + 1) * G]
+        o_g, lse_g = oracle.chunk_forward(qg, k_full[:, g:g + 1], v_full[:, g:g + 1], q0, wl.scale, sel=[sel_pages[g]],
+                                          page=P, dtype=np.float32)
+        compare(f"LSE head {g} all rows", res["lse"].cpu().numpy()[g * G:(g + 1) * G], lse_g, ATOL_LSE, rel=1e-5)
+        dd_g = np.einsum("thd,thd->ht", synth.bf16_widen(dog).astype(np.float32), o_g)
+        picked = [sel_pages[g][i] for i in (0, 40, 90, len(sel_pages[g]) - 1)] + [wl.n_pages - 1]
+        toks = np.concatenate([np.arange(p * P, (p + 1) * P) for p in picked])
+        r = oracle.key_gradients(qg, k_full[:, g:g + 1], v_full[:, g:g + 1], dog, q0, wl.scale, {0: toks}, lse_g, dd_g,
+                                 dtype=np.float32)[0]
+        compare(f"dK pages {picked} head {g}", res["dk"][toks, g], r[0], ATOL_GRAD)
+        compare(f"dV pages {picked} head {g}", res["dv"][toks, g], r[1], ATOL_GRAD)
 
 
 def test_paged_kv_copy_rejects_bad_arguments(pkv):

@@ -388,6 +388,23 @@ def test_mfma_probe_runs_and_counts(pkv):
     assert 0 < tflops < 2600.0 * n_wg / 256
 
 
+def test_atomic_probe_adds_exactly(pkv):
+    """The fp32 atomic-add diagnostic: every float of region r ends at the number of workgroups that
+    add into it (counts below 2^24 are exact in fp32), with and without contention, and the byte
+    count it reports."""
+    region = 3000  # not a multiple of the 256 threads: the strided tail is covered too
+    for n_wg, n_regions in ((64, 64), (70, 8)):
+        buf = torch.zeros(n_regions * region, dtype=torch.float32, device="cuda")
+        nbytes = pkv.atomic_probe(n_wg, n_regions, region, buf)
+        torch.cuda.synchronize()
+        assert nbytes == n_wg * region * 4
+        want = torch.tensor([sum(1 for w in range(n_wg) if w % n_regions == r) for r in range(n_regions)],
+                            dtype=torch.float32).repeat_interleave(region)
+        assert torch.equal(buf.cpu(), want)
+    with pytest.raises(pkv.PkvError):
+        pkv.atomic_probe(4, 8, region, torch.zeros(8 * region, dtype=torch.float32, device="cuda"))
+
+
 def test_bad_table_and_selection_entries_are_skipped_and_reported(pkv):
     """Device-side validation: a block-table entry outside the pool and a selection id outside
     [0, n_prior) are skipped by every kernel (the page acts as absent) and reported once through

@@ -72,6 +72,42 @@ def test_dense256k_sampled_rows_and_invariants(pkv, big):
     assert np.all(np.abs(dk).reshape(wl.n_pages, -1).max(axis=1) > 0)
 
 
+def _row_stats(q, k, v, do, q0, scale, page, g, G):
+    """The oracle's float32 forward over every chunk row of KV head g (its G query heads against all
+    keys the rows see): LSE [G][C] and D = dO.O [G][C]."""
+    qg, dog = q[:, g * G:(g + 1) * G], do[:, g * G:(g + 1) * G]
+    o, lse = oracle.chunk_forward(qg, k[:, g:g + 1], v[:, g:g + 1], q0, scale, page=page, dtype=np.float32)
+    dd = np.einsum("thd,thd->ht", synth.bf16_widen(dog).astype(np.float32), o)
+    return qg, dog, lse, dd
+
+
+def test_dense256k_sampled_pages_dkdv_over_all_rows(pkv, big):
+    """The dense 256K backward's accumulated dK/dV element by element for sampled pages (four prior
+    pages spread over the context and the first and last own pages) of two KV heads, each against
+    the oracle's sum over all 28,672 rows of the head's query heads (the oracle's own float32 forward
+    statistics of every row, then the key gradients from them)."""
+    wl, c, pool, bt, k, v, q, do = big
+    n_prior, P, G, q0 = wl.n_prior(c), wl.page, wl.group, wl.q0(c)
+    pool.zero_grad()
+    qt, dot = t16(q), t16(do)
+    o, lse = pkv.chunk_attn_fwd(pool, bt, n_prior, qt, wl.scale)
+    pkv.chunk_attn_bwd(pool, bt, n_prior, qt, o, dot, lse, wl.scale)
+    dk = pool.export(pkv.PKV_DK, bt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    dv = pool.export(pkv.PKV_DV, bt, 0, wl.n_pages).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    pool.check()
+    pages = [0, 517, 1333, n_prior - 1, n_prior, wl.n_pages - 1]
+    toks = np.concatenate([np.arange(p * P, (p + 1) * P) for p in pages])
+    for g in (0, 3):
+        say(f"dense256k: oracle forward statistics of all {wl.chunk * G} rows of KV head {g} (float32)")
+        qg, dog, lse_g, dd_g = _row_stats(q, k, v, do, q0, wl.scale, P, g, G)
+        compare(f"LSE head {g} all rows", lse.cpu().numpy()[g * G:(g + 1) * G], lse_g, ATOL_LSE, rel=1e-5)
+        ref = oracle.key_gradients(qg, k[:, g:g + 1], v[:, g:g + 1], dog, q0, wl.scale, {0: toks}, lse_g, dd_g,
+                                   dtype=np.float32)[0]
+        compare(f"dK pages {pages} head {g}", dk[toks, g], ref[0], ATOL_GRAD)
+        compare(f"dV pages {pages} head {g}", dv[toks, g], ref[1], ATOL_GRAD)
+
+
 def test_topk256k_selection_and_full_sparse_step(pkv, big):
     wl, c, pool, bt, k, v, q, do = big
     wk = synth.WORKLOADS["topk256k"]
@@ -192,4 +228,26 @@ def test_qwen32k_all_chunks_sampled_rows_last_page_and_invariants(pkv):
         skew = np.linalg.norm(dk[:, g].sum(axis=0)) / np.abs(dk[:, g]).sum(axis=0).mean()
         say(f"  head {g}: |sum dV - sum dO|/|sum dO| = {err:.2e}; |sum dK| / mean sum|dK| = {skew:.2e}")
         assert err < 1e-2 and skew < 1e-2
+    # A mid-sequence page (logical page 100, in chunk 3) after all 8 chunks: its gradient pages hold
+    # the sum of chunks 3..7's contributions, each from all of that chunk's rows.
+    mid, g = 100, 2
+    toks = np.arange(mid * P, (mid + 1) * P)
+    ref_dk = np.zeros((P, wl.d))
+    ref_dv = np.zeros((P, wl.d))
+    for c in wl.chunks:
+        q0 = wl.q0(c)
+        if q0 + C <= mid * P:
+            continue
+        say(f"qwen32k: page {mid} head {g}: oracle statistics of chunk {c}'s {C * G} rows")
+        q, do = synth.q_chunk(wl, c), synth.do_chunk(wl, c)
+        qg, dog = q[:, g * G:(g + 1) * G], do[:, g * G:(g + 1) * G]
+        L = q0 + C
+        o_g, lse_g = oracle.chunk_forward(qg, k[:L, g:g + 1], v[:L, g:g + 1], q0, wl.scale, page=P, dtype=np.float32)
+        dd_g = np.einsum("thd,thd->ht", synth.bf16_widen(dog).astype(np.float32), o_g)
+        r = oracle.key_gradients(qg, k[:L, g:g + 1], v[:L, g:g + 1], dog, q0, wl.scale, {0: toks}, lse_g, dd_g,
+                                 dtype=np.float32)[0]
+        ref_dk += r[0]
+        ref_dv += r[1]
+    compare(f"dK page {mid} head {g} over all chunks", dk[toks, g], ref_dk, ATOL_GRAD)
+    compare(f"dV page {mid} head {g} over all chunks", dv[toks, g], ref_dv, ATOL_GRAD)
     pool.free()

@@ -418,3 +418,30 @@ def test_planted_per_query_page_routing_mistakes_fail_the_pin(monkeypatch, broke
     assert _sparse_pin_errors(_SEL_PER_QPAGE) < 1e-12
     monkeypatch.setattr(oracle.attention, "_key_sets", broken)
     assert _sparse_pin_errors(_SEL_PER_QPAGE) > 1e-3
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_key_gradients_from_row_statistics_match_torch_autograd(sparse):
+    """dK/dV of a few keys, from the forward's LSE and D = dO.O, equal the gradients SDPA's autograd
+    gives those keys (dense, and a shared page list whose pages plus the own block every row sees)."""
+    rng = np.random.default_rng(17)
+    H_q, H_kv, d, P, C = 6, 2, 8, 4, 16
+    n_prior = 10
+    q0 = n_prior * P
+    L = q0 + C
+    q, k, v, do = _rand((C, H_q, d), rng), _rand((L, H_kv, d), rng), _rand((L, H_kv, d), rng), _rand((C, H_q, d), rng)
+    scale = 0.41
+    sel = [[1, 4, 7], [0, 8, 9]] if sparse else None
+    o, lse = oracle.chunk_forward(q, k, v, q0, scale, sel=sel, page=P)
+    dd = np.einsum("thd,thd->ht", do, o)
+    masks = [_hand_mask(C, L, q0, P, None if sel is None else sel[g]) for g in range(H_kv)]
+    _, _, tdk, tdv = _torch_reference(q, k, v, do, q0, scale, masks, H_q, H_kv)
+    # Keys from a prior page, the first own-block key (seen by every row) and the last one (seen by
+    # the last row only), written out by hand per head.
+    keys = {0: np.array([4 * P, 4 * P + 3, q0, q0 + C - 1]) if sparse else np.array([0, 17, q0, q0 + C - 1]),
+            1: np.array([8 * P + 1, 9 * P + 2, q0 + 5]) if sparse else np.array([3, 39, q0 + 5])}
+    got = oracle.key_gradients(q, k, v, do, q0, scale, keys, lse, dd)
+    for g, kidx in keys.items():
+        assert np.max(np.abs(got[g][0] - tdk[kidx, g])) < 1e-12
+        assert np.max(np.abs(got[g][1] - tdv[kidx, g])) < 1e-12
+        assert np.max(np.abs(got[g][0])) > 1e-3  # not vacuous

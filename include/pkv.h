@@ -224,6 +224,22 @@ int page_topk_select(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, 
                      void* stream);
 
 /*
+ * page_topk_select for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same selection, the same arguments
+ * except that there is no workspace argument, and bitwise the same output. Its scratch is a static
+ * 16 MiB array compiled into the library, one copy per GPU, held until the process ends; the call
+ * itself allocates nothing. A call whose page_topk_ws_bytes(...) exceeds 16 MiB (2^24 bytes) fails
+ * with PKV_E_NOMEM and enqueues nothing. Every call on one GPU uses that GPU's single scratch array,
+ * so calls that may overlap on one GPU (on different streams, or from several host threads) race
+ * and must be ordered by the caller; calls on one stream are ordered by the stream. Other errors
+ * are those of page_topk_select, plus PKV_E_HIP if the scratch's device address cannot be looked up
+ * (done once per GPU, on the first call there).
+ */
+int page_topk_select_noalloc(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
+                             const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
+                             int32_t n_lists, int32_t* sel_dev, int32_t* n_sel_out, void* stream);
+
+/*
  * Forward attention of one query chunk over the paged cache (pt 2.A, 2.B; es 2.B custom kernels).
  * Query head h (KV head g = h / G) at chunk row t (position q0 + t) attends to
  *   dense (sel_dev == NULL): every key at position <= q0 + t, i.e. logical pages [0, n_prior)

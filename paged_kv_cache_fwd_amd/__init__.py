@@ -29,7 +29,7 @@ EXPORTED = (
     "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "paged_kv_copy", "pkv_mfma_probe",
     "pkv_timing_enable", "pkv_timing_collect",
     "pkv_timing_get", "paged_kv_page_alloc", "paged_kv_page_release", "paged_kv_pages_available",
-    "pkv_atomic_probe",
+    "page_topk_select_noalloc", "pkv_atomic_probe",
 )
 
 
@@ -88,6 +88,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "paged_kv_page_alloc": (_I, [_P, _I, ctypes.POINTER(_I)]),
         "paged_kv_page_release": (_I, [_P, _I, ctypes.POINTER(_I)]),
         "paged_kv_pages_available": (_I, [_P]),
+        "page_topk_select_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), _P]),
         "pkv_atomic_probe": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
     }
     for name, (res, args) in sig.items():
@@ -259,6 +260,24 @@ def page_topk_select(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor
 
 def page_topk_ws_bytes(pool: Pool, n_prior: int, C: int, H_q: int, n_lists: int = 1) -> int:
     return load().page_topk_ws_bytes(pool.handle, n_prior, C, H_q, n_lists)
+
+
+def page_topk_select_noalloc(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, top_k: int, n_local: int,
+                             sel: torch.Tensor, stream=None, per_query_page: bool = False) -> torch.Tensor:
+    """page_topk_select with the library's static scratch instead of a workspace, for callers that
+    cannot allocate: nothing is allocated here either, so the output buffer sel is required
+    ([H_kv][n_sel] int32, or [H_kv][C / page][n_sel] with per_query_page)."""
+    _need(bt, torch.int32, "bt")
+    C, H_q = _need_q(pool, q)
+    n_cand = max(n_prior - n_local, 0)
+    n_sel = min(top_k, n_cand) + (n_prior - n_cand)
+    n_lists = C // pool.page if per_query_page else 1
+    shape = (pool.h_kv, n_lists, n_sel) if per_query_page else (pool.h_kv, n_sel)
+    _need(sel, torch.int32, "sel", shape)
+    out_n = _I(0)
+    _check(load().page_topk_select_noalloc(pool.handle, _ptr(bt), bt.numel(), n_prior, _ptr(q), C, H_q, top_k, n_local,
+                                           n_lists, _ptr(sel), ctypes.byref(out_n), _stream(stream)))
+    return sel
 
 
 def chunk_attn_fwd_ws_bytes(pool: Pool, n_prior: int, n_sel: int, n_kvh: int, C: int, H_q: int,

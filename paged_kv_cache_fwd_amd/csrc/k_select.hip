@@ -12,6 +12,8 @@
 // With one selection per query page (pt 2.C: the most relevant key pages for each page of
 // queries) the chunk's 64-token blocks are cut into n_lists groups of consecutive blocks; group i
 // is summarised, scored and selected on its own exactly as above (b running over its blocks).
+#include <mutex>
+
 #include "pkv_device.h"
 
 #pragma clang fp contract(off)
@@ -208,6 +210,33 @@ __global__ __launch_bounds__(kSelThreads) void k_topk(const float* __restrict__ 
     }
   }
   for (int32_t u = tid; u < n_prior - n_cand; u += kSelThreads) out[kk + u] = n_cand + u;
+}
+
+// Scratch of page_topk_select_noalloc, for callers that cannot allocate: it lives with the code
+// object, so each GPU the library runs on holds its own copy until the process ends. Host code
+// never passes the array's name to a kernel (on the host it is only a stand-in for the symbol):
+// topk_scratch_ptr looks up the device address of the current GPU's copy once and keeps it.
+static __device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+hipError_t topk_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* ptrs[kMaxScratchDevices] = {};
+  std::lock_guard<std::mutex> lk(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d, int32_t n_lists) {

@@ -683,8 +683,8 @@ size_t page_topk_ws_bytes(const pkv_pool* pool, int32_t n_prior, int32_t C, int3
   return pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d, n_lists);
 }
 
-// Checks of page_topk_select; on success *ws_need is the workspace the call needs and *n_sel the
-// selection length.
+// Shared checks of page_topk_select and page_topk_select_noalloc; on success *ws_need is the
+// scratch the call needs and *n_sel the selection length.
 static int check_topk(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior, const uint16_t* q_dev,
                       int32_t C, int32_t H_q, int32_t top_k, int32_t n_local, int32_t n_lists, const int32_t* sel_dev,
                       const int32_t* n_sel_out, size_t* ws_need, int32_t* n_sel, bool* needs_ws) {
@@ -704,6 +704,29 @@ static int check_topk(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt,
   if (*n_sel > 0 && !sel_dev) return fail(PKV_E_INVALID, "sel is NULL");
   *ws_need = pkv::topk_ws_bytes(n_prior, C, H_q, pool->h_kv, pool->d, n_lists);
   *needs_ws = kk > 0 && kk < n_cand;
+  return PKV_OK;
+}
+
+int page_topk_select_noalloc(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, int32_t n_prior,
+                             const uint16_t* q_dev, int32_t C, int32_t H_q, int32_t top_k, int32_t n_local,
+                             int32_t n_lists, int32_t* sel_dev, int32_t* n_sel_out, void* stream) {
+  size_t ws_need = 0;
+  int32_t n_sel = 0;
+  bool needs_ws = false;
+  int rc = check_topk(pool, bt_dev, n_bt, n_prior, q_dev, C, H_q, top_k, n_local, n_lists, sel_dev, n_sel_out,
+                      &ws_need, &n_sel, &needs_ws);
+  if (rc != PKV_OK) return rc;
+  if (ws_need > pkv::kTopkScratchBytes)
+    return fail(PKV_E_NOMEM, "this selection needs %zu bytes of scratch; the static scratch holds %zu", ws_need,
+                pkv::kTopkScratchBytes);
+  void* scratch = nullptr;
+  hipError_t e = pkv::topk_scratch_ptr(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (selection scratch)");
+  *n_sel_out = n_sel;
+  e = pkv::launch_topk(*pool, bt_dev, n_bt, n_prior, q_dev, C, H_q, top_k, n_local, n_lists, sel_dev, scratch,
+                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  ok();
   return PKV_OK;
 }
 

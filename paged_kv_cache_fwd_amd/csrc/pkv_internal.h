@@ -105,6 +105,10 @@ hipError_t launch_grad_offload(const pkv_pool& host, const int32_t* host_bt, int
                                const int32_t* dev_bt, int32_t n_dev_bt, const int32_t* lp, int32_t n, int32_t kvh0,
                                int32_t n_kvh, hipStream_t s);
 size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d, int32_t n_lists);
+// Static scratch of page_topk_select_noalloc: a file-scope device array in k_select.hip, one copy per
+// GPU. topk_scratch_ptr returns the current device's copy (looked up once per device).
+constexpr size_t kTopkScratchBytes = (size_t)16 << 20;
+hipError_t topk_scratch_ptr(void** out);
 hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, int32_t n_prior, const uint16_t* q,
                        int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t n_lists, int32_t* sel,
                        void* ws, hipStream_t s);

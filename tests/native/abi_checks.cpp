@@ -232,6 +232,20 @@ static void check_compute_validation() {
   FAILS(PKV_E_INVALID, page_topk_select(p, bt, n_bt, n_prior, q, C, Hq, 3, 1, 3, sel, &n_sel, ws, sizeof(ws), nullptr));
   FAILS(PKV_E_INVALID, page_topk_select(p, bt, n_bt, n_prior, q, C, Hq, 3, 1, 1, nullptr, &n_sel, ws, sizeof(ws), nullptr));
   FAILS(PKV_E_NOMEM, page_topk_select(p, bt, n_bt, n_prior, q, C, Hq, 3, 1, 1, sel, &n_sel, ws, tws - 1, nullptr));
+  // The static-scratch variant: the same checks, and requests beyond its 16 MiB refused up front.
+  n_sel = -1;
+  ENQUEUES(1, page_topk_select_noalloc(p, bt, n_bt, n_prior, q, C, Hq, 3, 1, 1, sel, &n_sel, nullptr));
+  CHECK(n_sel == 4);
+  FAILS(PKV_E_INVALID, page_topk_select_noalloc(p, bt, n_bt, n_prior, q, 96, Hq, 3, 1, 1, sel, &n_sel, nullptr));
+  FAILS(PKV_E_RANGE, page_topk_select_noalloc(p, bt, 7, n_prior, q, C, Hq, 3, 1, 1, sel, &n_sel, nullptr));
+  FAILS(PKV_E_INVALID, page_topk_select_noalloc(p, bt, n_bt, n_prior, q, C, Hq, 3, 1, 1, nullptr, &n_sel, nullptr));
+  FAILS(PKV_E_INVALID, page_topk_select_noalloc(nullptr, bt, n_bt, n_prior, q, C, Hq, 3, 1, 1, sel, &n_sel, nullptr));
+  {
+    // 2^17 chunk tokens of 64 query heads: the query partial sums alone exceed the scratch.
+    alignas(256) static int32_t big_bt[1 << 12];
+    FAILS(PKV_E_NOMEM, page_topk_select_noalloc(p, big_bt, 1 << 12, 1 << 12, q, 1 << 17, 64, 3, 1, 1, sel, &n_sel, nullptr));
+    CHECK(std::strstr(pkv_last_error(), "scratch") != nullptr);
+  }
 
   // Append, zeroing, export, check.
   ENQUEUES(1, paged_kv_append(p, bt, n_bt, 0, 128, q, o, nullptr));

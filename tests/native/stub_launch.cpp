@@ -35,6 +35,12 @@ hipError_t launch_grad_offload(const pkv_pool&, const int32_t*, int32_t, const p
 size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t, int32_t d, int32_t n_lists) {
   return 256 + (size_t)n_lists * ((size_t)n_cand + (size_t)C / 64 * h_q) * d * 4;
 }
+// The static selection scratch: any host buffer stands in for it here.
+hipError_t topk_scratch_ptr(void** out) {
+  static unsigned char buf[256];
+  *out = buf;
+  return hipSuccess;
+}
 hipError_t launch_topk(const pkv_pool&, const int32_t*, int32_t, int32_t, const uint16_t*, int32_t, int32_t, int32_t,
                        int32_t, int32_t, int32_t*, void*, hipStream_t) {
   ++g_stub_launches;

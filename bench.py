@@ -183,29 +183,37 @@ def bench_host1m(args, pkv, synth, dev, t16):
     o, dq = torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty((H_q, C), dtype=torch.float32, device=dev)
 
-    def timed(gather):
+    def timed(gather, lookahead=False):
+        # With lookahead each step also enqueues the next step's selection and first gather (the
+        # same queries here) beside its last heads, as a chunk loop that knows the next chunk's
+        # queries would.
+        nxt = q if lookahead else None
         for _ in range(args.warmup):
             step.append_own(k_own, v_own)
-            step.run(q, do, wl.scale, o, lse, dq, gather=gather)
+            step.run(q, do, wl.scale, o, lse, dq, gather=gather, next_q=nxt)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             step.append_own(k_own, v_own)
-            step.run(q, do, wl.scale, o, lse, dq, gather=gather)
+            step.run(q, do, wl.scale, o, lse, dq, gather=gather, next_q=nxt)
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / args.steps * 1e3
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        step.cancel_lookahead()
+        return ms
 
     log("[bench] host1m: steps with H2D gathers on a side stream")
     ms_host = timed(True)
+    log("[bench] host1m: the same steps, each looking ahead to the next one's selection and first gather")
+    ms_host_ahead = timed(True, lookahead=True)
     log("[bench] host1m: the same steps with the selected pages already on the device")
     ms_res = timed(False)
     # H2D gathers alone.
-    sel = step.sel
+    sel, sel_bt = step.last_sel, step.last_bt
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         for g in range(H_kv):
-            pkv.paged_kv_gather(hpool, step.dev, hbt, sel[g], g, step.slots[g], dev_bt_out=step.bt[g])
+            pkv.paged_kv_gather(hpool, step.dev, hbt, sel[g], g, step.slots[g], dev_bt_out=sel_bt[g])
     torch.cuda.synchronize()
     ms_gather = (time.perf_counter() - t0) / args.steps * 1e3
     # Pinned host -> device copy of the same byte count, for the link's practical peak.
@@ -240,24 +248,43 @@ def bench_host1m(args, pkv, synth, dev, t16):
         hpool.append(hbt, p0 * P, t16(k), t16(v))
     step = HostTierStep(hpool, hbt, n_prior, C, H_q, wl.top_k, wl.n_local, dev)
     ms_host_grads = timed(True)
+    ms_host_grads_ahead = timed(True, lookahead=True)
+    hpool.check()
+    step.dev.check()
+    step.free()
+    # The earlier offload for comparison: one kernel adds the device slots into the host pages over
+    # the host link (zero-copy loads and stores).
+    step = HostTierStep(hpool, hbt, n_prior, C, H_q, wl.top_k, wl.n_local, dev, grad_offload="kernel")
+    ms_host_grads_kernel = timed(True)
     hpool.check()
     step.dev.check()
     step.free()
     hpool.free()
-    offload_bytes = (H_kv * n_sel_1m + H_kv * (C // P)) * 2 * P * d * 4  # fp32 dK+dV blocks, read and written
-    log(f"[bench] host1m: {ms_host_grads:.3f} ms/step with gradient pages in host memory")
-    log(f"[bench] host1m: {ms_host:.3f} ms/step with gathers, {ms_res:.3f} ms resident, gathers alone {ms_gather:.3f} ms")
+    offload_bytes = (H_kv * n_sel_1m + H_kv * (C // P)) * 2 * P * d * 4  # fp32 dK+dV blocks
+    log(f"[bench] host1m: {ms_host_grads:.3f} ms/step with gradient pages in host memory (staged), "
+        f"{ms_host_grads_kernel:.3f} ms with the zero-copy offload kernel")
+    log(f"[bench] host1m: {ms_host:.3f} ms/step with gathers ({ms_host_ahead:.3f} with lookahead), {ms_res:.3f} ms "
+        f"resident, gathers alone {ms_gather:.3f} ms; host gradient pages with lookahead {ms_host_grads_ahead:.3f} ms")
     return {"workload": "host1m: 1M tokens, 8160 prior pages in pinned host memory, top-128 + 8 local per KV head, "
                         "per-head H2D gathers overlapped with the previous head's fwd+bwd",
             "value": round(flop / (ms_host * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_host, 4),
             "flop_per_step": flop, "ms_per_step_pages_resident": round(ms_res, 4),
             "overlap_overhead": round(ms_host / ms_res - 1.0, 4),
+            "ms_per_step_lookahead": round(ms_host_ahead, 4),
+            "overlap_overhead_lookahead": round(ms_host_ahead / ms_res - 1.0, 4),
             "h2d_bytes_per_step": h2d_bytes, "h2d_gather_ms": round(ms_gather, 4),
             "h2d_GBps": round(h2d_bytes / (ms_gather * 1e-3) / 1e9, 2),
             "h2d_pinned_memcpy_GBps": round(h2d_bytes / (ms_memcpy * 1e-3) / 1e9, 2),
             "ms_per_step_host_grads": round(ms_host_grads, 4),
             "host_grads_overhead": round(ms_host_grads / ms_host - 1.0, 4),
             "host_grads_overhead_vs_resident": round(ms_host_grads / ms_res - 1.0, 4),
+            "ms_per_step_host_grads_lookahead": round(ms_host_grads_ahead, 4),
+            "host_grads_overhead_lookahead": round(ms_host_grads_ahead / ms_host_ahead - 1.0, 4),
+            "host_grads_overhead_lookahead_vs_resident": round(ms_host_grads_ahead / ms_res - 1.0, 4),
+            "host_grads_offload": "device slots copied to pinned staging by the copy engines (one rectangular "
+                                  "copy per head), added into the host pages by host threads",
+            "ms_per_step_host_grads_zero_copy_kernel": round(ms_host_grads_kernel, 4),
+            "host_grads_overhead_zero_copy_kernel": round(ms_host_grads_kernel / ms_host - 1.0, 4),
             "grad_offload_bytes_per_step": offload_bytes}
 
 

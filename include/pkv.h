@@ -114,6 +114,44 @@ int paged_kv_grad_offload(pkv_pool* host, const int32_t* host_bt_dev, int32_t n_
                           int32_t kvh0, int32_t n_kvh, void* stream);
 
 /*
+ * Gradient offload for a host tier through the copy engines, in two stream-ordered steps (pt 2.D /
+ * es 2.B "asynchronous CPU offloading": the gradients of the KV cache move to CPU memory on
+ * dedicated streams; it 2.C). Unlike paged_kv_grad_offload no kernel touches host memory: the host
+ * pages receive the sums from host threads.
+ *
+ * paged_kv_grad_stage: for i < n, copies head kvh's gradient block (dK then dV, 2 * page_size *
+ * head_dim floats) of device page dev_page0 + i into staging block i with one rectangular
+ * device-to-host copy (a copy engine, no compute units), copies the n logical page ids lp_dev[0..n)
+ * beside them, and then clears those device blocks with a fill kernel (ready for the next
+ * backward). staging_host: pinned host memory of at least paged_kv_grad_staging_bytes(dev, n)
+ * bytes, laid out as n int32 page ids (padded to 256 bytes) followed by the n blocks. dev: a pool
+ * with device gradient pages; [dev_page0, dev_page0 + n) inside it.
+ *
+ * paged_kv_grad_accumulate: enqueues on stream a host function that, once the work before it on
+ * the stream is done, adds staged block i into host grad[host_bt_host[lp[i]]][kvh] of host (a pool
+ * with PKV_HOST_GRADS), lp being the ids staged beside the blocks. host_bt_host is a host copy of
+ * the host pool's block table (n_host_bt entries); it and the staging must stay valid until the
+ * function has run. The adds run on the library's host threads (PKV_HOST_THREADS in the
+ * environment, default 8, sets their number). A staged id outside [0, n_host_bt) or a table entry
+ * outside the pool is skipped and reported by paged_kv_check(host). Each host pool keeps 1024 job
+ * slots, so enqueueing allocates nothing: a call made while 1024 earlier calls on the pool are still
+ * pending waits on the host for the oldest to run, and fails with PKV_E_STATE after 60 s. The host
+ * function makes this call unfit for HIP graph capture.
+ *
+ * Ordering is the caller's: stage after the backward that wrote the blocks, accumulate after the
+ * stage (same stream, or an event), reuse a staging buffer only after its accumulation has run,
+ * and let calls that add into the same host pages run one after another (the library runs one
+ * accumulation at a time). Apart from that back-pressure nothing here waits on the host. Errors:
+ * PKV_E_INVALID (NULL pointers, ranges, kvh), PKV_E_STATE (pool kinds, pending slots), PKV_E_NOMEM
+ * (staging too small), PKV_E_HIP (a copy, kernel or host function could not be enqueued).
+ */
+size_t paged_kv_grad_staging_bytes(const pkv_pool* pool, int32_t n);
+int paged_kv_grad_stage(pkv_pool* dev, int32_t dev_page0, int32_t n, int32_t kvh, const int32_t* lp_dev,
+                        void* staging_host, size_t staging_bytes, void* stream);
+int paged_kv_grad_accumulate(pkv_pool* host, const int32_t* host_bt_host, int32_t n_host_bt, int32_t n, int32_t kvh,
+                             const void* staging_host, void* stream);
+
+/*
  * Bulk page copy between two pools of the same page size, heads and dim, for dense attention over a
  * host tier (pt 2.D: with dense or local attention the next block is fetched while the current one
  * is computed; es 2.B: transfers overlap the next layer's compute). Copies physical pages

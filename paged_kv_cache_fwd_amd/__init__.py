@@ -29,7 +29,8 @@ EXPORTED = (
     "chunk_attn_bwd", "paged_kv_gather", "paged_kv_grad_offload", "paged_kv_copy", "pkv_mfma_probe",
     "pkv_timing_enable", "pkv_timing_collect",
     "pkv_timing_get", "paged_kv_page_alloc", "paged_kv_page_release", "paged_kv_pages_available",
-    "page_topk_select_noalloc", "pkv_atomic_probe",
+    "page_topk_select_noalloc", "pkv_atomic_probe", "paged_kv_grad_staging_bytes", "paged_kv_grad_stage",
+    "paged_kv_grad_accumulate",
 )
 
 
@@ -90,6 +91,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "paged_kv_pages_available": (_I, [_P]),
         "page_topk_select_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), _P]),
         "pkv_atomic_probe": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
+        "paged_kv_grad_staging_bytes": (_S, [_P, _I]),
+        "paged_kv_grad_stage": (_I, [_P, _I, _I, _I, _P, _P, _S, _P]),
+        "paged_kv_grad_accumulate": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -380,6 +384,35 @@ def paged_kv_grad_offload(host: Pool, host_bt: torch.Tensor, dev: Pool, dev_bt: 
     n_kvh = host.h_kv - kvh0 if n_kvh is None else n_kvh
     _check(load().paged_kv_grad_offload(host.handle, _ptr(host_bt), host_bt.numel(), dev.handle, _ptr(dev_bt),
                                         dev_bt.numel(), _ptr(lps), lps.numel(), kvh0, n_kvh, _stream(stream)))
+
+
+def grad_staging_bytes(pool: Pool, n: int) -> int:
+    return load().paged_kv_grad_staging_bytes(pool.handle, n)
+
+
+def paged_kv_grad_stage(dev: Pool, dev_page0: int, n: int, kvh: int, lps: torch.Tensor, staging: torch.Tensor,
+                        stream=None):
+    """Copy head kvh's gradient blocks of device pages [dev_page0, dev_page0 + n) and the logical ids
+    lps (int32, device) into pinned host staging (uint8, pinned), then clear those device blocks."""
+    _need(lps, torch.int32, "lps")
+    if lps.numel() < n:
+        raise ValueError(f"lps holds {lps.numel()} ids, {n} needed")
+    if staging.is_cuda or not staging.is_pinned() or not staging.is_contiguous():
+        raise ValueError("staging must be a contiguous pinned host tensor")
+    _check(load().paged_kv_grad_stage(dev.handle, dev_page0, n, kvh, _ptr(lps), _ptr(staging),
+                                      staging.numel() * staging.element_size(), _stream(stream)))
+
+
+def paged_kv_grad_accumulate(host: Pool, host_bt_host: torch.Tensor, n: int, kvh: int, staging: torch.Tensor,
+                             stream=None):
+    """Enqueue the host-side add of n staged blocks into the host pool's gradient pages, head kvh.
+    host_bt_host (int32, host) and staging must stay alive until the stream has passed this call."""
+    if host_bt_host.is_cuda or host_bt_host.dtype != torch.int32 or not host_bt_host.is_contiguous():
+        raise ValueError("host_bt_host must be a contiguous int32 host tensor")
+    if staging.is_cuda or not staging.is_pinned():
+        raise ValueError("staging must be a pinned host tensor")
+    _check(load().paged_kv_grad_accumulate(host.handle, _ptr(host_bt_host), host_bt_host.numel(), n, kvh,
+                                           _ptr(staging), _stream(stream)))
 
 
 def paged_kv_copy(src: Pool, dst: Pool, what: int, first_page: int = 0, n_pages: Optional[int] = None, stream=None):

@@ -55,12 +55,12 @@ def build(verbose: bool = False, extra_hip_flags=None, out: str = LIB, build_dir
     for src in HOST:
         obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
-        jobs.append(["g++", "-O2", "-fPIC", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__",
+        jobs.append(["g++", "-O3", "-fPIC", "-std=c++17", "-Wall", "-pthread", "-D__HIP_PLATFORM_AMD__",
                      "-I" + os.path.join(ROCM, "include"), "-c", os.path.join(csrc, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         logs = list(ex.map(_run, jobs))
     tmp = out + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"])
     os.replace(tmp, out)
     if verbose:
         for lg in logs:

@@ -403,6 +403,29 @@ hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_
   return hipGetLastError();
 }
 
+// Clear head g's gradient block (dK and dV, 2*P*D floats) of physical pages [page0, page0 + n):
+// grid.y walks the pages, grid.x the block's 16-byte chunks.
+__global__ __launch_bounds__(256) void k_zero_head_blocks(float* __restrict__ grad, int32_t P, int32_t H, int32_t D,
+                                                          int32_t page0, int32_t n, int32_t g) {
+  const int64_t n16 = (int64_t)2 * P * D / 4;
+  for (int32_t r = blockIdx.y; r < n; r += gridDim.y) {
+    f32x4* b = reinterpret_cast<f32x4*>(grad + (((int64_t)(page0 + r) * H + g) * 2) * P * D);
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n16; c += (int64_t)gridDim.x * 256)
+      b[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+hipError_t launch_zero_head_blocks(const pkv_pool& pool, int32_t page0, int32_t n, int32_t g, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n16 = (int64_t)2 * pool.page * pool.d / 4;
+  {
+    TimerScope ts_("k_zero_head_blocks", s);
+    hipLaunchKernelGGL(k_zero_head_blocks, dim3((unsigned)((n16 + 255) / 256), (unsigned)(n < 65535 ? n : 65535)),
+                       dim3(256), 0, s, pool.grad, pool.page, pool.h_kv, pool.d, page0, n, g);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_grad_offload(const pkv_pool& host, const int32_t* host_bt, int32_t n_host_bt, const pkv_pool& dev,
                                const int32_t* dev_bt, int32_t n_dev_bt, const int32_t* lp, int32_t n, int32_t kvh0,
                                int32_t n_kvh, hipStream_t s) {

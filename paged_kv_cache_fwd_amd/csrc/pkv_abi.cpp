@@ -3,7 +3,10 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
+#include <condition_variable>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -12,6 +15,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <tuple>
 #include <vector>
 
@@ -24,6 +28,29 @@ struct pkv_page_alloc {
   std::mutex mu;
   std::vector<int32_t> free_pages;  // stack: the most recently released page is handed out first
   std::vector<uint8_t> is_free;     // per physical page
+};
+
+// One host-side accumulation: staged gradient blocks added into a host pool's gradient pages.
+struct pkv_add_job {
+  std::atomic<int32_t> busy{0};
+  float* grad_host = nullptr;        // host pool's gradient pages (host address)
+  int32_t n_pages = 0, h = 0, blk = 0, kvh = 0;  // blk: floats per (page, head) block
+  const int32_t* host_bt = nullptr;  // caller's host copy of the host pool's block table
+  int32_t n_host_bt = 0;
+  const unsigned char* staging = nullptr;
+  int32_t n = 0;
+  std::atomic<int32_t>* err = nullptr;
+};
+
+// Fixed ring of job slots per PKV_HOST_GRADS pool: enqueueing an accumulation allocates nothing.
+// Host code may run far ahead of the stream; when every slot is still pending, the enqueueing call
+// waits for the oldest to run.
+constexpr int kHostJobs = 1024;
+constexpr double kHostJobWaitSeconds = 60.0;
+struct pkv_host_jobs {
+  pkv_add_job slot[kHostJobs];
+  std::atomic<uint32_t> next{0};
+  std::atomic<int32_t> err{0};  // 5: a staged page id outside the block table or the pool
 };
 
 namespace {
@@ -292,9 +319,175 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_
   return p;
 }
 
+// Host threads that add staged gradient blocks into host gradient pages. A job is split by blocks
+// (one (page, head) block each) over the workers and the thread that runs it; the threads are made
+// on first use and live until the process ends. Jobs run one at a time.
+namespace {
+class HostAdder {
+ public:
+  static HostAdder& get() {
+    static HostAdder* inst = new HostAdder();  // never destroyed: callbacks may run during exit
+    return *inst;
+  }
+
+  void run(const pkv_add_job& j) {
+    std::lock_guard<std::mutex> serial(run_mu_);
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      job_ = &j;
+      next_.store(0);
+      ++gen_;
+    }
+    cv_.notify_all();
+    work(j);
+    std::unique_lock<std::mutex> lk(mu_);
+    job_ = nullptr;  // late wakers find no job
+    done_cv_.wait(lk, [&] { return active_ == 0; });
+  }
+
+ private:
+  HostAdder() {
+    int n = 8;
+    if (const char* e = getenv("PKV_HOST_THREADS")) n = atoi(e);
+    const int hw = (int)std::thread::hardware_concurrency();
+    if (hw > 0) n = std::min(n, hw);
+    n = std::max(0, std::min(n, 64));
+    for (int i = 0; i < n; ++i) std::thread([this] { loop(); }).detach();
+  }
+
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      const pkv_add_job* j;
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return gen_ != seen; });
+        seen = gen_;
+        j = job_;
+        if (!j) continue;
+        ++active_;
+      }
+      work(*j);
+      {
+        std::lock_guard<std::mutex> lk(mu_);
+        --active_;
+      }
+      done_cv_.notify_all();
+    }
+  }
+
+  void work(const pkv_add_job& j) {
+    const size_t lp_bytes = align256((size_t)j.n * sizeof(int32_t));
+    const int32_t* lp = reinterpret_cast<const int32_t*>(j.staging);
+    const float* blocks = reinterpret_cast<const float*>(j.staging + lp_bytes);
+    for (;;) {
+      const int32_t i = next_.fetch_add(1);
+      if (i >= j.n) return;
+      const int32_t l = lp[i];
+      const int32_t hp = (l >= 0 && l < j.n_host_bt) ? j.host_bt[l] : -1;
+      if (hp < 0 || hp >= j.n_pages) {
+        int32_t zero = 0;
+        j.err->compare_exchange_strong(zero, 5);
+        continue;
+      }
+      float* dst = j.grad_host + ((size_t)hp * j.h + j.kvh) * j.blk;
+      const float* src = blocks + (size_t)i * j.blk;
+      for (int32_t k = 0; k < j.blk; ++k) dst[k] += src[k];
+    }
+  }
+
+  std::mutex run_mu_, mu_;
+  std::condition_variable cv_, done_cv_;
+  const pkv_add_job* job_ = nullptr;
+  uint64_t gen_ = 0;
+  int active_ = 0;
+  std::atomic<int32_t> next_{0};
+};
+
+void host_add_callback(void* arg) {
+  pkv_add_job* j = static_cast<pkv_add_job*>(arg);
+  HostAdder::get().run(*j);
+  j->busy.store(0);
+}
+}  // namespace
+
 }  // namespace pkv
 
 extern "C" {
+
+size_t paged_kv_grad_staging_bytes(const pkv_pool* pool, int32_t n) {
+  if (!pool || n < 0) return 0;
+  return align256((size_t)n * sizeof(int32_t)) + (size_t)n * 2 * pool->page * pool->d * sizeof(float);
+}
+
+int paged_kv_grad_stage(pkv_pool* dev, int32_t dev_page0, int32_t n, int32_t kvh, const int32_t* lp_dev,
+                        void* staging_host, size_t staging_bytes, void* stream) {
+  if (!dev) return fail(PKV_E_INVALID, "pool is NULL");
+  if (!dev->grad || (dev->flags & PKV_HOST_GRADS)) return fail(PKV_E_STATE, "the pool needs device gradient pages");
+  if (n < 0 || dev_page0 < 0 || (int64_t)dev_page0 + n > dev->n_pages)
+    return fail(PKV_E_INVALID, "pages [%d, %lld) outside the pool (%d pages)", dev_page0, (long long)dev_page0 + n,
+                dev->n_pages);
+  if (kvh < 0 || kvh >= dev->h_kv) return fail(PKV_E_INVALID, "kvh=%d outside [0, %d)", kvh, dev->h_kv);
+  if (n == 0) {
+    ok();
+    return PKV_OK;
+  }
+  if (!lp_dev || !staging_host) return fail(PKV_E_INVALID, "NULL page ids or staging");
+  const size_t need = paged_kv_grad_staging_bytes(dev, n);
+  if (staging_bytes < need) return fail(PKV_E_NOMEM, "staging too small: %zu < %zu bytes", staging_bytes, need);
+  const size_t blk_bytes = (size_t)2 * dev->page * dev->d * sizeof(float);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(staging_host, lp_dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (staged page ids)");
+  const char* src = reinterpret_cast<const char*>(dev->grad) + ((size_t)dev_page0 * dev->h_kv + kvh) * blk_bytes;
+  e = hipMemcpy2DAsync(static_cast<char*>(staging_host) + align256((size_t)n * sizeof(int32_t)), blk_bytes, src,
+                       blk_bytes * dev->h_kv, blk_bytes, (size_t)n, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy2DAsync (staged gradient blocks)");
+  e = pkv::launch_zero_head_blocks(*dev, dev_page0, n, kvh, s);
+  if (e != hipSuccess) return hip_fail(e, "clearing the staged blocks");
+  ok();
+  return PKV_OK;
+}
+
+int paged_kv_grad_accumulate(pkv_pool* host, const int32_t* host_bt_host, int32_t n_host_bt, int32_t n, int32_t kvh,
+                             const void* staging_host, void* stream) {
+  if (!host) return fail(PKV_E_INVALID, "pool is NULL");
+  if (!(host->flags & PKV_HOST_GRADS) || !host->jobs) return fail(PKV_E_STATE, "the pool has no host gradient pages");
+  if (kvh < 0 || kvh >= host->h_kv) return fail(PKV_E_INVALID, "kvh=%d outside [0, %d)", kvh, host->h_kv);
+  if (n < 0 || n_host_bt < 0) return fail(PKV_E_INVALID, "negative count");
+  if (n == 0) {
+    ok();
+    return PKV_OK;
+  }
+  if (!host_bt_host || !staging_host) return fail(PKV_E_INVALID, "NULL block table or staging");
+  pkv_host_jobs& J = *host->jobs;
+  pkv_add_job& j = J.slot[J.next.fetch_add(1) % kHostJobs];
+  const auto t0 = std::chrono::steady_clock::now();
+  for (;;) {
+    int32_t idle = 0;
+    if (j.busy.compare_exchange_strong(idle, 1)) break;
+    if (std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count() > kHostJobWaitSeconds)
+      return fail(PKV_E_STATE, "%d accumulations pending on this pool for %.0f s", kHostJobs, kHostJobWaitSeconds);
+    std::this_thread::sleep_for(std::chrono::microseconds(50));
+  }
+  j.grad_host = static_cast<float*>(host->grad_host);
+  j.n_pages = host->n_pages;
+  j.h = host->h_kv;
+  j.blk = 2 * host->page * host->d;
+  j.kvh = kvh;
+  j.host_bt = host_bt_host;
+  j.n_host_bt = n_host_bt;
+  j.staging = static_cast<const unsigned char*>(staging_host);
+  j.n = n;
+  j.err = &J.err;
+  hipError_t e = hipLaunchHostFunc((hipStream_t)stream, pkv::host_add_callback, &j);
+  if (e != hipSuccess) {
+    j.busy.store(0);
+    return hip_fail(e, "hipLaunchHostFunc (gradient accumulation)");
+  }
+  ok();
+  return PKV_OK;
+}
 
 int pkv_version(void) { return 100; }
 
@@ -388,7 +581,10 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
   p->rep = nullptr;
   p->err = nullptr;
   p->alloc = new (std::nothrow) pkv_page_alloc();
-  if (!p->alloc) {
+  p->jobs = (flags & PKV_HOST_GRADS) ? new (std::nothrow) pkv_host_jobs() : nullptr;
+  if (!p->alloc || ((flags & PKV_HOST_GRADS) && !p->jobs)) {
+    delete p->alloc;
+    delete p->jobs;
     delete p;
     return fail(PKV_E_NOMEM, "out of host memory");
   }
@@ -397,6 +593,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
     p->alloc->is_free.assign((size_t)n_pages, 1);
   } catch (const std::bad_alloc&) {
     delete p->alloc;
+    delete p->jobs;
     delete p;
     return fail(PKV_E_NOMEM, "out of host memory for the page free list");
   }
@@ -404,6 +601,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
   hipError_t e = hipGetDevice(&p->device);
   if (e != hipSuccess) {
     delete p->alloc;
+    delete p->jobs;
     delete p;
     return hip_fail(e, "hipGetDevice");
   }
@@ -418,6 +616,7 @@ int paged_kv_alloc(pkv_pool** out, int32_t n_pages, int32_t page_size, int32_t n
     if (p->rep) (void)hipFree(p->rep);
     if (p->err) (void)hipFree(p->err);
     delete p->alloc;
+    delete p->jobs;
     delete p;
   };
   if (getenv("PKV_FAIL_HOST_ALLOC") && (flags & PKV_HOST_TIER)) {
@@ -513,6 +712,7 @@ int paged_kv_free(pkv_pool* pool) {
   if (pool->rep) (void)hipFree(pool->rep);
   if (pool->err) (void)hipFree(pool->err);
   delete pool->alloc;
+  delete pool->jobs;
   delete pool;
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize in paged_kv_free");
   ok();
@@ -664,6 +864,7 @@ int paged_kv_check(pkv_pool* pool) {
   int32_t word = 0;
   e = hipMemcpy(&word, pool->err, sizeof(word), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "reading the error word");
+  if (pool->jobs && word == 0) word = pool->jobs->err.exchange(0);
   if (word != 0) {
     const int32_t zero = 0;
     e = hipMemcpy(pool->err, &zero, sizeof(zero), hipMemcpyHostToDevice);
@@ -671,6 +872,7 @@ int paged_kv_check(pkv_pool* pool) {
     const char* what = word == 1   ? "block-table entry outside the pool"
                        : word == 2 ? "selected page outside [0, n_prior)"
                        : word == 3 ? "logical page beyond the block table"
+                       : word == 5 ? "staged gradient page outside the host block table or pool"
                                    : "gather destination outside the device pool";
     return fail(PKV_E_DEVICE, "a kernel skipped a page: %s", what);
   }

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 struct pkv_page_alloc;  // host-side free list of physical pages (pkv_abi.cpp)
+struct pkv_host_jobs;   // host-side gradient accumulation jobs of a PKV_HOST_GRADS pool (pkv_abi.cpp)
 
 struct pkv_pool {
   int32_t n_pages;
@@ -21,6 +22,7 @@ struct pkv_pool {
   float* rep;         // fp32 representative key per (page, head)
   int32_t* err;       // device word: nonzero once a kernel met an out-of-range table entry
   pkv_page_alloc* alloc;  // free list of physical pages handed out by paged_kv_page_alloc
+  pkv_host_jobs* jobs;    // host gradient accumulation (PKV_HOST_GRADS pools only, else NULL)
 };
 
 namespace pkv {
@@ -104,6 +106,7 @@ hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_
 hipError_t launch_grad_offload(const pkv_pool& host, const int32_t* host_bt, int32_t n_host_bt, const pkv_pool& dev,
                                const int32_t* dev_bt, int32_t n_dev_bt, const int32_t* lp, int32_t n, int32_t kvh0,
                                int32_t n_kvh, hipStream_t s);
+hipError_t launch_zero_head_blocks(const pkv_pool& pool, int32_t page0, int32_t n, int32_t g, hipStream_t s);
 size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d, int32_t n_lists);
 // Static scratch of page_topk_select_noalloc: a file-scope device array in k_select.hip, one copy per
 // GPU. topk_scratch_ptr returns the current device's copy (looked up once per device).

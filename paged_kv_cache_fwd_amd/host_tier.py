@@ -19,15 +19,22 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import (PKV_COPY_GRAD, PKV_COPY_KV, Pool, chunk_attn_bwd, chunk_attn_bwd_ws_bytes, chunk_attn_fwd,
-               chunk_attn_fwd_ws_bytes, load, page_topk_select, paged_kv_copy, paged_kv_gather, paged_kv_grad_offload)
+               chunk_attn_fwd_ws_bytes, grad_staging_bytes, load, page_topk_select, paged_kv_copy, paged_kv_gather,
+               paged_kv_grad_accumulate, paged_kv_grad_offload, paged_kv_grad_stage)
 
 
 class HostTierStep:
     """Reusable buffers and streams for the sparse step of one chunk shape over a host-tier pool."""
 
     def __init__(self, host: Pool, host_bt: torch.Tensor, n_prior: int, C: int, H_q: int, top_k: int,
-                 n_local: int, device: torch.device):
+                 n_local: int, device: torch.device, grad_offload: str = "staged"):
+        """grad_offload (gradient pages in host memory only): "staged" copies each head's device
+        gradient slots to pinned staging with the copy engines and adds them into the host pages on
+        host threads (paged_kv_grad_stage / paged_kv_grad_accumulate); "kernel" adds them with a
+        kernel that reads and writes the host pages over the host link (paged_kv_grad_offload)."""
         assert host.host_tier
+        assert grad_offload in ("staged", "kernel")
+        self.grad_offload = grad_offload
         self.host, self.host_bt = host, host_bt
         self.n_prior, self.C, self.H_q = n_prior, C, H_q
         self.top_k, self.n_local = top_k, n_local
@@ -51,6 +58,7 @@ class HostTierStep:
                                    device=device) for g in range(H)]
         self.sel = [torch.empty((H, self.n_sel), dtype=torch.int32, device=device) for _ in range(2)]
         self.parity = 0
+        self._pre: Optional[torch.Tensor] = None  # queries whose selection a lookahead enqueued
         self.own_lps = torch.arange(n_prior, n_prior + self.n_own, dtype=torch.int32, device=device)
         lib = load()
         self.ws_t = torch.empty(max(lib.page_topk_ws_bytes(host.handle, n_prior, C, H_q, 1), 1), dtype=torch.uint8,
@@ -69,8 +77,32 @@ class HostTierStep:
         # sel[b][g] and bt[b][g] and clears head g's device gradient slots).
         self.off_done = [[torch.cuda.Event() for _ in range(H)] for _ in range(2)]
         self.own_done = torch.cuda.Event()  # the last head's own-page offload
-        for ev in self.done + self.off_done[0] + self.off_done[1] + [self.own_done]:
+        # Staged offload: pinned staging per (buffer, head) for the own pages and the selected slots,
+        # the host copy of the host pool's block table, and a stream that runs the host-side adds.
+        # added[b][g]: the adds that last read staging[b][g] have run.
+        self.staged = self.host_grads and grad_offload == "staged"
+        self.added = [[torch.cuda.Event() for _ in range(H)] for _ in range(2)]
+        if self.staged:
+            self.acc = torch.cuda.Stream(device=device)
+            self.host_bt_host = host_bt.to("cpu").contiguous()
+            nb_own = grad_staging_bytes(host, self.n_own)
+            nb_sel = grad_staging_bytes(host, self.n_sel)
+            self.stg_own = [[torch.empty(nb_own, dtype=torch.uint8, pin_memory=True) for _ in range(H)]
+                            for _ in range(2)]
+            self.stg_sel = [[torch.empty(max(nb_sel, 1), dtype=torch.uint8, pin_memory=True) for _ in range(H)]
+                            for _ in range(2)]
+        for ev in self.done + self.off_done[0] + self.off_done[1] + self.added[0] + self.added[1] + [self.own_done]:
             ev.record(torch.cuda.current_stream(device))
+
+    @property
+    def last_sel(self) -> torch.Tensor:
+        """The selection of the last step that gathered."""
+        return self.sel[self.parity ^ 1]
+
+    @property
+    def last_bt(self) -> List[torch.Tensor]:
+        """The per-head device block tables of the last step that gathered."""
+        return self.bt[self.parity ^ 1]
 
     def append_own(self, k: torch.Tensor, v: torch.Tensor):
         """Append the chunk's own K/V ([C][H_kv][d] bf16) into its device pages.
@@ -82,18 +114,61 @@ class HostTierStep:
             torch.cuda.current_stream(k.device).wait_event(self.own_done)
         self.dev.append(self.own_bt, self.n_prior * self.dev.page, k, v)
 
+    def cancel_lookahead(self):
+        """Drop the selection and first gather that the last run() enqueued for next_q: the next run()
+        then selects and gathers anew (after that gather has finished reading its selection)."""
+        if self._pre is not None:
+            torch.cuda.current_stream(self._pre.device).wait_event(self.ready[0])
+            self._pre = None
+
+    def _lookahead(self, next_q: torch.Tensor, compute):
+        """Enqueue on the side stream the next step's selection (into the next step's buffers) and its
+        first head's gather, behind this step's gathers and head 0's backward, so that they run
+        beside this step's remaining heads instead of at the start of the next step."""
+        H = self.host.h_kv
+        nb = self.parity  # the next step's buffers
+        after = torch.cuda.Event()
+        after.record(compute)  # next_q is ready, and head 0's slots are no longer read (done[0])
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(after)
+            if self.host_grads:
+                self.side.wait_event(self.off_done[nb][H - 1])  # sel[nb] no longer read by an offload
+            page_topk_select(self.host, self.host_bt, self.n_prior, next_q, self.top_k, self.n_local,
+                             sel=self.sel[nb], ws=self.ws_t, stream=self.side)
+            if self.host_grads:
+                self.side.wait_event(self.off_done[nb][0])  # bt[nb][0] no longer read by an offload
+            paged_kv_gather(self.host, self.dev, self.host_bt, self.sel[nb][0], 0, self.slots[0],
+                            dev_bt_out=self.bt[nb][0], stream=self.side)
+            self.ready[0].record(self.side)
+        self._pre = next_q
+
     def run(self, q: torch.Tensor, dout: torch.Tensor, scale: float, o: torch.Tensor, lse: torch.Tensor,
-            dq: torch.Tensor, gather: bool = True):
+            dq: torch.Tensor, gather: bool = True, next_q: Optional[torch.Tensor] = None):
         """One sparse step. With gather=False the slots are assumed filled already (for timing the
         same selection without host traffic; not with gradient pages in host memory).
 
-        Gradient pages in host memory: head g's backward accumulates into its device slots, and an
-        offload stream then adds them, and head g's blocks of the chunk's own pages, to the host pages
-        and clears them (paged_kv_grad_offload). The next step's backward of head g waits for that
-        offload, so a slot is cleared before it is reused."""
+        next_q (the next step's queries, already written on the current stream): the next step's page
+        selection and its first head's gather are enqueued on the side stream beside this step's
+        last heads, so that the next step starts with head 0's pages in place. The next run() must
+        then take that same tensor as q (or cancel_lookahead() must come first).
+
+        Gradient pages in host memory: head g's backward accumulates into its device slots. An
+        offload stream then copies them, and head g's blocks of the chunk's own pages, to pinned
+        staging and clears them (paged_kv_grad_stage), and a second stream has the library's host
+        threads add the staging into the host pages (paged_kv_grad_accumulate); with
+        grad_offload="kernel" one kernel adds the device blocks into the host pages over the host
+        link and clears them (paged_kv_grad_offload). The next step's backward of head g waits for
+        the clearing, so a slot is cleared before it is reused. Host gradient pages are complete
+        once the accumulation stream has passed the step (torch.cuda.synchronize())."""
         assert gather or not self.host_grads
+        assert next_q is None or gather
         compute = torch.cuda.current_stream(q.device)
         H = self.host.h_kv
+        pre = self._pre is not None
+        if pre:
+            if self._pre is not q or not gather:
+                raise ValueError("the last step looked ahead to other queries: pass them as q, or cancel_lookahead()")
+            self._pre = None
         if gather:
             b = self.parity
             self.parity ^= 1
@@ -101,12 +176,15 @@ class HostTierStep:
             b = self.parity ^ 1  # the buffers the last gathering step filled
         prev = b ^ 1
         bts = self.bt[b]
-        if self.host_grads:
-            # sel[b] was last read by the offloads of the step before the previous one; the offload
-            # stream runs in order, so its last head's event covers them all.
-            compute.wait_event(self.off_done[b][H - 1])
-        sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local, sel=self.sel[b],
-                               ws=self.ws_t)
+        if pre:
+            sel = self.sel[b]  # selected, and head 0 gathered, by the last step's lookahead
+        else:
+            if self.host_grads:
+                # sel[b] was last read by the offloads of the step before the previous one; the offload
+                # stream runs in order, so its last head's event covers them all.
+                compute.wait_event(self.off_done[b][H - 1])
+            sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local,
+                                   sel=self.sel[b], ws=self.ws_t)
 
         def enqueue_gather(g, after=None):
             # Events are waited on at their latest record: `after` is this step's selection, done[g]
@@ -122,11 +200,12 @@ class HostTierStep:
                 self.ready[g].record(self.side)
 
         if gather:
-            sel_ready = torch.cuda.Event()
-            sel_ready.record(compute)
-            enqueue_gather(0, sel_ready)
+            if not pre:
+                sel_ready = torch.cuda.Event()
+                sel_ready.record(compute)
+                enqueue_gather(0, sel_ready)
             for g in range(1, H):
-                enqueue_gather(g)
+                enqueue_gather(g)  # behind the selection on the side stream when it came from a lookahead
         for g in range(H):
             if gather:
                 compute.wait_event(self.ready[g])
@@ -141,7 +220,26 @@ class HostTierStep:
                 chunk_attn_bwd(self.dev, bts[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
                                gpool=self.host, gbt=self.host_bt, dq=dq, ws=self.ws_b)
             self.done[g].record(compute)
-            if self.host_grads:
+            if g == 0 and next_q is not None:
+                self._lookahead(next_q, compute)
+            if self.staged:
+                with torch.cuda.stream(self.off):
+                    self.off.wait_event(self.done[g])
+                    self.off.wait_event(self.added[b][g])  # staging[b][g] read by the adds of two steps ago
+                    # Own pages first: the next chunk's append waits for them, not for the slots.
+                    paged_kv_grad_stage(self.dev, 0, self.n_own, g, self.own_lps, self.stg_own[b][g], stream=self.off)
+                    self.own_done.record(self.off)
+                    paged_kv_grad_stage(self.dev, self.n_own + g * self.n_sel, self.n_sel, g, sel[g],
+                                        self.stg_sel[b][g], stream=self.off)
+                    self.off_done[b][g].record(self.off)
+                with torch.cuda.stream(self.acc):
+                    self.acc.wait_event(self.off_done[b][g])
+                    paged_kv_grad_accumulate(self.host, self.host_bt_host, self.n_own, g, self.stg_own[b][g],
+                                             stream=self.acc)
+                    paged_kv_grad_accumulate(self.host, self.host_bt_host, self.n_sel, g, self.stg_sel[b][g],
+                                             stream=self.acc)
+                    self.added[b][g].record(self.acc)
+            elif self.host_grads:
                 with torch.cuda.stream(self.off):
                     self.off.wait_event(self.done[g])
                     # Only head g's backward writes head g's blocks of the own pages. They go first:

@@ -11,6 +11,8 @@
 #include <limits>
 #include <vector>
 
+#include <hip/hip_runtime_api.h>
+
 #include "../../include/pkv.h"
 
 extern long g_stub_launches;
@@ -293,12 +295,85 @@ static void check_compute_validation() {
   CHECK(fake_hip_live_device() == 0 && fake_hip_live_host() == 0);
 }
 
+// The staged gradient offload: a rectangular copy of one head's device blocks to staging, the
+// device blocks cleared, and the host threads' adds into the host pages the staged ids name.
+static void check_staged_offload() {
+  const int32_t NP = 16, P = 64, H = 2, D = 64, blk = 2 * P * D;
+  pkv_pool* dev = nullptr;
+  pkv_pool* hg = nullptr;
+  pkv_pool* ho = nullptr;
+  CHECK(paged_kv_alloc(&dev, NP, P, H, D, PKV_GRADS) == PKV_OK);
+  CHECK(paged_kv_alloc(&hg, NP, P, H, D, PKV_HOST_TIER | PKV_GRADS | PKV_HOST_GRADS) == PKV_OK);
+  CHECK(paged_kv_alloc(&ho, NP, P, H, D, PKV_HOST_TIER | PKV_GRADS) == PKV_OK);
+  float* dg = static_cast<float*>(paged_kv_data(dev, PKV_DK));
+  float* hgr = static_cast<float*>(paged_kv_data(hg, PKV_DK));  // the fake maps host memory 1:1
+  for (int32_t pg = 0; pg < NP; ++pg)
+    for (int32_t g = 0; g < H; ++g)
+      for (int32_t k = 0; k < blk; ++k) dg[((size_t)pg * H + g) * blk + k] = 1000.f * pg + 100.f * g + (float)(k % 7);
+  int32_t host_bt[NP];
+  for (int32_t i = 0; i < NP; ++i) host_bt[i] = (i * 5 + 3) % NP;  // a permutation
+  alignas(256) static int32_t lp[3] = {3, 7, 11};
+  const size_t need = paged_kv_grad_staging_bytes(dev, 3);
+  CHECK(need == 256 + 3 * (size_t)blk * 4);
+  void* stg = nullptr;
+  CHECK(hipHostMalloc(&stg, need, 0) == hipSuccess);
+  for (int rep = 1; rep <= 2; ++rep) {
+    if (rep == 2)  // refill the device blocks the first stage cleared
+      for (int32_t i = 0; i < 3; ++i)
+        for (int32_t k = 0; k < blk; ++k) dg[((size_t)(2 + i) * H + 1) * blk + k] = 1000.f * (2 + i) + 100.f + (float)(k % 7);
+    ENQUEUES(1, paged_kv_grad_stage(dev, 2, 3, 1, lp, stg, need, nullptr));
+    ENQUEUES(0, paged_kv_grad_accumulate(hg, host_bt, NP, 3, 1, stg, nullptr));
+    bool ok_host = true, ok_dev = true, ok_rest = true;
+    for (int32_t i = 0; i < 3; ++i)
+      for (int32_t k = 0; k < blk; ++k) {
+        const float want = rep * (1000.f * (2 + i) + 100.f + (float)(k % 7));
+        ok_host &= hgr[((size_t)host_bt[lp[i]] * H + 1) * blk + k] == want;
+        ok_dev &= dg[((size_t)(2 + i) * H + 1) * blk + k] == 0.f;
+        ok_rest &= dg[((size_t)(2 + i) * H + 0) * blk + k] == 1000.f * (2 + i) + (float)(k % 7);
+      }
+    CHECK(ok_host);
+    CHECK(ok_dev);
+    CHECK(ok_rest);
+  }
+  double other = 0.0;  // host blocks nobody staged stay zero
+  for (int32_t pg = 0; pg < NP; ++pg)
+    for (int32_t g = 0; g < H; ++g) {
+      const bool staged = g == 1 && (pg == host_bt[3] || pg == host_bt[7] || pg == host_bt[11]);
+      if (!staged)
+        for (int32_t k = 0; k < blk; ++k) other += std::fabs(hgr[((size_t)pg * H + g) * blk + k]);
+    }
+  CHECK(other == 0.0);
+  CHECK(paged_kv_check(hg) == PKV_OK);
+  // A staged id outside the host table is skipped and reported.
+  alignas(256) static int32_t bad_lp[1] = {99};
+  ENQUEUES(1, paged_kv_grad_stage(dev, 0, 1, 0, bad_lp, stg, need, nullptr));
+  ENQUEUES(0, paged_kv_grad_accumulate(hg, host_bt, NP, 1, 0, stg, nullptr));
+  CHECK(paged_kv_check(hg) == PKV_E_DEVICE);
+  CHECK(paged_kv_check(hg) == PKV_OK);
+  // Argument errors: nothing enqueued.
+  FAILS(PKV_E_NOMEM, paged_kv_grad_stage(dev, 2, 3, 1, lp, stg, need - 1, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_grad_stage(dev, 14, 3, 1, lp, stg, need, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_grad_stage(dev, 2, 3, 2, lp, stg, need, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_grad_stage(dev, 2, 3, 1, nullptr, stg, need, nullptr));
+  FAILS(PKV_E_STATE, paged_kv_grad_stage(hg, 2, 3, 1, lp, stg, need, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_grad_stage(nullptr, 2, 3, 1, lp, stg, need, nullptr));
+  FAILS(PKV_E_STATE, paged_kv_grad_accumulate(ho, host_bt, NP, 3, 1, stg, nullptr));
+  FAILS(PKV_E_STATE, paged_kv_grad_accumulate(dev, host_bt, NP, 3, 1, stg, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_grad_accumulate(hg, host_bt, NP, 3, 2, stg, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_grad_accumulate(hg, nullptr, NP, 3, 1, stg, nullptr));
+  CHECK(paged_kv_grad_staging_bytes(nullptr, 3) == 0);
+  CHECK(hipHostFree(stg) == hipSuccess);
+  for (pkv_pool* x : {dev, hg, ho}) CHECK(paged_kv_free(x) == PKV_OK);
+  CHECK(fake_hip_live_device() == 0 && fake_hip_live_host() == 0);
+}
+
 int main() {
   CHECK(pkv_version() > 0);
   check_alloc_errors();
   check_alloc_failures();
   check_page_allocator();
   check_compute_validation();
+  check_staged_offload();
   std::printf("%d checks, %d failed\n", g_checks, g_failures);
   return g_failures == 0 ? 0 : 1;
 }

@@ -148,6 +148,23 @@ hipError_t hipMemcpyAsync(void* dst, const void* src, size_t sizeBytes, hipMemcp
   return hipSuccess;
 }
 
+hipError_t hipMemcpy2DAsync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height,
+                             hipMemcpyKind kind, hipStream_t stream) {
+  (void)kind;
+  (void)stream;
+  if (width > dpitch || width > spitch) return hipErrorInvalidValue;
+  for (size_t r = 0; r < height; ++r)
+    std::memcpy((char*)dst + r * dpitch, (const char*)src + r * spitch, width);
+  return hipSuccess;
+}
+
+// Host functions run at once: with no device work pending, stream order is call order.
+hipError_t hipLaunchHostFunc(hipStream_t stream, hipHostFn_t fn, void* userData) {
+  (void)stream;
+  fn(userData);
+  return hipSuccess;
+}
+
 hipError_t hipDeviceSynchronize(void) { return hipSuccess; }
 
 hipError_t hipGetLastError(void) {

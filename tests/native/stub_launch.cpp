@@ -26,6 +26,15 @@ hipError_t launch_gather(const pkv_pool&, const pkv_pool&, const int32_t*, int32
   ++g_stub_launches;
   return hipSuccess;
 }
+// Clears the blocks for real (the fake device memory is host memory), so the checks can follow
+// the staged offload's data.
+hipError_t launch_zero_head_blocks(const pkv_pool& pool, int32_t page0, int32_t n, int32_t g, hipStream_t) {
+  ++g_stub_launches;
+  const size_t blk = (size_t)2 * pool.page * pool.d;
+  for (int32_t i = 0; i < n; ++i)
+    for (size_t k = 0; k < blk; ++k) pool.grad[((size_t)(page0 + i) * pool.h_kv + g) * blk + k] = 0.f;
+  return hipSuccess;
+}
 hipError_t launch_grad_offload(const pkv_pool&, const int32_t*, int32_t, const pkv_pool&, const int32_t*, int32_t,
                                const int32_t*, int32_t, int32_t, int32_t, hipStream_t) {
   ++g_stub_launches;

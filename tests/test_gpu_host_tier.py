@@ -131,7 +131,8 @@ def test_host_grads_small_parity_and_accumulation(pkv):
     hpool.free()
 
 
-def test_host_grads_back_to_back_steps_with_different_selections(pkv):
+@pytest.mark.parametrize("offload", ["staged", "kernel"])
+def test_host_grads_back_to_back_steps_with_different_selections(pkv, offload):
     """Gradient pages in host memory over two steps enqueued back to back whose queries, and so page
     selections, differ. The second step selects and gathers while the first step's gradient offload
     may still be running, so the offload must keep reading its own step's selection and device block
@@ -142,10 +143,10 @@ def test_host_grads_back_to_back_steps_with_different_selections(pkv):
     wl2 = wl.with_seed(24)  # the second step's queries and output gradients
     c, top_k, n_local = 7, 6, 2
     n_prior, C, P = wl.n_prior(c), wl.chunk, wl.page
-    say("host gradient pages: two back-to-back steps with different selections")
+    say(f"host gradient pages ({offload} offload): two back-to-back steps with different selections")
     bt_np = synth.page_permutation(wl)
     hpool, hbt = fill_pool(pkv, wl, wl.n_pages, bt_np, host_tier=True, host_grads=True)
-    step = HostTierStep(hpool, hbt, n_prior, C, wl.h_q, top_k, n_local, torch.device("cuda:0"))
+    step = HostTierStep(hpool, hbt, n_prior, C, wl.h_q, top_k, n_local, torch.device("cuda:0"), grad_offload=offload)
     k, v = synth.kv_tokens(wl, 0, wl.n_pages)
     step.append_own(t16(k[n_prior * P:]), t16(v[n_prior * P:]))
     hpool.zero_grad()
@@ -187,6 +188,46 @@ def test_host_grads_back_to_back_steps_with_different_selections(pkv):
     assert not np.any(slots) and not np.any(slots_v)
     step.free()
     hpool.free()
+
+
+def test_host_tier_lookahead_matches_plain_steps(pkv):
+    """Three steps with different queries, each looking ahead to the next one's selection and first
+    gather (run(..., next_q=...)), against the same steps run plainly: selections, O, LSE and dQ equal
+    bit for bit, and the host gradient pages (staged offload) equal to fp32 atomic-order rounding."""
+    from paged_kv_cache_fwd_amd.host_tier import HostTierStep
+    wl = synth.Workload("host-small", 14, 2, 128, 128, 128 * 24, 384, (7,), offset_std=0.5, seed=25)
+    c, top_k, n_local = 7, 6, 2
+    n_prior, C, P = wl.n_prior(c), wl.chunk, wl.page
+    say("host tier lookahead: 3 steps with next-step selection and first gather overlapped")
+    bt_np = synth.page_permutation(wl)
+    k, v = synth.kv_tokens(wl, 0, wl.n_pages)
+    qs = [t16(synth.q_chunk(wl.with_seed(s), c)) for s in (25, 26, 27)]
+    dos = [t16(synth.do_chunk(wl.with_seed(s), c)) for s in (25, 26, 27)]
+    runs = []
+    for lookahead in (False, True):
+        hpool, hbt = fill_pool(pkv, wl, wl.n_pages, bt_np, host_tier=True, host_grads=True)
+        step = HostTierStep(hpool, hbt, n_prior, C, wl.h_q, top_k, n_local, torch.device("cuda:0"))
+        step.append_own(t16(k[n_prior * P:]), t16(v[n_prior * P:]))
+        hpool.zero_grad()
+        outs = []
+        for i, (q, do) in enumerate(zip(qs, dos)):
+            o, dq = torch.empty_like(q), torch.empty_like(q)
+            lse = torch.empty((wl.h_q, C), dtype=torch.float32, device=q.device)
+            nxt = qs[i + 1] if lookahead and i + 1 < len(qs) else None
+            sel = step.run(q, do, wl.scale, o, lse, dq, next_q=nxt)
+            outs.append((sel.clone(), o, lse, dq))
+        torch.cuda.synchronize()
+        dk = hpool.export(pkv.PKV_DK, hbt, 0, wl.n_pages).cpu().numpy()
+        hpool.check()
+        step.dev.check()
+        runs.append((outs, dk))
+        step.free()
+        hpool.free()
+    (plain, dk0), (ahead, dk1) = runs
+    for i, (a, b) in enumerate(zip(plain, ahead)):
+        for name, x, y in zip(("selection", "O", "LSE", "dQ"), a, b):
+            assert torch.equal(x, y), f"step {i}: {name} differs with the lookahead"
+    compare("host dK, lookahead vs plain", dk1, dk0, 1e-5, rel=1e-5)
 
 
 def test_dense_layer_prefetch_matches_resident(pkv):

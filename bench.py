@@ -33,7 +33,8 @@ LOCAL_WINDOW = 1  # pages kept by a local (sliding-window) layer
 # HBM bytes per launch of the dense 256K step's attention kernels, from one FETCH_SIZE and one
 # WRITE_SIZE rocprofv3 pass each, scaled by what those counters read for a plain 1 GiB streaming
 # kernel (x2.0 fetch, x1.0 write). Valid only for the kernel sources they were taken on.
-TRAFFIC_SOURCES = ("paged_kv_cache_fwd_amd/csrc/k_attn_fwd.hip", "paged_kv_cache_fwd_amd/csrc/k_attn_bwd.hip",
+TRAFFIC_SOURCES = ("paged_kv_cache_fwd_amd/csrc/k_attn_fwd.hip", "paged_kv_cache_fwd_amd/csrc/k_attn_fwd64.hip",
+                   "paged_kv_cache_fwd_amd/csrc/k_attn_bwd.hip",
                    "paged_kv_cache_fwd_amd/csrc/k_attn_dkdv.hip", "paged_kv_cache_fwd_amd/csrc/pkv_device.h", "paged_kv_cache_fwd_amd/csrc/pkv_internal.h",
                    "paged_kv_cache_fwd_amd/csrc/pkv_abi.cpp", "paged_kv_cache_fwd_amd/build.py")
 TRAFFIC_SHA = "33ed4c61ed7898a6"
@@ -695,13 +696,13 @@ def main():
         log(f"[bench]   {kname:18s} launches {n:4d}  avg {ms / n:.3f} ms")
 
     # Roofline of the dominant kernel: its own algorithmic MFMA work per launch / its average duration.
-    kernel_flop = {"k_attn_fwd": 4.0 * d * H_q * pd, "k_bwd_dq": 6.0 * d * H_q * pd,
-                   "k_bwd_dkdv": 8.0 * d * H_q * pd}
+    kernel_flop = {"k_attn_fwd": 4.0 * d * H_q * pd, "k_attn_fwd64": 4.0 * d * H_q * pd,
+                   "k_bwd_dq": 6.0 * d * H_q * pd, "k_bwd_dkdv": 8.0 * d * H_q * pd}
     dom = max(kt_dense.items(), key=lambda x: x[1][1])[0]
     n_l, tot_ms = kt_dense[dom]
     avg_ms = tot_ms / n_l
     def split_ms(kt):
-        fwd = sum(v[1] / v[0] for k, v in kt.items() if k in ("k_attn_fwd", "k_fwd_combine"))
+        fwd = sum(v[1] / v[0] for k, v in kt.items() if k in ("k_attn_fwd", "k_attn_fwd64", "k_fwd_combine"))
         bwd = sum(v[1] / v[0] for k, v in kt.items() if k.startswith("k_bwd"))
         return round(fwd, 4), round(bwd, 4)
 
@@ -709,7 +710,8 @@ def main():
     if dom in kernel_flop:
         ach = kernel_flop[dom] / (avg_ms * 1e-3) / 1e12
         tb = traffic_bytes(dom)
-        credited = {"k_attn_fwd": "4*d (S, PV)", "k_bwd_dq": "6*d (S and dP recomputed, dQ)",
+        credited = {"k_attn_fwd": "4*d (S, PV)", "k_attn_fwd64": "4*d (S, PV)",
+                    "k_bwd_dq": "6*d (S and dP recomputed, dQ)",
                     "k_bwd_dkdv": "8*d (S and dP recomputed, dV, dK)"}[dom]
         bwd_flop = 10.0 * d * H_q * pd
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -19,6 +20,7 @@ KERNELS = {
     "k_select.hip": ["-ffp-contract=off"],
     # MFMA results stay in architectural VGPRs (the softmax and gradient math reads them there).
     "k_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_attn_fwd64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     # dQ pass: the ILP-maximising machine scheduler measured about 1.7% faster here (and slower on
     # the forward, which keeps the default).
     "k_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
@@ -26,6 +28,9 @@ KERNELS = {
     "k_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 HOST = ["pkv_abi.cpp"]
+# Kernels whose written-out MFMAs carry no hazard padding of their own: the emitted assembly is
+# checked at every build for the VALU-write / MFMA-read rule (see check_mfma_operand_waits).
+ASM_CHECKED = ["k_attn_fwd64.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
@@ -40,6 +45,80 @@ def _run(cmd):
     if r.returncode != 0:
         raise RuntimeError("build step failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
     return r.stderr
+
+
+_INSN = re.compile(r"^\s+([a-z][a-z0-9_]*)(?:\s+(.*))?$")
+_REG = re.compile(r"\b([va])(?:\[(\d+):(\d+)\]|(\d+)(?![0-9]))")
+
+
+def _reg_set(text):
+    out = set()
+    for m in _REG.finditer(text):
+        lo = int(m.group(2) if m.group(2) is not None else m.group(4))
+        hi = int(m.group(3) if m.group(3) is not None else m.group(4))
+        out.update((m.group(1), r) for r in range(lo, hi + 1))
+    return out
+
+
+def _split_operands(args):
+    ops, depth, cur = [], 0, ""
+    for ch in args:
+        if ch == "[":
+            depth += 1
+        elif ch == "]":
+            depth -= 1
+        if ch == "," and depth == 0:
+            ops.append(cur.strip())
+            cur = ""
+        else:
+            cur += ch
+    if cur.strip():
+        ops.append(cur.strip())
+    return ops
+
+
+def check_mfma_operand_waits(asm: str, need: int = 2):
+    """Violations of the gfx950 rule that an MFMA may read a VGPR/AGPR written by a VALU instruction
+    only `need` wait states later (each issued instruction is one wait state, s_nop N is N+1), in
+    compiled assembly text. A block label inside the window counts as a violation (its predecessors
+    are not followed). Returns a list of (line number, text) of the offending MFMAs."""
+    bad = []
+    window = []  # (kind, written registers, wait states) of the instructions since the last label
+    for no, raw in enumerate(asm.split("\n"), 1):
+        line = raw.split(";")[0].rstrip()
+        if not line.strip():
+            continue
+        if not line[0].isspace():
+            if line.endswith(":"):
+                window = [("label", set(), 0)]
+            continue
+        m = _INSN.match(line)
+        if not m or m.group(1).startswith("."):
+            continue
+        op, args = m.group(1), m.group(2) or ""
+        ops = _split_operands(args)
+        if op.startswith("v_mfma"):
+            srcs = set()
+            for o in ops[1:4]:
+                srcs |= _reg_set(o)
+            ws = 0
+            for kind, dst, w in reversed(window):
+                if ws >= need:
+                    break
+                if kind == "label" or (kind == "valu" and dst & srcs):
+                    bad.append((no, raw.strip()))
+                    break
+                ws += w
+        if op == "s_nop":
+            w = int(ops[0], 0) + 1 if ops else 1
+        else:
+            w = 1
+        valu = (op.startswith("v_") and not op.startswith("v_mfma") and not op.startswith("v_cmp")
+                and op not in ("v_readfirstlane_b32", "v_readlane_b32"))
+        window.append(("valu" if valu else "other", _reg_set(ops[0]) if (valu and ops) else set(), w))
+        if len(window) > 64:
+            window = window[-64:]
+    return bad
 
 
 def build(verbose: bool = False, extra_hip_flags=None, out: str = LIB, build_dir: str = BUILD,
@@ -57,8 +136,20 @@ def build(verbose: bool = False, extra_hip_flags=None, out: str = LIB, build_dir
         objs.append(obj)
         jobs.append(["g++", "-O3", "-fPIC", "-std=c++17", "-Wall", "-pthread", "-D__HIP_PLATFORM_AMD__",
                      "-I" + os.path.join(ROCM, "include"), "-c", os.path.join(csrc, src), "-o", obj])
+    checks = []
+    for src in ASM_CHECKED:
+        asm_out = os.path.join(build_dir, src + ".s")
+        checks.append(asm_out)
+        jobs.append([HIPCC, *HIP_FLAGS, *KERNELS[src], *(extra_hip_flags or []), "--cuda-device-only", "-S",
+                     os.path.join(csrc, src), "-o", asm_out])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         logs = list(ex.map(_run, jobs))
+    for asm_out in checks:
+        with open(asm_out) as fh:
+            bad = check_mfma_operand_waits(fh.read())
+        if bad:
+            raise RuntimeError("MFMA operand written by VALU without 2 wait states in %s:\n%s" %
+                               (asm_out, "\n".join("  line %d: %s" % b for b in bad[:20])))
     tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs, "-lpthread"])
     os.replace(tmp, out)

@@ -44,25 +44,6 @@ struct DkvCfg {
 static_assert(DkvCfg<128>::SEG_PER_WAVE == 2 && DkvCfg<64>::SEG_PER_WAVE == 1, "staging split");
 static_assert(NKT_TILES_PER_WG == DkvCfg<128>::NW * DkvCfg<128>::NKT, "host plan and kernel disagree");
 
-// dK/dV accumulate in AGPRs for the whole kernel (the file is built with MFMA results in VGPRs,
-// which the softmax needs for S and dP); the instruction is written out so that its accumulator is
-// pinned to the AGPR file. The compiler's hazard recognizer does not see inline assembly as an
-// MFMA, so the wait states it would insert are part of the statement: a VALU write of a VGPR
-// followed by an MFMA that reads it (here the bf16 P / dS operands, packed by VALU conversions, and
-// any VALU move assembling an operand) needs 2 wait states (CDNA3 instruction set reference, the
-// MAI dependency-resolution table: "VALU write VGPR, V_MFMA* read of that VGPR"; gfx950 keeps the
-// rule), which s_nop 1 provides. Back-to-back MFMAs accumulating into the same registers need none.
-__device__ __forceinline__ void mfma32_agpr(f32x16& c, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-
-// Read-back fence for an AGPR accumulator: an XDL (MFMA) write of a register followed by a VALU
-// read of it, v_accvgpr_read included, needs the MFMA's pass count plus 2 wait states (same table:
-// "XDL write VGPR/AGPR, VALU read"; 18 for a 16-pass MFMA, fewer for 8 passes). The three s_nop 7
-// give 24. The accumulator is an in/out operand, so the statement is ordered after every MFMA that
-// writes it and before every read of it. It runs once per workgroup, at the end.
-__device__ __forceinline__ void agpr_readback_fence(f32x16& c) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c)); }
-
 // x / G for 0 <= x < 2^24 from a float reciprocal, corrected to the exact quotient.
 __device__ __forceinline__ int32_t div_small_kv(int32_t x, int32_t G, float invG) {
   int32_t q = (int32_t)((float)x * invG);

@@ -22,6 +22,9 @@
 // accumulator layout gives P^T (4 keys from each half-wave, twice per 16-key step).
 // The running maximum is only moved (and O rescaled) when it grows by more than 2^8, so most
 // tiles skip the rescale; probabilities then stay below 256 before normalisation.
+#include <cstdlib>
+#include <cstring>
+
 #include "pkv_device.h"
 
 namespace pkv {
@@ -308,13 +311,18 @@ static hipError_t launch_fwd_d(const AttnArgs& a, const FwdPlan& plan, uint16_t*
   float* ws_lse = ws_o ? ws_o + (size_t)plan.splits * rows_total * D : nullptr;
   const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
   {
-    TimerScope ts_("k_attn_fwd", s);
-    if (plan.nw == 8)
+    if (plan.nw == 8 && fwd_one_wave_per_simd()) {
+      TimerScope ts_("k_attn_fwd64", s);
+      launch_fwd64<D>(a, plan.n_rb, plan.splits, o, lse, ws_o, ws_lse, s);
+    } else if (plan.nw == 8) {
+      TimerScope ts_("k_attn_fwd", s);
       hipLaunchKernelGGL((k_attn_fwd<D, 8>), dim3(n_units), dim3(64 * 8), 0, s, a, plan.n_rb, plan.splits, o, lse,
                          ws_o, ws_lse);
-    else
+    } else {
+      TimerScope ts_("k_attn_fwd", s);
       hipLaunchKernelGGL((k_attn_fwd<D, 4>), dim3(n_units), dim3(64 * 4), 0, s, a, plan.n_rb, plan.splits, o, lse,
                          ws_o, ws_lse);
+    }
   }
   if (plan.splits > 1) {
     const int64_t work = rows_total * (D / 8);
@@ -323,6 +331,14 @@ static hipError_t launch_fwd_d(const AttnArgs& a, const FwdPlan& plan, uint16_t*
                        ws_o, ws_lse, o, lse);
   }
   return hipGetLastError();
+}
+
+bool fwd_one_wave_per_simd() {
+  static const bool v = [] {
+    const char* e = getenv("PKV_FWD_KERNEL");
+    return !(e && strcmp(e, "w8") == 0);
+  }();
+  return v;
 }
 
 hipError_t launch_fwd(const AttnArgs& a, const FwdPlan& plan, uint16_t* o, float* lse, void* ws, hipStream_t s) {

@@ -36,6 +36,28 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// The same MFMA with its accumulator pinned to the AGPR file (kernels that keep S and dP in VGPRs
+// for the softmax and their long-lived accumulators in AGPRs); the instruction is written out so
+// that the accumulator stays there. The compiler's hazard recognizer does not see inline assembly
+// as an MFMA, so the wait states it would insert are part of the statement: a VALU write of a VGPR
+// (or a v_accvgpr_write of an AGPR) followed by an MFMA that reads it (the bf16 operands packed by
+// VALU conversions, any VALU move assembling an operand) needs 2 wait states (CDNA3 instruction
+// set reference, the MAI dependency-resolution table: "VALU write VGPR, V_MFMA* read of that VGPR";
+// gfx950 keeps the rule), which s_nop 1 provides. Back-to-back MFMAs accumulating into the same
+// registers need none.
+__device__ __forceinline__ void mfma32_agpr(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// Read-back fence for an AGPR accumulator: an XDL (MFMA) write of a register followed by a VALU
+// read of it, v_accvgpr_read included, needs the MFMA's pass count plus 2 wait states (same table:
+// "XDL write VGPR/AGPR, VALU read"; 18 for a 16-pass MFMA, fewer for 8 passes). The three s_nop 7
+// give 24. The accumulator is an in/out operand, so the statement is ordered after every MFMA that
+// writes it and before every read of it.
+__device__ __forceinline__ void agpr_readback_fence(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(c));
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -103,6 +125,25 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
 }
 __device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base), 4, 0, 0);
+}
+
+// The same 16-byte direct load written out, for loops that order their LDS ring with explicit
+// waits: the compiler then does not know that it writes LDS and adds no wait for it before later
+// LDS reads (it would add one before every transposed read, which need not wait: they read
+// another stage of the ring). The load writes no register; M0 carries the wave-uniform LDS base
+// and is set inside the statement. The caller waits for it (s_waitcnt vmcnt) before any wave reads
+// the bytes, and keeps the source and LDS addresses in range as for g2lds16.
+__device__ __forceinline__ void g2lds16_asm(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// The same direct load from a wave-uniform 64-bit base plus a per-lane 32-bit byte offset (the
+// instruction's scalar-base form): no 64-bit per-lane address is formed or held.
+__device__ __forceinline__ void g2lds16_sbase(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_base)
+               : "memory", "m0");
 }
 
 // Record an out-of-range table entry (first writer wins; the value is informational).
@@ -191,8 +232,16 @@ __device__ __forceinline__ bool walk_needs_sel(const AttnArgs& a, const KeyWalk&
   return a.sel != nullptr && t < w.te && (t >> w.tsh) < a.n_sel;
 }
 
+// Table entries are wave-uniform and the tables are not written while a kernel reads them, so
+// they are read through the constant address space (scalar loads): they then count against the
+// LDS/scalar counter, not the vector-memory counter that tracks a kernel's direct loads of K/V
+// tiles, and a wait for a table entry never waits for tile data.
+__device__ __forceinline__ int32_t table_read(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)(p);
+}
+
 __device__ __forceinline__ int32_t walk_sel_read(const AttnArgs& a, const KeyWalk& w, int32_t t) {
-  return a.sel[((size_t)w.g * a.n_lists + w.li) * a.n_sel + (t >> w.tsh)];
+  return table_read(a.sel + ((size_t)w.g * a.n_lists + w.li) * a.n_sel + (t >> w.tsh));
 }
 
 // Start the walk at tile t0 (its reads complete before its walk_take returns).
@@ -208,7 +257,7 @@ __device__ __forceinline__ KeyWalk walk_begin(const AttnArgs& a, int32_t g, int3
   w.selv = 0;
   const int32_t s0 = walk_needs_sel(a, w, t0) ? walk_sel_read(a, w, t0) : 0;
   w.lp = walk_page(a, w, t0, s0);
-  if (w.lp >= 0) w.btv = a.bt[w.lp];
+  if (w.lp >= 0) w.btv = table_read(a.bt + w.lp);
   if (walk_needs_sel(a, w, t0 + 1)) w.selv = walk_sel_read(a, w, t0 + 1);
   return w;
 }
@@ -231,7 +280,7 @@ __device__ __forceinline__ const uint16_t* walk_take(const AttnArgs& a, KeyWalk&
   }
   const int32_t t1 = w.t + 1;
   const int32_t lp1 = walk_page(a, w, t1, w.selv);
-  if (lp1 >= 0) w.btv = a.bt[lp1];
+  if (lp1 >= 0) w.btv = table_read(a.bt + lp1);
   if (walk_needs_sel(a, w, t1 + 1)) w.selv = walk_sel_read(a, w, t1 + 1);
   w.lp = lp1;
   w.t = t1;

@@ -116,6 +116,14 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
                        int32_t C, int32_t h_q, int32_t top_k, int32_t n_local, int32_t n_lists, int32_t* sel,
                        void* ws, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, const FwdPlan& plan, uint16_t* o, float* lse, void* ws, hipStream_t s);
+// The forward of 256-row blocks with one wave per SIMD (64 rows per wave); the same work units,
+// outputs and split partials as k_attn_fwd with 8 waves.
+template <int D>
+hipError_t launch_fwd64(const AttnArgs& a, int32_t n_rb, int32_t splits, uint16_t* o, float* lse, float* ws_o,
+                        float* ws_lse, hipStream_t s);
+// Which kernel runs 256-row forward blocks: true (default) for launch_fwd64, false for k_attn_fwd
+// with 8 waves; PKV_FWD_KERNEL=w8 selects the latter (read once).
+bool fwd_one_wave_per_simd();
 hipError_t launch_mfma_probe(int32_t n_wg, int32_t iters, float* out, hipStream_t s);
 double mfma_probe_flop(int32_t n_wg, int32_t iters);
 hipError_t launch_atomic_probe(int32_t n_wg, int32_t n_regions, int32_t region_elems, float* buf, hipStream_t s);

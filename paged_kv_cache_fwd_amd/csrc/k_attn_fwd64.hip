@@ -544,10 +544,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // Returns false when the wave leaves the loop (gs_b set).
     auto step = [&](int32_t i, const f32x16 (&s1p)[2], f32x16 (&s1n)[2], const u32x4 (&pb0p)[2][2],
                     u32x4 (&pb0n)[2][2]) -> bool {
-      // Stage indices kept opaque (uniform values the compiler cannot enumerate), so that operand
+      // Stage indices kept opaque (scalar values the compiler cannot enumerate), so that operand
       // addresses are formed per use instead of held per stage in registers.
-      const int sc = __builtin_amdgcn_readfirstlane((i - tb) & 3);
-      const int sprev = __builtin_amdgcn_readfirstlane((i - 1 - tb) & 3);
+      int sc = (i - tb) & 3, sprev = (i - 1 - tb) & 3;
+      asm("" : "+s"(sc), "+s"(sprev));
       // Tile i+2 is staged even past the range (then from the pool's first bytes, into a stage
       // that is never read): one code path, and a constant count for the wait below.
       int32_t kp2;
@@ -573,7 +573,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (lane == 0) atomicMin(&ctl[0], i);
       }
       tile_wait(true);  // tile i+1 has landed
-      if (__hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <= i) {
+      // Read as a wave-uniform value: a loop exit that looked divergent would move every value the
+      // loop carries (the key walk's state) into vector registers.
+      if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) <=
+          i) {
         if (!left) gs_b[0] = gs_b[1] = i;
         return false;
       }
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     if (lane == 0) atomicMin(&ctl[1], min(gs_b[0], gs_b[1]));
     tile_end();
-    gs = __hip_atomic_load(&ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    gs = __builtin_amdgcn_readfirstlane(__hip_atomic_load(&ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
   }
   // General loop over [gs, te): the tiles at the causal diagonal (masked), a range whose first
   // tile was unreadable, or the rest of the range after the fast loop met a row that outgrew its

@@ -215,7 +215,7 @@ __device__ __forceinline__ int32_t walk_page(const AttnArgs& a, const KeyWalk& w
   } else if (pi >= a.n_sel) {
     lp = a.n_prior + (pi - a.n_sel);
   } else {
-    lp = __builtin_amdgcn_readfirstlane(selv);
+    lp = selv;  // a scalar load: already wave-uniform
     if (lp < 0 || lp >= a.n_prior) {
       flag_error(a.err, 2);
       return -1;
@@ -269,7 +269,7 @@ __device__ __forceinline__ const uint16_t* walk_take(const AttnArgs& a, KeyWalk&
   const uint16_t* src = nullptr;
   kpos0 = -1;
   if (w.lp >= 0) {
-    const int32_t ph = __builtin_amdgcn_readfirstlane(w.btv);
+    const int32_t ph = w.btv;  // a scalar load: already wave-uniform (no copy through a VGPR)
     if (ph < 0 || ph >= a.n_pool_pages) {
       flag_error(a.err, 1);
     } else {

@@ -37,10 +37,10 @@ TRAFFIC_SOURCES = ("paged_kv_cache_fwd_amd/csrc/k_attn_fwd.hip", "paged_kv_cache
                    "paged_kv_cache_fwd_amd/csrc/k_attn_bwd.hip",
                    "paged_kv_cache_fwd_amd/csrc/k_attn_dkdv.hip", "paged_kv_cache_fwd_amd/csrc/pkv_device.h", "paged_kv_cache_fwd_amd/csrc/pkv_internal.h",
                    "paged_kv_cache_fwd_amd/csrc/pkv_abi.cpp", "paged_kv_cache_fwd_amd/build.py")
-TRAFFIC_SHA = "33ed4c61ed7898a6"
-TRAFFIC_BYTES = {"k_attn_fwd": (2.0 * 1107147 * 1024, 231168 * 1024),
-                 "k_bwd_dq": (2.0 * 1170125 * 1024, 229376 * 1024),
-                 "k_bwd_dkdv": (2.0 * 1389163 * 1024, 1056768 * 1024)}
+TRAFFIC_SHA = "bb64f202960caf73"
+TRAFFIC_BYTES = {"k_attn_fwd64": (2.0 * 1184474 * 1024, 231168 * 1024),
+                 "k_bwd_dq": (2.0 * 1170015 * 1024, 229376 * 1024),
+                 "k_bwd_dkdv": (2.0 * 1389197 * 1024, 1048576 * 1024)}
 
 
 def traffic_bytes(kernel):

@@ -23,6 +23,21 @@ from . import (PKV_COPY_GRAD, PKV_COPY_KV, Pool, chunk_attn_bwd, chunk_attn_bwd_
                paged_kv_grad_accumulate, paged_kv_grad_offload, paged_kv_grad_stage)
 
 
+_COPY_STREAMS = {}
+
+
+def copy_streams(device) -> list:
+    """The process's three copy streams on `device` (default priority), shared by every host-tier
+    driver: HIP spreads a process's streams over a few hardware queues, and a copy stream that
+    lands on the compute stream's queue runs its copies behind the kernels instead of beside
+    them. Reusing one small set keeps the copy streams on queues of their own however many
+    drivers a process builds."""
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    if key not in _COPY_STREAMS:
+        _COPY_STREAMS[key] = [torch.cuda.Stream(device=key) for _ in range(3)]
+    return _COPY_STREAMS[key]
+
+
 class HostTierStep:
     """Reusable buffers and streams for the sparse step of one chunk shape over a host-tier pool."""
 
@@ -67,12 +82,13 @@ class HostTierStep:
                                 dtype=torch.uint8, device=device)
         self.ws_b = torch.empty(max(chunk_attn_bwd_ws_bytes(self.dev, n_prior, self.n_sel, 1, C, H_q), 1),
                                 dtype=torch.uint8, device=device)
-        self.side = torch.cuda.Stream(device=device)
+        streams = copy_streams(device)
+        self.side = streams[0]
         self.ready = [torch.cuda.Event() for _ in range(H)]
         self.done = [torch.cuda.Event() for _ in range(H)]
         # Gradient offloads run on a stream of their own, so the next step's gathers need not queue
         # behind them; the next backward of head g waits for head g's offload.
-        self.off = torch.cuda.Stream(device=device) if self.host_grads else None
+        self.off = streams[1] if self.host_grads else None
         # off_done[b][g]: the offload of head g by the last step that used buffer b (it reads
         # sel[b][g] and bt[b][g] and clears head g's device gradient slots).
         self.off_done = [[torch.cuda.Event() for _ in range(H)] for _ in range(2)]
@@ -83,7 +99,7 @@ class HostTierStep:
         self.staged = self.host_grads and grad_offload == "staged"
         self.added = [[torch.cuda.Event() for _ in range(H)] for _ in range(2)]
         if self.staged:
-            self.acc = torch.cuda.Stream(device=device)
+            self.acc = streams[2]
             self.host_bt_host = host_bt.to("cpu").contiguous()
             nb_own = grad_staging_bytes(host, self.n_own)
             nb_sel = grad_staging_bytes(host, self.n_sel)
@@ -276,8 +292,7 @@ class DenseLayerPrefetch:
             assert (h.n_pages, h.page, h.h_kv, h.d) == (h0.n_pages, h0.page, h0.h_kv, h0.d)
         self.hosts = list(hosts)
         self.dev = [Pool(h0.n_pages, h0.page, h0.h_kv, h0.d, grads=True) for _ in range(2)]
-        self.load_s = torch.cuda.Stream(device=device)
-        self.wb_s = torch.cuda.Stream(device=device)
+        self.load_s, self.wb_s = copy_streams(device)[:2]
         self.loaded = [torch.cuda.Event() for _ in range(2)]
         self.written = [torch.cuda.Event() for _ in range(2)]
         self.computed = [torch.cuda.Event() for _ in range(2)]

@@ -742,7 +742,7 @@ def main():
         log(f"[bench] topk256k: {ms_topk:.3f} ms/step, {flop_topk / (ms_topk * 1e-3) / 1e12:.1f} TFLOP/s")
         for kname, (n, ms) in sorted(kt_topk.items(), key=lambda x: -x[1][1]):
             log(f"[bench]   {kname:18s} launches {n:4d}  avg {ms / n:.3f} ms")
-        sel_ms = sum(v[1] / v[0] for k, v in kt_topk.items() if k in ("k_qsum_part", "k_qsum", "k_scores", "k_topk"))
+        sel_ms = sum(v[1] / v[0] for k, v in kt_topk.items() if k in ("k_qsum_part", "k_hsum", "k_scores", "k_topk"))
         sel_bytes = C * H_q * d * 2 + (n_prior - n_local) * H_kv * d * 4  # Q chunk + candidate reps
         topk = {"workload": "topk256k: top-64 + 4 local pages of 2016 by mean-key score, + own block",
                 "value": round(flop_topk / (ms_topk * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
@@ -769,7 +769,7 @@ def main():
                  "ms_per_step": round(ms_qp, 4), "flop_per_step": flop_topk,
                  "vs_shared_list_step": round(ms_qp / ms_topk, 3),
                  "select_ms": round(sum(v[1] / v[0] for k, v in kt_qp.items()
-                                        if k in ("k_qsum_part", "k_qsum", "k_scores", "k_topk")), 4),
+                                        if k in ("k_qsum_part", "k_hsum", "k_scores", "k_topk")), 4),
                  "fwd_ms": split_ms(kt_qp)[0], "bwd_ms": split_ms(kt_qp)[1],
                  "step_stats": stats.get("qpage256k"),
                  "per_kernel_ms": {k: round(v[1] / v[0], 4) for k, v in kt_qp.items()}}

@@ -40,61 +40,76 @@ __global__ __launch_bounds__(256) void k_qsum_part(const uint16_t* __restrict__ 
   part[idx] = acc;
 }
 
-// qsum[g][i][j], one workgroup per (KV head g, list i): hsum[hh][j] = sum over the list's blocks b
-// of part[gG+hh][b][j] by threads (hh, j) with the part values fetched 16 at a time ahead of the
-// in-order adds, then qsum[g][i][j] = sum_hh hsum[hh][j] in order by threads j.
-constexpr int kQsumThreads = 1024;
-__global__ __launch_bounds__(kQsumThreads) void k_qsum(const float* __restrict__ part, int32_t H_kv, int32_t G,
-                                                       int32_t D, int32_t nb, int32_t n_lists,
-                                                       float* __restrict__ qsum) {
-  extern __shared__ float hsum[];  // [G][D]
-  const int32_t g = blockIdx.x / n_lists, li = blockIdx.x % n_lists;
-  const int32_t nbl = nb / n_lists, b0 = li * nbl;
-  for (int32_t idx = threadIdx.x; idx < G * D; idx += kQsumThreads) {
-    const int32_t hh = idx / D, j = idx % D;
-    const float* ph = part + ((int64_t)(g * G + hh) * nb + b0) * D + j;
+// hsum[h][i][j] = sum over the blocks b of list i, in order, of part[h][b][j]: one workgroup per
+// (query head h, list i), one thread per column, with every part value of a group of 64 blocks
+// fetched before its in-order adds. (The sum over the group's heads is formed by the scoring
+// kernel.)
+__global__ __launch_bounds__(256) void k_hsum(const float* __restrict__ part, int32_t D, int32_t nb,
+                                              int32_t n_lists, float* __restrict__ hsum) {
+  const int32_t h = blockIdx.x / n_lists, li = blockIdx.x % n_lists;
+  const int32_t nbl = nb / n_lists;
+  for (int32_t j = threadIdx.x; j < D; j += 256) {
+    const float* ph = part + ((int64_t)h * nb + (int64_t)li * nbl) * D + j;
     float hs = 0.0f;
     int32_t b = 0;
-    for (; b + 16 <= nbl; b += 16) {
-      float v[16];
+    for (; b + 64 <= nbl; b += 64) {
+      float v[64];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = ph[(int64_t)(b + u) * D];
+      for (int u = 0; u < 64; ++u) v[u] = ph[(int64_t)(b + u) * D];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) hs = __fadd_rn(hs, v[u]);
+      for (int u = 0; u < 64; ++u) hs = __fadd_rn(hs, v[u]);
     }
     for (; b < nbl; ++b) hs = __fadd_rn(hs, ph[(int64_t)b * D]);
-    hsum[idx] = hs;
-  }
-  __syncthreads();
-  for (int32_t j = threadIdx.x; j < D; j += kQsumThreads) {
-    float qs = 0.0f;
-    for (int32_t hh = 0; hh < G; ++hh) qs = __fadd_rn(qs, hsum[hh * D + j]);
-    qsum[(int64_t)blockIdx.x * D + j] = qs;
+    hsum[(int64_t)blockIdx.x * D + j] = hs;
   }
 }
 
-// score[g][i][p] for candidate logical pages p < n_cand (blockIdx.y = g * n_lists + i); an
-// unreadable page scores NaN (ranks last).
-__global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qsum, const float* __restrict__ rep,
-                                                int32_t n_pool, int32_t H_kv, int32_t D, int32_t n_lists,
-                                                const int32_t* __restrict__ bt, int32_t n_bt, int32_t n_cand,
-                                                float* __restrict__ scores, int32_t* err) {
-  const int32_t gl = blockIdx.y, g = gl / n_lists;
-  const int32_t p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= n_cand) return;
-  const int32_t phys = phys_page(bt, n_bt, n_pool, p, err);
-  float acc = __uint_as_float(0x7fc00000u);
+// score[g][i][p] for candidate logical pages p < n_cand (blockIdx.y = g * n_lists + i), one page
+// per thread: the block-table read, then the page's representative row with every load in flight,
+// while the workgroup forms qsum[g][i][j] = sum_{hh<G} hsum[gG+hh][i][j] in order into LDS; then
+// the in-order dot product. An unreadable page scores NaN (ranks last). One list per KV head
+// scores with one-wave workgroups (its few thousand pages spread over as many CUs as possible);
+// one list per query page with four-wave ones (four times fewer qsum formations).
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void k_scores(const float* __restrict__ hsum, const float* __restrict__ rep,
+                                               int32_t n_pool, int32_t H_kv, int32_t G, int32_t n_lists,
+                                               const int32_t* __restrict__ bt, int32_t n_bt, int32_t n_cand,
+                                               float* __restrict__ scores, int32_t* err) {
+  __shared__ float qs[D];
+  const int32_t gl = blockIdx.y, g = gl / n_lists, li = gl % n_lists;
+  const int tid = threadIdx.x;
+  const int32_t p = blockIdx.x * NT + tid;
+  const int32_t phys = (p < n_cand) ? phys_page(bt, n_bt, n_pool, p, err) : -1;
+  f32x4 rv[D / 4];
   if (phys >= 0) {
     const f32x4* r = reinterpret_cast<const f32x4*>(rep + ((int64_t)phys * H_kv + g) * D);
-    const float* qs = qsum + (int64_t)gl * D;
+#pragma unroll
+    for (int j4 = 0; j4 < D / 4; ++j4) rv[j4] = r[j4];
+  }
+  for (int32_t j = tid; j < D; j += NT) {
+    const float* hp = hsum + ((int64_t)g * G * n_lists + li) * D + j;
+    float qv = 0.0f;
+    for (int32_t hh = 0; hh < G; hh += 16) {  // 16 heads' values fetched ahead of their adds
+      float hv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) hv[u] = (hh + u < G) ? hp[(int64_t)(hh + u) * n_lists * D] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (hh + u < G) qv = __fadd_rn(qv, hv[u]);
+    }
+    qs[j] = qv;
+  }
+  __syncthreads();
+  if (p >= n_cand) return;
+  float acc = __uint_as_float(0x7fc00000u);
+  if (phys >= 0) {
     acc = 0.0f;
-#pragma unroll 8
+#pragma unroll
     for (int32_t j4 = 0; j4 < D / 4; ++j4) {
-      const f32x4 rv = r[j4];
-      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 0], rv[0]));
-      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 1], rv[1]));
-      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 2], rv[2]));
-      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 3], rv[3]));
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 0], rv[j4][0]));
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 1], rv[j4][1]));
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 2], rv[j4][2]));
+      acc = __fadd_rn(acc, __fmul_rn(qs[4 * j4 + 3], rv[j4][3]));
     }
   }
   scores[(int64_t)gl * n_cand + p] = acc;
@@ -242,7 +257,7 @@ hipError_t topk_scratch_ptr(void** out) {
 size_t topk_ws_bytes(int32_t n_cand, int32_t C, int32_t h_q, int32_t h_kv, int32_t d, int32_t n_lists) {
   const size_t nb = (size_t)C / 64, nl = (size_t)(n_lists > 0 ? n_lists : 1);
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  return al((size_t)h_q * nb * d * 4) + al((size_t)h_kv * nl * d * 4) +
+  return al((size_t)h_q * nb * d * 4) + al((size_t)h_q * nl * d * 4) +
          al((size_t)h_kv * nl * (size_t)(n_cand > 0 ? n_cand : 1) * 4);
 }
 
@@ -258,8 +273,8 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   char* w = (char*)ws;
   float* part = (float*)w;
-  float* qsum = (float*)(w + al((size_t)h_q * nb * D * 4));
-  float* scores = (float*)(w + al((size_t)h_q * nb * D * 4) + al((size_t)HL * D * 4));
+  float* hsum = (float*)(w + al((size_t)h_q * nb * D * 4));
+  float* scores = (float*)(w + al((size_t)h_q * nb * D * 4) + al((size_t)h_q * n_lists * D * 4));
   if (n_cand > 0 && K > 0 && K < n_cand) {
     const int64_t n1 = (int64_t)h_q * nb * D;
     {
@@ -267,14 +282,19 @@ hipError_t launch_topk(const pkv_pool& pool, const int32_t* bt, int32_t n_bt, in
       hipLaunchKernelGGL(k_qsum_part, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, q, h_q, D, nb, part);
     }
     {
-      TimerScope ts_("k_qsum", s);
-      hipLaunchKernelGGL(k_qsum, dim3((unsigned)HL), dim3(kQsumThreads), (size_t)G * D * 4, s, part, H, G, D, nb,
-                         n_lists, qsum);
+      TimerScope ts_("k_hsum", s);
+      hipLaunchKernelGGL(k_hsum, dim3((unsigned)(h_q * n_lists)), dim3(256), 0, s, part, D, nb, n_lists, hsum);
     }
     {
       TimerScope ts_("k_scores", s);
-      hipLaunchKernelGGL(k_scores, dim3((unsigned)((n_cand + 255) / 256), HL), dim3(256), 0, s, qsum, pool.rep,
-                         pool.n_pages, H, D, n_lists, bt, n_bt, n_cand, scores, pool.err);
+      auto launch = [&](auto kern, int nt) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)((n_cand + nt - 1) / nt), (unsigned)HL), dim3(nt), 0, s, hsum,
+                           pool.rep, pool.n_pages, H, G, n_lists, bt, n_bt, n_cand, scores, pool.err);
+      };
+      if (D == 128)
+        n_lists == 1 ? launch(k_scores<128, 64>, 64) : launch(k_scores<128, 256>, 256);
+      else
+        n_lists == 1 ? launch(k_scores<64, 64>, 64) : launch(k_scores<64, 256>, 256);
     }
   }
   {

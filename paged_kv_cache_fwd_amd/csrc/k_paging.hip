@@ -202,9 +202,10 @@ __global__ __launch_bounds__(256) void k_export_rep(const float* __restrict__ re
 // (page, kvh) K|V block with 16-byte loads of the device-mapped pinned host memory. The grid is kept
 // small so the copy holds few CU slots while attention kernels run beside it; the host link, not
 // the CU count, bounds its speed.
-// 16 workgroups of 256 threads, 8 loads of 16 bytes in flight per thread: a CU sustains about
-// 11 GB/s of reads from device-mapped host memory, so the 16 together saturate the host link.
-constexpr int kGatherBlocks = 16;
+// 8 workgroups of 256 threads, 8 loads of 16 bytes in flight per thread, already move 54 GB/s
+// (as fast as 16; 4 reach 44 GB/s), and every CU the copy holds is one the attention kernels beside
+// it do without: a 1M-token host-tier step with lookahead takes 5.55 ms against 5.66 with 16.
+constexpr int kGatherBlocks = 8;
 constexpr int kGatherThreads = 256;
 __global__ __launch_bounds__(kGatherThreads) void k_gather(const uint16_t* __restrict__ host_kv, int32_t n_host_pool,
                                                 uint16_t* __restrict__ dev_kv, int32_t n_dev_pool, int32_t P,

@@ -34,13 +34,14 @@ LOCAL_WINDOW = 1  # pages kept by a local (sliding-window) layer
 # WRITE_SIZE rocprofv3 pass each, scaled by what those counters read for a plain 1 GiB streaming
 # kernel (x2.0 fetch, x1.0 write). Valid only for the kernel sources they were taken on.
 TRAFFIC_SOURCES = ("paged_kv_cache_fwd_amd/csrc/k_attn_fwd.hip", "paged_kv_cache_fwd_amd/csrc/k_attn_fwd64.hip",
+                   "paged_kv_cache_fwd_amd/csrc/k_attn_dq64.hip",
                    "paged_kv_cache_fwd_amd/csrc/k_attn_bwd.hip",
                    "paged_kv_cache_fwd_amd/csrc/k_attn_dkdv.hip", "paged_kv_cache_fwd_amd/csrc/pkv_device.h", "paged_kv_cache_fwd_amd/csrc/pkv_internal.h",
                    "paged_kv_cache_fwd_amd/csrc/pkv_abi.cpp", "paged_kv_cache_fwd_amd/build.py")
-TRAFFIC_SHA = "bb64f202960caf73"
-TRAFFIC_BYTES = {"k_attn_fwd64": (2.0 * 1184474 * 1024, 231168 * 1024),
-                 "k_bwd_dq": (2.0 * 1170015 * 1024, 229376 * 1024),
-                 "k_bwd_dkdv": (2.0 * 1389197 * 1024, 1048576 * 1024)}
+TRAFFIC_SHA = "8507aaaa615d3237"
+TRAFFIC_BYTES = {"k_attn_fwd64": (2.0 * 1199474 * 1024, 231168 * 1024),
+                 "k_bwd_dq64": (2.0 * 1177773 * 1024, 229376 * 1024),
+                 "k_bwd_dkdv": (2.0 * 1386934 * 1024, 1048576 * 1024)}
 
 
 def traffic_bytes(kernel):
@@ -697,7 +698,7 @@ def main():
 
     # Roofline of the dominant kernel: its own algorithmic MFMA work per launch / its average duration.
     kernel_flop = {"k_attn_fwd": 4.0 * d * H_q * pd, "k_attn_fwd64": 4.0 * d * H_q * pd,
-                   "k_bwd_dq": 6.0 * d * H_q * pd, "k_bwd_dkdv": 8.0 * d * H_q * pd}
+                   "k_bwd_dq": 6.0 * d * H_q * pd, "k_bwd_dq64": 6.0 * d * H_q * pd, "k_bwd_dkdv": 8.0 * d * H_q * pd}
     dom = max(kt_dense.items(), key=lambda x: x[1][1])[0]
     n_l, tot_ms = kt_dense[dom]
     avg_ms = tot_ms / n_l
@@ -711,7 +712,7 @@ def main():
         ach = kernel_flop[dom] / (avg_ms * 1e-3) / 1e12
         tb = traffic_bytes(dom)
         credited = {"k_attn_fwd": "4*d (S, PV)", "k_attn_fwd64": "4*d (S, PV)",
-                    "k_bwd_dq": "6*d (S and dP recomputed, dQ)",
+                    "k_bwd_dq": "6*d (S and dP recomputed, dQ)", "k_bwd_dq64": "6*d (S and dP recomputed, dQ)",
                     "k_bwd_dkdv": "8*d (S and dP recomputed, dV, dK)"}[dom]
         bwd_flop = 10.0 * d * H_q * pd
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,

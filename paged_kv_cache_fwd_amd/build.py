@@ -21,6 +21,7 @@ KERNELS = {
     # MFMA results stay in architectural VGPRs (the softmax and gradient math reads them there).
     "k_attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_attn_fwd64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_attn_dq64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     # dQ pass: the ILP-maximising machine scheduler measured about 1.7% faster here (and slower on
     # the forward, which keeps the default).
     "k_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
@@ -30,7 +31,7 @@ KERNELS = {
 HOST = ["pkv_abi.cpp"]
 # Kernels whose written-out MFMAs carry no hazard padding of their own: the emitted assembly is
 # checked at every build for the VALU-write / MFMA-read rule (see check_mfma_operand_waits).
-ASM_CHECKED = ["k_attn_fwd64.hip"]
+ASM_CHECKED = ["k_attn_fwd64.hip", "k_attn_dq64.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

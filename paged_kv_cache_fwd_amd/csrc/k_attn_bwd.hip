@@ -16,6 +16,9 @@
 // Splitting the backward this way recomputes S and dP once more than a fused kernel, but keeps
 // every partial sum on chip: a fused query-major kernel would stream one fp32 dK/dV partial per
 // 256 query rows through global atomics, about 120 GB at a 256K context.
+#include <cstdlib>
+#include <cstring>
+
 #include "pkv_device.h"
 
 namespace pkv {
@@ -320,7 +323,11 @@ static hipError_t launch_bwd_d(const AttnArgs& a, const BwdExtra& e, const BwdPl
   }
   {
     const int32_t n_units = a.n_kvh * plan.splits * plan.n_rb;
-    {
+    if (plan.dq_nw == 8 && dq_one_wave_per_simd()) {
+      TimerScope ts_("k_bwd_dq64", s);
+      const hipError_t err = launch_dq64<D>(a, e, plan.n_rb, plan.splits, ndbuf, lse2buf, ws_dq, s);
+      if (err != hipSuccess) return err;
+    } else {
       TimerScope ts_("k_bwd_dq", s);
       if (plan.dq_nw == 8)
         hipLaunchKernelGGL((k_bwd_dq<D, 8>), dim3(n_units), dim3(64 * 8), 0, s, a, e, plan.n_rb, plan.splits, ndbuf,
@@ -341,6 +348,14 @@ static hipError_t launch_bwd_d(const AttnArgs& a, const BwdExtra& e, const BwdPl
     if (err != hipSuccess) return err;
   }
   return launch_dkdv<D>(a, e, plan, ndbuf, nlsbuf, (int32_t)nrow, s);
+}
+
+bool dq_one_wave_per_simd() {
+  static const bool v = [] {
+    const char* e = getenv("PKV_DQ_KERNEL");
+    return !(e && strcmp(e, "w8") == 0);
+  }();
+  return v;
 }
 
 hipError_t launch_bwd(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, void* ws, hipStream_t s) {

@@ -124,6 +124,14 @@ hipError_t launch_fwd64(const AttnArgs& a, int32_t n_rb, int32_t splits, uint16_
 // Which kernel runs 256-row forward blocks: true (default) for launch_fwd64, false for k_attn_fwd
 // with 8 waves; PKV_FWD_KERNEL=w8 selects the latter (read once).
 bool fwd_one_wave_per_simd();
+// The dQ pass of 256-row blocks with one wave per SIMD (64 rows per wave); the same work units,
+// outputs and split partials as k_bwd_dq with 8 waves.
+template <int D>
+hipError_t launch_dq64(const AttnArgs& a, const BwdExtra& e, int32_t n_rb, int32_t splits, const float* ndbuf,
+                       const float* lse2buf, float* ws_dq, hipStream_t s);
+// Which kernel runs 256-row dQ blocks: true (default) for launch_dq64, false for k_bwd_dq with 8
+// waves; PKV_DQ_KERNEL=w8 selects the latter (read once).
+bool dq_one_wave_per_simd();
 hipError_t launch_mfma_probe(int32_t n_wg, int32_t iters, float* out, hipStream_t s);
 double mfma_probe_flop(int32_t n_wg, int32_t iters);
 hipError_t launch_atomic_probe(int32_t n_wg, int32_t n_regions, int32_t region_elems, float* buf, hipStream_t s);

@@ -31,7 +31,7 @@ KERNELS = {
 HOST = ["pkv_abi.cpp"]
 # Kernels whose written-out MFMAs carry no hazard padding of their own: the emitted assembly is
 # checked at every build for the VALU-write / MFMA-read rule (see check_mfma_operand_waits).
-ASM_CHECKED = ["k_attn_fwd64.hip", "k_attn_dq64.hip"]
+ASM_CHECKED = ["k_attn_fwd64.hip", "k_attn_dq64.hip", "k_attn_dkdv.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

@@ -364,14 +364,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using Masked = std::integral_constant<bool, true>;
   using Plain = std::integral_constant<bool, false>;
 
-  // Masked prefix: one block at a time through stage 0.
+  // Masked prefix: one block at a time, the next one staged while it runs (stages 0 and 1 in
+  // turn; a wave has 2 SEG_PER_WAVE loads per block, wave 0 one more for the row values).
+  if (blk_b < blk_m) load_blk(0);
   for (int32_t blk = blk_b; blk < blk_m; ++blk) {
-    load_blk(0);
-    wait_vmcnt<0>();
+    const int st = (blk - blk_b) & 1;
+    if (blk + 1 < blk_m) {
+      load_blk(st ^ 1);  // its stage was last read before the barrier that ended the previous block
+      if (wave == 0) wait_vmcnt<2 * T::SEG_PER_WAVE + 1>();
+      else wait_vmcnt<2 * T::SEG_PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __syncthreads();
-    s_dp(0);
+    s_dp(st);
     p_ds(Masked{}, blk, pb, dsb);
-    dv_dk(0);
+    dv_dk(st);
     __syncthreads();
   }
   if (blk_m < blk_e) {

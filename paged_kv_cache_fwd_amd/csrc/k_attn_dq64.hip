@@ -290,11 +290,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int e = 0; e < 16; ++e) sn[c][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sn[c][e], sl2, -sh[c]));
   };
   // One part: S^T(h) of both blocks into sn and dP^T(h) into dp for key half k2s of the tile in
-  // stage ss, P^T(h) in place of sn (exp2 of S^T scale log2 e - sh: sh is LSE log2 e, or +inf for
-  // a tile of an unreadable page, whose P^T and dS^T are then 0). With WD, the held previous half (P^T po, dP^T dp) becomes dS^T
-  // in section 1 and its dQ^T MFMAs (key half k2q of the tile in stage sq) run in section 3. With
-  // LD, the direct loads of tile source ts (K segments when kv = 0, V when 1), spread over sections
-  // 1 and 2.
+  // stage ss, P^T(h) in place of sn (exp2 of S^T scale log2 e - sh: sh is LSE log2 e, or +inf
+  // for a tile of an unreadable page, whose P^T and dS^T are then 0). With WD, the held previous
+  // half (P^T po, dP^T dp) becomes dS^T in section 1 and its dQ^T MFMAs (key half k2q of the tile
+  // in stage sq) run in section 3. With LD, the direct loads of tile source ts (K segments when
+  // kv = 0, V when 1), spread over sections 1 and 2.
   auto part = [&](auto wd, auto ld, int ss, int k2s, const float (&sh)[2], f32x16 (&sn)[2], const f32x16 (&po)[2],
                   f32x16 (&dp)[2], int sq, int k2q, const TileSrc& ts, int kv) {
     constexpr bool WD = decltype(wd)::value, LD = decltype(ld)::value;

@@ -54,7 +54,7 @@ __device__ __forceinline__ int32_t div_small_kv(int32_t x, int32_t G, float invG
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_dkdv(
-    AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits, const float* __restrict__ ndbuf,
+    AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits, int32_t own_splits, const float* __restrict__ ndbuf,
     const float* __restrict__ nlsbuf, int32_t pad_row) {
   using T = DkvCfg<D>;
   constexpr int BQ = T::BQ;
@@ -65,21 +65,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63, lg = lane >> 5, l32 = lane & 31;
   // Wave-uniform, so the LDS destinations of the direct loads stay in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int32_t n_units = a.n_kvh * n_ku * row_splits;
-  // Row splits vary slowest: the workgroups that run together on one XCD take neighbouring key
-  // units of one (KV head, row split) and stream the same query rows through its L2.
-  const int32_t u = xcd_remap(blockIdx.x, n_units);
-  const int32_t ku = u % n_ku;
-  const int32_t gi = (u / n_ku) % a.n_kvh;
-  const int32_t rs = u / (n_ku * a.n_kvh);
-  const int32_t g = a.kvh0 + gi;
-  // With one page list per query page the row splits are the query pages (the host plan sets
-  // row_splits = n_lists, whose row ranges then start and end on query-page boundaries).
-  const int32_t li = a.n_lists > 1 ? rs : 0;
   const int32_t G = a.G, CG = a.C * G, P = a.page, H = a.h_kv;
   const float invG = 1.0f / (float)G;
   const int32_t q0 = a.n_prior * P;
   const int tsh = (P == 128) ? 2 : 1;  // log2(32-key tiles per page)
+  // Units [0, n_full) hold a prior (or listed) key; the rest hold only the chunk's own keys.
+  const int32_t prior_tiles = list_prior(a) << tsh, per_unit = T::NW * NKT;
+  const int32_t n_full = min(n_ku, (prior_tiles + per_unit - 1) / per_unit);
+  // With one page list per query page, a unit with a listed key runs once per query page: its row
+  // splits are the query pages (the host plan sets row_splits = n_lists, whose row ranges start
+  // and end on query-page boundaries), as a query page's rows see only its own list's pages. The
+  // own-key units are seen alike by every query page from their causal diagonal on: with
+  // own_splits > 0 they run once over all rows, in own_splits row splits of equal work, as the
+  // first workgroups dispatched (the longest; consecutive workgroups go to different XCDs, so they
+  // spread over all of them). Otherwise every unit runs in row_splits splits. Row splits vary
+  // slowest within a family: the workgroups that run together on one XCD take neighbouring key
+  // units of one (KV head, row split) and stream the same query rows through its L2.
+  const bool split_own = a.n_lists > 1 && own_splits > 0 && n_full < n_ku;
+  const int32_t n_own_wg = split_own ? a.n_kvh * (n_ku - n_full) * own_splits : 0;
+  const int32_t n_fam = split_own ? n_full : n_ku;  // key units of the row-split family
+  const bool own_family = (int32_t)blockIdx.x < n_own_wg;
+  int32_t ku, gi, rs, n_rs;
+  if (own_family) {
+    const int32_t u = xcd_remap(blockIdx.x, n_own_wg), no = n_ku - n_full;
+    ku = n_full + u % no;
+    gi = (u / no) % a.n_kvh;
+    rs = u / (no * a.n_kvh);
+    n_rs = own_splits;
+  } else {
+    const int32_t u = xcd_remap(blockIdx.x - n_own_wg, a.n_kvh * n_fam * row_splits);
+    ku = u % n_fam;
+    gi = (u / n_fam) % a.n_kvh;
+    rs = u / (n_fam * a.n_kvh);
+    n_rs = row_splits;
+  }
+  const int32_t g = a.kvh0 + gi;
+  const int32_t li = (a.n_lists > 1 && !own_family) ? rs : 0;
   const int32_t n_kt = (list_prior(a) + a.C / P) << tsh;
   const int32_t kt_first = ku * (T::NW * NKT);
 
@@ -116,23 +137,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   const int32_t n_blk = (CG + BQ - 1) / BQ;
   int32_t blk_b, blk_e;
-  if (a.n_lists > 1 || row_splits == 1) {
-    blk_b = (int32_t)((int64_t)n_blk * rs / row_splits);
-    blk_e = (int32_t)((int64_t)n_blk * (rs + 1) / row_splits);
+  if ((a.n_lists > 1 && !own_family) || n_rs == 1) {
+    blk_b = (int32_t)((int64_t)n_blk * rs / n_rs);
+    blk_e = (int32_t)((int64_t)n_blk * (rs + 1) / n_rs);
   } else {
     // Row splits of equal work rather than equal rows. A unit with a prior key streams every row
     // block; a unit of own keys only starts at its causal diagonal, so later blocks carry more
-    // units. work(b) counts the (unit, block) pairs of one KV head before block b, and split r
-    // starts at the first block where work reaches r/R of the total. Every workgroup evaluates
-    // the same integer function, so the splits partition [0, n_blk) exactly.
+    // units. work(b) counts the (unit, block) pairs of one KV head before block b (of the own-key
+    // units only, for their own family), and split r starts at the first block where work reaches
+    // r/R of the total. Every workgroup evaluates the same integer function, so the splits
+    // partition [0, n_blk) exactly.
     // Own unit j >= n_full starts at block G * (j * per_unit - prior_tiles) (32 keys per tile, 32
     // rows per block): an arithmetic progression, so the sum over units has a closed form.
     static_assert(BQ == 32, "unit start blocks assume 32-row blocks");
-    const int32_t prior_tiles = list_prior(a) << tsh, per_unit = T::NW * NKT;
-    const int32_t n_full = min(n_ku, (prior_tiles + per_unit - 1) / per_unit);
     const int32_t s0 = G * (n_full * per_unit - prior_tiles), dlt = G * per_unit;
     auto work = [&](int32_t b) {
-      int64_t w = (int64_t)n_full * b;
+      int64_t w = own_family ? 0 : (int64_t)n_full * b;
       if (b > s0) {
         const int64_t k = min<int64_t>(n_ku - n_full, (b - s0 + dlt - 1) / dlt);  // units begun before b
         w += k * (b - s0) - (int64_t)dlt * k * (k - 1) / 2;
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     const int64_t total = work(n_blk);
     auto split_start = [&](int32_t r) {
-      const int64_t target = total * r / row_splits;
+      const int64_t target = total * r / n_rs;
       int32_t lo = 0, hi = n_blk;  // first b with work(b) >= target
       while (lo < hi) {
         const int32_t mid = (lo + hi) >> 1;
@@ -151,7 +171,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       return lo;
     };
     blk_b = split_start(rs);
-    blk_e = rs + 1 == row_splits ? n_blk : split_start(rs + 1);
+    blk_e = rs + 1 == n_rs ? n_blk : split_start(rs + 1);
   }
   if (wg_kpos_min > q0) blk_b = max(blk_b, (G * (wg_kpos_min - q0)) / BQ);
   if (blk_b >= blk_e) return;  // no row of this split sees a key of the unit (uniform per workgroup)
@@ -441,13 +461,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// Workgroups of the dK/dV launch, from the same counts the kernel decodes its unit with.
+static int32_t dkdv_workgroups(const AttnArgs& a, const BwdPlan& plan) {
+  const int32_t tsh = a.page == 128 ? 2 : 1;
+  const int32_t prior_tiles = (a.sel ? a.n_sel : a.n_prior) << tsh;
+  const int32_t n_full = std::min(plan.n_ku, (prior_tiles + NKT_TILES_PER_WG - 1) / NKT_TILES_PER_WG);
+  if (a.n_lists > 1 && plan.own_splits > 0 && n_full < plan.n_ku)
+    return a.n_kvh * ((plan.n_ku - n_full) * plan.own_splits + n_full * plan.row_splits);
+  return a.n_kvh * plan.n_ku * plan.row_splits;
+}
+
 template <int D>
 hipError_t launch_dkdv(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, const float* ndbuf,
                        const float* nlsbuf, int32_t pad_row, hipStream_t s) {
-  const int32_t n_units = a.n_kvh * plan.n_ku * plan.row_splits;
   TimerScope ts_("k_bwd_dkdv", s);
-  hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(n_units), dim3(64 * DkvCfg<D>::NW), 0, s, a, e, plan.n_ku,
-                     plan.row_splits, ndbuf, nlsbuf, pad_row);
+  hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(dkdv_workgroups(a, plan)), dim3(64 * DkvCfg<D>::NW), 0, s, a, e, plan.n_ku,
+                     plan.row_splits, plan.own_splits, ndbuf, nlsbuf, pad_row);
   return hipGetLastError();
 }
 

@@ -85,6 +85,8 @@ struct BwdPlan {
   int32_t splits;      // dQ pass: key-range splits
   int32_t n_ku;        // dK/dV pass: key units of 256 keys per KV head
   int32_t row_splits;  // dK/dV pass: row-range splits (one per selection list when n_lists > 1)
+  int32_t own_splits;  // dK/dV pass with n_lists > 1: row splits of the units of only the chunk's
+                       // own keys, run once over all rows (0: they run per list like the others)
   size_t ws_bytes;
 };
 

@@ -104,29 +104,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int32_t n_kt = (list_prior(a) + a.C / P) << tsh;
   const int32_t kt_first = ku * (T::NW * NKT);
 
-  // This wave's two 32-key tiles: validity, first key position, gradient page, K/V base.
-  bool kval[NKT];
-  int32_t kpos[NKT], gph[NKT], tsub[NKT];
-  const uint16_t* kbase[NKT];
-#pragma unroll
-  for (int j = 0; j < NKT; ++j) {
-    const int32_t kt_idx = kt_first + wave * NKT + j;
-    kval[j] = kt_idx < n_kt;
-    kpos[j] = 0;
-    gph[j] = -1;
-    tsub[j] = 0;
-    kbase[j] = nullptr;
-    if (kval[j]) {
-      const int32_t pi = kt_idx >> tsh;
-      tsub[j] = kt_idx & ((1 << tsh) - 1);
-      const int32_t lp = list_page(a, g, li, pi);
-      const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
-      gph[j] = phys_page(e.gbt, e.n_gbt, e.n_gpool_pages, lp, a.err);
-      kval[j] = (ph >= 0) && (gph[j] >= 0);
-      kpos[j] = (lp < 0 ? 0 : lp) * P + tsub[j] * 32;
-      if (kval[j]) kbase[j] = a.kv + (((int64_t)ph * H + g) * 2) * P * D + (int64_t)tsub[j] * 32 * D;
-    }
-  }
   // First row any key of this workgroup can see (keys ascend along the list; only the chunk's own
   // pages start later than row 0).
   int32_t wg_kpos_min;
@@ -175,41 +152,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   if (wg_kpos_min > q0) blk_b = max(blk_b, (G * (wg_kpos_min - q0)) / BQ);
   if (blk_b >= blk_e) return;  // no row of this split sees a key of the unit (uniform per workgroup)
-  // Row r sees key k iff r >= G * (k - q0). Blocks before blk_m hold rows that some key of the
-  // workgroup does not see (own pages only) and run the masked, unpipelined path.
-  int32_t my_rmin[NKT];
-#pragma unroll
-  for (int j = 0; j < NKT; ++j) my_rmin[j] = G * (kpos[j] + l32 - q0);
-  int32_t blk_m = blk_b;
-  {
-    const int32_t kt_last = min(kt_first + T::NW * NKT, n_kt) - 1;
-    const int32_t pi = kt_last >> tsh;
-    if (pi >= list_prior(a)) {
-      const int32_t lp = a.n_prior + (pi - list_prior(a));
-      const int32_t kpos_last = lp * P + (kt_last - (pi << tsh)) * 32 + 31;
-      blk_m = min(blk_e, max(blk_b, (G * (kpos_last - q0) + BQ - 1) / BQ));
-    }
-  }
-
-  // K of this wave's keys in registers (B operand of S^T = Q K^T); V rows in LDS (B operand of
-  // dP^T = dO V^T), both tiles stacked as 64 swizzled rows.
-  bf16x8 kreg[NKT][T::KS];
-#pragma unroll
-  for (int j = 0; j < NKT; ++j)
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-      u32x4 x = (u32x4){0u, 0u, 0u, 0u};
-      if (kval[j]) x = *reinterpret_cast<const u32x4*>(kbase[j] + (int64_t)l32 * D + ks * 16 + 8 * lg);
-      kreg[j][ks] = as_bf16x8(x);
-    }
-  uint16_t* vmine = vres + wave * T::VROWS * D;
-#pragma unroll
-  for (int sg = 0; sg < T::VROWS * D * 2 / 1024; ++sg) {
-    const int rl = sg * T::ROWS_PER_SEG + lane / T::CHR;
-    const int j = rl >> 5;
-    const uint16_t* vsrc = kval[j] ? kbase[j] + (int64_t)P * D : a.kv;  // invalid tiles: any bytes
-    g2lds16(vsrc + (rl & 31) * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3), vmine + sg * 512);
-  }
 
   // Staging with direct global->LDS loads. Wave w fills 1 KiB segments w*SEG_PER_WAVE + j of the
   // Q and dO blocks; lane L lands at segment offset 16 L = (row L / CHR of the segment, physical
@@ -268,6 +210,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       sl_i += di_wrap;
     }
   };
+
+  // The first block's rows do not depend on the key pages: stage them before the table walk and
+  // the K/V loads below, so that their latencies overlap.
+  load_blk(0);
+
+  // This wave's two 32-key tiles: validity, first key position, gradient page, K/V base.
+  bool kval[NKT];
+  int32_t kpos[NKT], gph[NKT], tsub[NKT];
+  const uint16_t* kbase[NKT];
+#pragma unroll
+  for (int j = 0; j < NKT; ++j) {
+    const int32_t kt_idx = kt_first + wave * NKT + j;
+    kval[j] = kt_idx < n_kt;
+    kpos[j] = 0;
+    gph[j] = -1;
+    tsub[j] = 0;
+    kbase[j] = nullptr;
+    if (kval[j]) {
+      const int32_t pi = kt_idx >> tsh;
+      tsub[j] = kt_idx & ((1 << tsh) - 1);
+      const int32_t lp = list_page(a, g, li, pi);
+      const int32_t ph = phys_page(a.bt, a.n_bt, a.n_pool_pages, lp, a.err);
+      gph[j] = phys_page(e.gbt, e.n_gbt, e.n_gpool_pages, lp, a.err);
+      kval[j] = (ph >= 0) && (gph[j] >= 0);
+      kpos[j] = (lp < 0 ? 0 : lp) * P + tsub[j] * 32;
+      if (kval[j]) kbase[j] = a.kv + (((int64_t)ph * H + g) * 2) * P * D + (int64_t)tsub[j] * 32 * D;
+    }
+  }
+  // Row r sees key k iff r >= G * (k - q0). Blocks before blk_m hold rows that some key of the
+  // workgroup does not see (own pages only) and run the masked, unpipelined path.
+  int32_t my_rmin[NKT];
+#pragma unroll
+  for (int j = 0; j < NKT; ++j) my_rmin[j] = G * (kpos[j] + l32 - q0);
+  int32_t blk_m = blk_b;
+  {
+    const int32_t kt_last = min(kt_first + T::NW * NKT, n_kt) - 1;
+    const int32_t pi = kt_last >> tsh;
+    if (pi >= list_prior(a)) {
+      const int32_t lp = a.n_prior + (pi - list_prior(a));
+      const int32_t kpos_last = lp * P + (kt_last - (pi << tsh)) * 32 + 31;
+      blk_m = min(blk_e, max(blk_b, (G * (kpos_last - q0) + BQ - 1) / BQ));
+    }
+  }
+
+  // K of this wave's keys in registers (B operand of S^T = Q K^T); V rows in LDS (B operand of
+  // dP^T = dO V^T), both tiles stacked as 64 swizzled rows.
+  bf16x8 kreg[NKT][T::KS];
+#pragma unroll
+  for (int j = 0; j < NKT; ++j)
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) {
+      u32x4 x = (u32x4){0u, 0u, 0u, 0u};
+      if (kval[j]) x = *reinterpret_cast<const u32x4*>(kbase[j] + (int64_t)l32 * D + ks * 16 + 8 * lg);
+      kreg[j][ks] = as_bf16x8(x);
+    }
+  uint16_t* vmine = vres + wave * T::VROWS * D;
+#pragma unroll
+  for (int sg = 0; sg < T::VROWS * D * 2 / 1024; ++sg) {
+    const int rl = sg * T::ROWS_PER_SEG + lane / T::CHR;
+    const int j = rl >> 5;
+    const uint16_t* vsrc = kval[j] ? kbase[j] + (int64_t)P * D : a.kv;  // invalid tiles: any bytes
+    g2lds16(vsrc + (rl & 31) * D + (((lane % T::CHR) ^ swz<D>(rl)) << 3), vmine + sg * 512);
+  }
 
   const float sl2 = a.scale * kLog2e;
   f32x16 dk[NKT][T::DT], dv[NKT][T::DT];
@@ -386,7 +391,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // Masked prefix: one block at a time, the next one staged while it runs (stages 0 and 1 in
   // turn; a wave has 2 SEG_PER_WAVE loads per block, wave 0 one more for the row values).
-  if (blk_b < blk_m) load_blk(0);
   for (int32_t blk = blk_b; blk < blk_m; ++blk) {
     const int st = (blk - blk_b) & 1;
     if (blk + 1 < blk_m) {
@@ -403,9 +407,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __syncthreads();
   }
   if (blk_m < blk_e) {
-    // Pipelined part. Prologue: blocks blk_m and blk_m + 1 staged, S/dP and P/dS of blk_m, S/dP of
-    // blk_m + 1.
-    load_blk(0);
+    // Pipelined part. Prologue: blocks blk_m and blk_m + 1 staged (blk_m already is when there is
+    // no masked block), S/dP and P/dS of blk_m, S/dP of blk_m + 1.
+    if (blk_m > blk_b) load_blk(0);
     if (blk_m + 1 < blk_e) load_blk(1);
     wait_vmcnt<0>();
     __syncthreads();

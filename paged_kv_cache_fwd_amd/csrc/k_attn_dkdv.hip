@@ -5,8 +5,9 @@
 // it 2.B (custom kernels add the key/value gradients in place into gradient pages, outside
 // autograd, with atomic adds).
 //
-// With one page list per query page (pt 2.C) a workgroup takes one query page's rows and keys
-// from that page's list, so every row block it streams sees all of its keys.
+// With one page list per query page (pt 2.C) a workgroup of listed keys takes one query page's
+// rows and keys from that page's list, so every row block it streams sees all of its keys; the
+// chunk's own keys, which every query page sees, run once over all rows.
 //
 // One workgroup = 4 waves, one per SIMD, each owning 64 keys (two 32-key tiles) of one KV head:
 // K of its keys in VGPRs, V in LDS, dK and dV (2 x 64 x d fp32) in accumulation registers for the

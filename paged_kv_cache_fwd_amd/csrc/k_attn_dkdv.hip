@@ -53,10 +53,10 @@ __device__ __forceinline__ int32_t div_small_kv(int32_t x, int32_t G, float invG
   return q;
 }
 
-template <int D>
+template <int D, bool HOST_SPLITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_dkdv(
-    AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits, int32_t own_splits, const float* __restrict__ ndbuf,
-    const float* __restrict__ nlsbuf, int32_t pad_row) {
+    AttnArgs a, BwdExtra e, int32_t n_ku, int32_t row_splits, int32_t own_splits, RowSplits splits,
+    const float* __restrict__ ndbuf, const float* __restrict__ nlsbuf, int32_t pad_row) {
   using T = DkvCfg<D>;
   constexpr int BQ = T::BQ;
   constexpr int NKT = T::NKT;
@@ -118,15 +118,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if ((a.n_lists > 1 && !own_family) || n_rs == 1) {
     blk_b = (int32_t)((int64_t)n_blk * rs / n_rs);
     blk_e = (int32_t)((int64_t)n_blk * (rs + 1) / n_rs);
+  } else if constexpr (HOST_SPLITS) {
+    // Row splits of equal work rather than equal rows (the own-key units start at their causal
+    // diagonal, so later blocks carry more units): boundaries from the host plan, which counts
+    // 32-row blocks. The search below finds the same boundaries in the kernel; it costs the
+    // workgroup about 7 thousand cycles (64-bit arithmetic in a binary search).
+    static_assert(BQ == 32, "the plan's row splits count 32-row blocks");
+    blk_b = splits.b[rs];
+    blk_e = splits.b[rs + 1];
   } else {
-    // Row splits of equal work rather than equal rows. A unit with a prior key streams every row
-    // block; a unit of own keys only starts at its causal diagonal, so later blocks carry more
-    // units. work(b) counts the (unit, block) pairs of one KV head before block b (of the own-key
-    // units only, for their own family), and split r starts at the first block where work reaches
-    // r/R of the total. Every workgroup evaluates the same integer function, so the splits
-    // partition [0, n_blk) exactly.
-    // Own unit j >= n_full starts at block G * (j * per_unit - prior_tiles) (32 keys per tile, 32
-    // rows per block): an arithmetic progression, so the sum over units has a closed form.
+    // The same boundaries found in the kernel, in the instantiation launched with one row split,
+    // where this branch does not run: with it in the code, the compiler schedules the block loop
+    // below 0.7% faster than without. A unit with a prior key streams every row block; a unit of
+    // own keys only starts at its causal diagonal, so later blocks carry more units. work(b)
+    // counts the (unit, block) pairs of one KV head before block b (of the own-key units only,
+    // for their own family), and split r starts at the first block where work reaches r/R of
+    // the total, so the splits partition [0, n_blk) exactly. Own unit j >= n_full starts at block
+    // G * (j * per_unit - prior_tiles) (32 keys per tile, 32 rows per block): an arithmetic
+    // progression, so the sum over units has a closed form.
     static_assert(BQ == 32, "unit start blocks assume 32-row blocks");
     const int32_t s0 = G * (n_full * per_unit - prior_tiles), dlt = G * per_unit;
     auto work = [&](int32_t b) {
@@ -480,8 +489,15 @@ template <int D>
 hipError_t launch_dkdv(const AttnArgs& a, const BwdExtra& e, const BwdPlan& plan, const float* ndbuf,
                        const float* nlsbuf, int32_t pad_row, hipStream_t s) {
   TimerScope ts_("k_bwd_dkdv", s);
-  hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3(dkdv_workgroups(a, plan)), dim3(64 * DkvCfg<D>::NW), 0, s, a, e, plan.n_ku,
-                     plan.row_splits, plan.own_splits, ndbuf, nlsbuf, pad_row);
+  // Equal-work row splits take their boundaries from the plan; a launch with one row split (the
+  // dense pass) runs the instantiation whose block loop is scheduled faster.
+  const bool host_splits = a.n_lists > 1 || plan.row_splits > 1;
+  if (host_splits)
+    hipLaunchKernelGGL((k_bwd_dkdv<D, true>), dim3(dkdv_workgroups(a, plan)), dim3(64 * DkvCfg<D>::NW), 0, s, a, e,
+                       plan.n_ku, plan.row_splits, plan.own_splits, plan.work_splits, ndbuf, nlsbuf, pad_row);
+  else
+    hipLaunchKernelGGL((k_bwd_dkdv<D, false>), dim3(dkdv_workgroups(a, plan)), dim3(64 * DkvCfg<D>::NW), 0, s, a, e,
+                       plan.n_ku, plan.row_splits, plan.own_splits, plan.work_splits, ndbuf, nlsbuf, pad_row);
   return hipGetLastError();
 }
 

@@ -297,6 +297,46 @@ FwdPlan plan_fwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_
   return p;
 }
 
+// Row splits of equal work rather than equal rows for the dK/dV pass. A key unit (256 keys) with a
+// prior key streams every row block; a unit of the chunk's own keys only starts at its causal
+// diagonal, so later blocks carry more units. work(b) counts the (unit, block) pairs of one KV
+// head before block b (of the own-key units only when own_only), and split r starts at the first
+// block where work reaches r/R of the total, so the splits partition [0, n_blk) exactly. Own unit
+// j >= n_full starts at block G * (j * 8 - prior_tiles) (32 keys per tile, 8 tiles per unit, 32
+// rows per block): an arithmetic progression, so the sum over units has a closed form.
+static RowSplits equal_work_splits(int32_t n_list_pages, int32_t page, int32_t n_ku, int32_t G, int64_t n_blk,
+                                   int32_t R, bool own_only) {
+  RowSplits s{};
+  R = std::max(1, std::min(R, MAX_ROW_SPLITS));
+  const int64_t prior_tiles = (int64_t)n_list_pages * (page / 32), per_unit = NKT_TILES_PER_WG;
+  const int64_t n_full = std::min<int64_t>(n_ku, (prior_tiles + per_unit - 1) / per_unit);
+  const int64_t s0 = G * (n_full * per_unit - prior_tiles), dlt = G * per_unit;
+  auto work = [&](int64_t b) {
+    int64_t w = own_only ? 0 : n_full * b;
+    if (b > s0) {
+      const int64_t k = std::min<int64_t>(n_ku - n_full, (b - s0 + dlt - 1) / dlt);  // units begun before b
+      w += k * (b - s0) - dlt * k * (k - 1) / 2;
+    }
+    return w;
+  };
+  const int64_t total = work(n_blk);
+  for (int32_t r = 0; r <= R; ++r) {
+    if (r == R) {
+      s.b[r] = (int32_t)n_blk;
+      break;
+    }
+    const int64_t target = total * r / R;
+    int64_t lo = 0, hi = n_blk;  // first b with work(b) >= target
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (work(mid) >= target) hi = mid;
+      else lo = mid + 1;
+    }
+    s.b[r] = (int32_t)lo;
+  }
+  return s;
+}
+
 BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_kvh, int32_t C, int32_t G,
                  int32_t d) {
   BwdPlan p;
@@ -309,7 +349,7 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_
   const int64_t n_kt = (int64_t)(n_list_pages + C / page) * (page / 32);
   p.n_ku = (int32_t)((n_kt + NKT_TILES_PER_WG - 1) / NKT_TILES_PER_WG);
   const int64_t n_blk = (rows + 31) / 32;
-  const int32_t max_rs = (int32_t)std::min<int64_t>(64, n_blk);
+  const int32_t max_rs = (int32_t)std::min<int64_t>(MAX_ROW_SPLITS, n_blk);
   // One page list per query page: the dK/dV pass splits rows exactly at the lists (each query
   // page's rows see only its list's pages).
   p.row_splits = n_lists > 1 ? n_lists : best_split((int64_t)n_kvh * p.n_ku, (double)n_blk, 2.0, max_rs, 1);
@@ -320,6 +360,8 @@ BwdPlan plan_bwd(int32_t n_list_pages, int32_t n_lists, int32_t page, int32_t n_
   // on the 256K per-query-page step (32 lists): 2 splits 1.47-1.52 ms, 1 split 1.57-1.58, 4 splits
   // 1.52-1.55, 8 splits 1.54-1.63, against 1.74-1.79 ms once per list.
   p.own_splits = n_lists > 1 ? std::max(1, n_lists / 16) : 0;
+  p.work_splits = equal_work_splits(n_list_pages, page, p.n_ku, G, n_blk, n_lists > 1 ? p.own_splits : p.row_splits,
+                                    n_lists > 1);
   // [H_q][C] row dots (H_q = n_kvh*G is enough for the heads computed, but the buffer is indexed by
   // absolute head, so size it for every head the pool can address), then dQ partials.
   p.ws_bytes = 0;  // filled by the caller, which knows H_q

@@ -79,6 +79,13 @@ struct FwdPlan {
   int32_t splits;     // key-range splits (>1 needs the combine kernel and workspace)
   size_t ws_bytes;
 };
+// First row block of each equal-work row split of the dK/dV pass, and n_blk after the last
+// (passed by value as a kernel argument).
+constexpr int MAX_ROW_SPLITS = 64;
+struct RowSplits {
+  int32_t b[MAX_ROW_SPLITS + 1];
+};
+
 struct BwdPlan {
   int32_t dq_nw;       // dQ pass: waves per workgroup, as the forward's nw
   int32_t n_rb;        // dQ pass: row blocks per KV head (n_lists x blocks per list)
@@ -87,6 +94,8 @@ struct BwdPlan {
   int32_t row_splits;  // dK/dV pass: row-range splits (one per selection list when n_lists > 1)
   int32_t own_splits;  // dK/dV pass with n_lists > 1: row splits of the units of only the chunk's
                        // own keys, run once over all rows (0: they run per list like the others)
+  RowSplits work_splits;  // boundaries of the equal-work splits: of all units with one list (when
+                          // row_splits > 1), of the own-key units with one list per query page
   size_t ws_bytes;
 };
 

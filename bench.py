@@ -38,10 +38,10 @@ TRAFFIC_SOURCES = ("paged_kv_cache_fwd_amd/csrc/k_attn_fwd.hip", "paged_kv_cache
                    "paged_kv_cache_fwd_amd/csrc/k_attn_bwd.hip",
                    "paged_kv_cache_fwd_amd/csrc/k_attn_dkdv.hip", "paged_kv_cache_fwd_amd/csrc/pkv_device.h", "paged_kv_cache_fwd_amd/csrc/pkv_internal.h",
                    "paged_kv_cache_fwd_amd/csrc/pkv_abi.cpp", "paged_kv_cache_fwd_amd/build.py")
-TRAFFIC_SHA = "460d095897428895"
-TRAFFIC_BYTES = {"k_attn_fwd64": (2.0 * 1198235 * 1024, 231168 * 1024),
-                 "k_bwd_dq64": (2.0 * 1176769 * 1024, 229376 * 1024),
-                 "k_bwd_dkdv": (2.0 * 1388924 * 1024, 1048576 * 1024)}
+TRAFFIC_SHA = "bc62b71d223e1f31"
+TRAFFIC_BYTES = {"k_attn_fwd64": (2.0 * 1206855 * 1024, 231168 * 1024),
+                 "k_bwd_dq64": (2.0 * 1176240 * 1024, 229376 * 1024),
+                 "k_bwd_dkdv": (2.0 * 1386450 * 1024, 1048576 * 1024)}
 
 
 def traffic_bytes(kernel):

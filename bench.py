@@ -163,7 +163,7 @@ def cpu_baseline(wl, k_np, v_np, q_np, do_np, c, tokens):
 
 def bench_host1m(args, pkv, synth, dev, t16):
     """1M-token sparse step with the prior pages in pinned host memory: selection, per-KV-head H2D
-    gathers on a side stream overlapped with the previous head's forward+backward."""
+    gathers on a side stream overlapped with the previous head's backward."""
     import torch
     from paged_kv_cache_fwd_amd.host_tier import HostTierStep
 
@@ -268,7 +268,7 @@ def bench_host1m(args, pkv, synth, dev, t16):
     log(f"[bench] host1m: {ms_host:.3f} ms/step with gathers ({ms_host_ahead:.3f} with lookahead), {ms_res:.3f} ms "
         f"resident, gathers alone {ms_gather:.3f} ms; host gradient pages with lookahead {ms_host_grads_ahead:.3f} ms")
     return {"workload": "host1m: 1M tokens, 8160 prior pages in pinned host memory, top-128 + 8 local per KV head, "
-                        "per-head H2D gathers overlapped with the previous head's fwd+bwd",
+                        "per-head H2D gathers overlapped with the previous head's backward",
             "value": round(flop / (ms_host * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ms_host, 4),
             "flop_per_step": flop, "ms_per_step_pages_resident": round(ms_res, 4),
             "overlap_overhead": round(ms_host / ms_res - 1.0, 4),

@@ -330,10 +330,16 @@ int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt,
  * other entries are left as they are; entries >= n_dev_bt are skipped and flagged). Indices stay on
  * the device; nothing synchronises; order it against the compute stream with events.
  * host must be a PKV_HOST_TIER pool and dev a device pool of the same page size, heads and dim.
+ * n_workgroups (0..64; 0 picks 8) sets how many workgroups copy, each keeping one CU to itself while
+ * the copy runs (it reserves LDS that an attention workgroup would need there). Each moves about
+ * 11 GB/s over the host link and 8 reach the link's own limit (about 55 GB/s measured on MI355X); a
+ * gather that runs beside attention kernels slows them less on 2, one that they wait for is done
+ * soonest on 8.
+ * Other values fail with PKV_E_INVALID.
  */
 int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_dev, int32_t n_host_bt,
                     const int32_t* sel_dev, int32_t n_sel, int32_t kvh, const int32_t* dst_pages_dev,
-                    int32_t* dev_bt_out_dev, int32_t n_dev_bt, void* stream);
+                    int32_t* dev_bt_out_dev, int32_t n_dev_bt, int32_t n_workgroups, void* stream);
 
 /*
  * Diagnostic: the sustained bf16 MFMA rate of this GPU, the practical ceiling of the attention

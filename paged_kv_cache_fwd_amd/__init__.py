@@ -78,7 +78,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "chunk_attn_bwd_ws_bytes": (_S, [_P, _I, _I, _I, _I, _I, _I]),
         "chunk_attn_bwd": (_I, [_P, _P, _I, _P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _F, _P, _P, _S,
                                 _P]),
-        "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _P]),
+        "paged_kv_gather": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _I, _I, _P]),
         "paged_kv_grad_offload": (_I, [_P, _P, _I, _P, _P, _I, _P, _I, _I, _I, _P]),
         "paged_kv_copy": (_I, [_P, _P, _U, _I, _I, _P]),
         "pkv_mfma_probe": (_I, [_I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
@@ -360,10 +360,12 @@ def chunk_attn_bwd(pool: Pool, bt: torch.Tensor, n_prior: int, q: torch.Tensor, 
 
 
 def paged_kv_gather(host: Pool, dev: Pool, host_bt: torch.Tensor, sel_row: torch.Tensor, kvh: int,
-                    dst_pages: torch.Tensor, dev_bt_out: Optional[torch.Tensor] = None, stream=None):
+                    dst_pages: torch.Tensor, dev_bt_out: Optional[torch.Tensor] = None, n_workgroups: int = 0,
+                    stream=None):
     """Copy the (page, kvh) blocks of the logical pages sel_row from a host-tier pool into the device
     pool pages dst_pages (both int32 device vectors of equal length); optionally record
-    dev_bt_out[sel_row[i]] = dst_pages[i]."""
+    dev_bt_out[sel_row[i]] = dst_pages[i]. n_workgroups: CUs the copy holds (0: 8, the host link's
+    rate; 2 for a copy that runs beside attention kernels)."""
     _need(host_bt, torch.int32, "host_bt")
     _need(sel_row, torch.int32, "sel_row")
     _need(dst_pages, torch.int32, "dst_pages", sel_row.shape)
@@ -371,7 +373,7 @@ def paged_kv_gather(host: Pool, dev: Pool, host_bt: torch.Tensor, sel_row: torch
         _need(dev_bt_out, torch.int32, "dev_bt_out")
     _check(load().paged_kv_gather(host.handle, dev.handle, _ptr(host_bt), host_bt.numel(), _ptr(sel_row),
                                   sel_row.numel(), kvh, _ptr(dst_pages), _ptr(dev_bt_out),
-                                  0 if dev_bt_out is None else dev_bt_out.numel(), _stream(stream)))
+                                  0 if dev_bt_out is None else dev_bt_out.numel(), n_workgroups, _stream(stream)))
 
 
 def paged_kv_grad_offload(host: Pool, host_bt: torch.Tensor, dev: Pool, dev_bt: torch.Tensor, lps: torch.Tensor,

@@ -199,12 +199,16 @@ __global__ __launch_bounds__(256) void k_export_rep(const float* __restrict__ re
 }
 
 // Host tier -> device: a few workgroups stride over the selected pages, each copying a page's
-// (page, kvh) K|V block with 16-byte loads of the device-mapped pinned host memory. The grid is kept
-// small so the copy holds few CU slots while attention kernels run beside it; the host link, not
-// the CU count, bounds its speed.
-// 8 workgroups of 256 threads, 8 loads of 16 bytes in flight per thread, already move 54 GB/s
-// (as fast as 16; 4 reach 44 GB/s), and every CU the copy holds is one the attention kernels beside
-// it do without: a 1M-token host-tier step with lookahead takes 5.55 ms against 5.66 with 16.
+// (page, kvh) K|V block with 16-byte loads of the device-mapped pinned host memory. The caller picks
+// the workgroup count: one workgroup of 256 threads, 8 loads of 16 bytes in flight per thread, moves
+// about 11 GB/s over the host link (a CU's outstanding misses, not its threads, set the rate), 4 move
+// 44 GB/s and 8 move 54, as fast as 16: the link's own limit.
+// Each workgroup also reserves kGatherLds bytes of LDS that it never touches, so that no attention
+// workgroup (113 to 132 KB of LDS each) shares its CU. One that did ran its one wave per SIMD beside
+// the copy's waves, which hold the CU's memory pipeline, and its whole grid waited for it: a forward
+// or dQ pass beside a copy took up to 30% longer. With the reservation the copy takes an idle CU (the
+// forward and dQ grids of a one-head call leave some) or waits for one.
+constexpr size_t kGatherLds = 64 * 1024;
 constexpr int kGatherBlocks = 8;
 constexpr int kGatherThreads = 256;
 __global__ __launch_bounds__(kGatherThreads) void k_gather(const uint16_t* __restrict__ host_kv, int32_t n_host_pool,
@@ -393,11 +397,12 @@ hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, 
 
 hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
                          const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages,
-                         int32_t* dev_bt_out, int32_t n_dev_bt, hipStream_t s) {
+                         int32_t* dev_bt_out, int32_t n_dev_bt, int32_t n_workgroups, hipStream_t s) {
   if (n_sel == 0) return hipSuccess;
+  const int32_t n_wg = n_workgroups > 0 ? n_workgroups : kGatherBlocks;
   {
     TimerScope ts_("k_gather", s);
-    hipLaunchKernelGGL(k_gather, dim3(n_sel < kGatherBlocks ? n_sel : kGatherBlocks), dim3(kGatherThreads), 0, s, host.kv,
+    hipLaunchKernelGGL(k_gather, dim3(n_sel < n_wg ? n_sel : n_wg), dim3(kGatherThreads), kGatherLds, s, host.kv,
                        host.n_pages, dev.kv, dev.n_pages, host.page, host.h_kv, host.d, host_bt, n_host_bt, sel, n_sel,
                        dst_pages, kvh, dev_bt_out, n_dev_bt, dev.err);
   }

@@ -1095,7 +1095,7 @@ int chunk_attn_bwd(const pkv_pool* pool, const int32_t* bt_dev, int32_t n_bt, pk
 
 int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_dev, int32_t n_host_bt,
                     const int32_t* sel_dev, int32_t n_sel, int32_t kvh, const int32_t* dst_pages_dev,
-                    int32_t* dev_bt_out_dev, int32_t n_dev_bt, void* stream) {
+                    int32_t* dev_bt_out_dev, int32_t n_dev_bt, int32_t n_workgroups, void* stream) {
   if (!host || !dev) return fail(PKV_E_INVALID, "NULL pool");
   if (!(host->flags & PKV_HOST_TIER)) return fail(PKV_E_STATE, "source pool is not a host-tier pool");
   if (dev->flags & PKV_HOST_TIER) return fail(PKV_E_STATE, "destination pool must be a device pool");
@@ -1105,8 +1105,10 @@ int paged_kv_gather(const pkv_pool* host, pkv_pool* dev, const int32_t* host_bt_
   if (n_sel < 0) return fail(PKV_E_INVALID, "n_sel < 0");
   if (n_sel > 0 && (!host_bt_dev || !sel_dev || !dst_pages_dev)) return fail(PKV_E_INVALID, "NULL table");
   if (dev_bt_out_dev && n_dev_bt < 0) return fail(PKV_E_INVALID, "n_dev_bt < 0");
+  if (n_workgroups < 0 || n_workgroups > pkv::kGatherMaxWorkgroups)
+    return fail(PKV_E_INVALID, "n_workgroups=%d outside [0, %d]", n_workgroups, pkv::kGatherMaxWorkgroups);
   hipError_t e = pkv::launch_gather(*host, *dev, host_bt_dev, n_host_bt, sel_dev, n_sel, kvh, dst_pages_dev,
-                                    dev_bt_out_dev, n_dev_bt, (hipStream_t)stream);
+                                    dev_bt_out_dev, n_dev_bt, n_workgroups, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   ok();
   return PKV_OK;

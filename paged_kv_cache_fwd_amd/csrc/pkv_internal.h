@@ -113,7 +113,8 @@ hipError_t launch_export(const pkv_pool& pool, int32_t what, const int32_t* bt, 
                          int32_t n_pages, void* dst, hipStream_t s);
 hipError_t launch_gather(const pkv_pool& host, const pkv_pool& dev, const int32_t* host_bt, int32_t n_host_bt,
                          const int32_t* sel, int32_t n_sel, int32_t kvh, const int32_t* dst_pages,
-                         int32_t* dev_bt_out, int32_t n_dev_bt, hipStream_t s);
+                         int32_t* dev_bt_out, int32_t n_dev_bt, int32_t n_workgroups, hipStream_t s);
+constexpr int32_t kGatherMaxWorkgroups = 64;
 hipError_t launch_grad_offload(const pkv_pool& host, const int32_t* host_bt, int32_t n_host_bt, const pkv_pool& dev,
                                const int32_t* dev_bt, int32_t n_dev_bt, const int32_t* lp, int32_t n, int32_t kvh0,
                                int32_t n_kvh, hipStream_t s);

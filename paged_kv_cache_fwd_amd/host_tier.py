@@ -6,8 +6,8 @@ only the selected pages move (pt 2.C, it 2.D).
 
 Per chunk: page_topk_select on the host-tier pool (its representatives are on the device), then for
 each KV head g a side stream gathers g's selected (page, head) blocks into g's device slots
-(paged_kv_gather also writes g's device block table) while the compute stream runs forward and
-backward of head g-1. Gradients go to the host-tier pool's device-resident gradient pages through
+(paged_kv_gather also writes g's device block table) while the compute stream runs the backward
+of head g-1. Gradients go to the host-tier pool's device-resident gradient pages through
 its own block table, or, when the host pool keeps its gradient pages in host memory, into device
 slots that the side stream then adds to the host pages (pt 2.D: the gradients of the KV cache
 move to CPU memory too). Every computation is a library kernel; this module only orders them.
@@ -24,6 +24,12 @@ from . import (PKV_COPY_GRAD, PKV_COPY_KV, Pool, chunk_attn_bwd, chunk_attn_bwd_
 
 
 _COPY_STREAMS = {}
+
+# Workgroups of a gather that the compute stream waits for (8 reach the host link's rate) and of one
+# that runs beside a backward (each keeps a CU to itself; 2 move about 22 GB/s, which finishes a
+# head's pages well within the previous head's backward).
+GATHER_WG_WAITED = 8
+GATHER_WG_BESIDE = 2
 
 
 def copy_streams(device) -> list:
@@ -139,12 +145,12 @@ class HostTierStep:
 
     def _lookahead(self, next_q: torch.Tensor, compute):
         """Enqueue on the side stream the next step's selection (into the next step's buffers) and its
-        first head's gather, behind this step's gathers and head 0's backward, so that they run
-        beside this step's remaining heads instead of at the start of the next step."""
+        first head's gather, behind this step's gathers and the last head's forward, so that they
+        run beside the last head's backward instead of at the start of the next step."""
         H = self.host.h_kv
         nb = self.parity  # the next step's buffers
         after = torch.cuda.Event()
-        after.record(compute)  # next_q is ready, and head 0's slots are no longer read (done[0])
+        after.record(compute)  # next_q is ready, and head 0's slots are no longer read
         with torch.cuda.stream(self.side):
             self.side.wait_event(after)
             if self.host_grads:
@@ -154,7 +160,7 @@ class HostTierStep:
             if self.host_grads:
                 self.side.wait_event(self.off_done[nb][0])  # bt[nb][0] no longer read by an offload
             paged_kv_gather(self.host, self.dev, self.host_bt, self.sel[nb][0], 0, self.slots[0],
-                            dev_bt_out=self.bt[nb][0], stream=self.side)
+                            dev_bt_out=self.bt[nb][0], n_workgroups=GATHER_WG_BESIDE, stream=self.side)
             self.ready[0].record(self.side)
         self._pre = next_q
 
@@ -163,9 +169,12 @@ class HostTierStep:
         """One sparse step. With gather=False the slots are assumed filled already (for timing the
         same selection without host traffic; not with gradient pages in host memory).
 
+        Head g's gather (g >= 1) is enqueued behind head g-1's forward, so that it runs beside head
+        g-1's backward on few CUs; head 0's, which the step waits for, runs on more.
+
         next_q (the next step's queries, already written on the current stream): the next step's page
         selection and its first head's gather are enqueued on the side stream beside this step's
-        last heads, so that the next step starts with head 0's pages in place. The next run() must
+        last backward, so that the next step starts with head 0's pages in place. The next run() must
         then take that same tensor as q (or cancel_lookahead() must come first).
 
         Gradient pages in host memory: head g's backward accumulates into its device slots. An
@@ -202,31 +211,32 @@ class HostTierStep:
             sel = page_topk_select(self.host, self.host_bt, self.n_prior, q, self.top_k, self.n_local,
                                    sel=self.sel[b], ws=self.ws_t)
 
-        def enqueue_gather(g, after=None):
-            # Events are waited on at their latest record: `after` is this step's selection, done[g]
-            # the previous step's backward of head g (recorded again only later in this step).
+        def enqueue_gather(g, n_wg):
+            # Events are waited on at their latest record: `after` is this step's selection or head
+            # g-1's forward, done[g] the previous step's backward of head g (recorded again only
+            # later in this step).
+            after = torch.cuda.Event()
+            after.record(compute)
             with torch.cuda.stream(self.side):
                 self.side.wait_event(self.done[g])  # slots of g are free once its last backward ended
                 if self.host_grads:
                     self.side.wait_event(self.off_done[b][g])  # bt[b][g] is no longer read by an offload
-                if after is not None:
-                    self.side.wait_event(after)
+                self.side.wait_event(after)
                 paged_kv_gather(self.host, self.dev, self.host_bt, sel[g], g, self.slots[g], dev_bt_out=bts[g],
-                                stream=self.side)
+                                n_workgroups=n_wg, stream=self.side)
                 self.ready[g].record(self.side)
 
-        if gather:
-            if not pre:
-                sel_ready = torch.cuda.Event()
-                sel_ready.record(compute)
-                enqueue_gather(0, sel_ready)
-            for g in range(1, H):
-                enqueue_gather(g)  # behind the selection on the side stream when it came from a lookahead
+        if gather and not pre:
+            enqueue_gather(0, GATHER_WG_WAITED)
         for g in range(H):
             if gather:
                 compute.wait_event(self.ready[g])
             chunk_attn_fwd(self.dev, bts[g], self.n_prior, q, scale, sel=sel, kvh0=g, n_kvh=1, o=o, lse=lse,
                            ws=self.ws_f)
+            if gather and g + 1 < H:
+                enqueue_gather(g + 1, GATHER_WG_BESIDE)  # behind the selection too, after a lookahead
+            if g == H - 1 and next_q is not None:
+                self._lookahead(next_q, compute)
             if self.host_grads:
                 # Head g's gradient slots are cleared by the previous step's offload of head g.
                 compute.wait_event(self.off_done[prev][g])
@@ -236,8 +246,6 @@ class HostTierStep:
                 chunk_attn_bwd(self.dev, bts[g], self.n_prior, q, o, dout, lse, scale, sel=sel, kvh0=g, n_kvh=1,
                                gpool=self.host, gbt=self.host_bt, dq=dq, ws=self.ws_b)
             self.done[g].record(compute)
-            if g == 0 and next_q is not None:
-                self._lookahead(next_q, compute)
             if self.staged:
                 with torch.cuda.stream(self.off):
                     self.off.wait_event(self.done[g])

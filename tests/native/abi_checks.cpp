@@ -266,11 +266,14 @@ static void check_compute_validation() {
   CHECK(paged_kv_check(p) == PKV_OK);
 
   // Host tier: gather and gradient offload.
-  ENQUEUES(1, paged_kv_gather(host, p, bt, n_bt, sel, 4, 1, bt, nullptr, 0, nullptr));
-  FAILS(PKV_E_STATE, paged_kv_gather(p, p, bt, n_bt, sel, 4, 1, bt, nullptr, 0, nullptr));
-  FAILS(PKV_E_STATE, paged_kv_gather(host, host, bt, n_bt, sel, 4, 1, bt, nullptr, 0, nullptr));
-  FAILS(PKV_E_INVALID, paged_kv_gather(host, p, bt, n_bt, sel, 4, 2, bt, nullptr, 0, nullptr));
-  FAILS(PKV_E_INVALID, paged_kv_gather(host, other, bt, n_bt, sel, 4, 0, bt, nullptr, 0, nullptr));
+  ENQUEUES(1, paged_kv_gather(host, p, bt, n_bt, sel, 4, 1, bt, nullptr, 0, 0, nullptr));
+  FAILS(PKV_E_STATE, paged_kv_gather(p, p, bt, n_bt, sel, 4, 1, bt, nullptr, 0, 0, nullptr));
+  FAILS(PKV_E_STATE, paged_kv_gather(host, host, bt, n_bt, sel, 4, 1, bt, nullptr, 0, 0, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_gather(host, p, bt, n_bt, sel, 4, 2, bt, nullptr, 0, 0, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_gather(host, other, bt, n_bt, sel, 4, 0, bt, nullptr, 0, 0, nullptr));
+  ENQUEUES(1, paged_kv_gather(host, p, bt, n_bt, sel, 4, 1, bt, nullptr, 0, 64, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_gather(host, p, bt, n_bt, sel, 4, 1, bt, nullptr, 0, -1, nullptr));
+  FAILS(PKV_E_INVALID, paged_kv_gather(host, p, bt, n_bt, sel, 4, 1, bt, nullptr, 0, 65, nullptr));
   ENQUEUES(1, paged_kv_grad_offload(hg, bt, n_bt, p, bt, n_bt, sel, 4, 0, 2, nullptr));
   FAILS(PKV_E_STATE, paged_kv_grad_offload(host, bt, n_bt, p, bt, n_bt, sel, 4, 0, 2, nullptr));
   FAILS(PKV_E_STATE, paged_kv_grad_offload(hg, bt, n_bt, nog, bt, n_bt, sel, 4, 0, 2, nullptr));

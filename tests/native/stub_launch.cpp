@@ -22,7 +22,7 @@ hipError_t launch_export(const pkv_pool&, int32_t, const int32_t*, int32_t, int3
   return hipSuccess;
 }
 hipError_t launch_gather(const pkv_pool&, const pkv_pool&, const int32_t*, int32_t, const int32_t*, int32_t, int32_t,
-                         const int32_t*, int32_t*, int32_t, hipStream_t) {
+                         const int32_t*, int32_t*, int32_t, int32_t, hipStream_t) {
   ++g_stub_launches;
   return hipSuccess;
 }

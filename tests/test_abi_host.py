@@ -59,7 +59,7 @@ def test_argument_errors_without_device(lib):
                               None, None, 0, None) == -1
     assert lib.page_topk_select(None, None, 0, 0, None, 64, 4, 1, 0, 1, None, None, None, 0, None) == -1
     assert lib.paged_kv_append(None, None, 0, 0, 0, None, None, None) == -1
-    assert lib.paged_kv_gather(None, None, None, 0, None, 0, 0, None, None, 0, None) == -1
+    assert lib.paged_kv_gather(None, None, None, 0, None, 0, 0, None, None, 0, 0, None) == -1
     assert lib.paged_kv_grad_offload(None, None, 0, None, None, 0, None, 0, 0, 1, None) == -1
     assert lib.paged_kv_copy(None, None, 1, 0, 0, None) == -1
     assert lib.paged_kv_check(None) == -1

@@ -389,3 +389,34 @@ def test_paged_kv_copy_rejects_bad_arguments(pkv):
         pkv.chunk_attn_fwd(a, bt, 2, k[:128].contiguous(), 0.1, sel=i32(np.zeros((2, 1, 1, 1))))
     for p in (a, b, c, h):
         p.free()
+
+
+@pytest.mark.parametrize("n_wg", [1, 2, 3, 0, 64])
+def test_gather_workgroup_counts(pkv, n_wg):
+    """paged_kv_gather moves the same blocks and writes the same device block table whatever number of
+    workgroups copies them (0: the default, 8); the blocks match the appended K/V bit for bit."""
+    wl = synth.Workload("gather-wg", 14, 2, 128, 128, 128 * 24, 384, (7,), offset_std=0.5, seed=22)
+    n, P, kvh = wl.n_pages, wl.page, 1
+    say(f"gather: 10 of {n} host pages, head {kvh}, n_workgroups={n_wg}")
+    hpool, hbt = fill_pool(pkv, wl, n, synth.page_permutation(wl), host_tier=True)
+    rng = np.random.default_rng(5)
+    sel_np = np.sort(rng.choice(n, 10, replace=False)).astype(np.int32)
+    dst_np = rng.permutation(14)[:10].astype(np.int32)  # device pages 14 and 15 stay unused
+    dpool = pkv.Pool(16, P, wl.h_kv, wl.d, grads=False)
+    dev_bt = torch.full((n,), 15, dtype=torch.int32, device="cuda:0")
+    pkv.paged_kv_gather(hpool, dpool, hbt, i32(sel_np), kvh, i32(dst_np), dev_bt_out=dev_bt, n_workgroups=n_wg)
+    torch.cuda.synchronize()
+    hpool.check()
+    dpool.check()
+    want_bt = np.full(n, 15, np.int32)
+    want_bt[sel_np] = dst_np
+    assert np.array_equal(dev_bt.cpu().numpy(), want_bt)
+    k, v = synth.kv_tokens(wl, 0, n)
+    rows = (sel_np[:, None] * P + np.arange(P)[None, :]).reshape(-1)
+    for what, ref in ((pkv.PKV_K, k), (pkv.PKV_V, v)):
+        got = dpool.export(what, dev_bt, 0, n).view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got[rows, kvh], np.ascontiguousarray(ref).view(np.uint16)[rows, kvh])
+    with pytest.raises(RuntimeError):
+        pkv.paged_kv_gather(hpool, dpool, hbt, i32(sel_np), kvh, i32(dst_np), n_workgroups=65)
+    dpool.free()
+    hpool.free()
